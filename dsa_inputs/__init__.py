@@ -247,3 +247,36 @@ def _draw_cache(draw, n, d, std, dtype, device, slab=1 << 20):
         if scale is not None:
             scale[a:b] = s
     return cache, scale
+
+
+def to_torch(inp: Dict[str, np.ndarray], cfg: DsaConfig, device) -> Dict[str, "object"]:
+    """Move make_inputs() arrays to ``device`` as torch tensors of the stored dtypes
+    (bf16 bit patterns -> torch.bfloat16, fp8 codes -> torch.float8_e4m3fn), bit for bit."""
+    import torch
+    out = {}
+    dt = {"q_idx": cfg.q_idx_dtype, "k_cache": cfg.key_dtype, "q_mla": cfg.q_mla_dtype,
+          "kv_cache": cfg.kv_dtype}
+    for name, arr in inp.items():
+        if arr is None:
+            out[name] = None
+            continue
+        kind = dt.get(name)
+        if kind == "bf16":
+            t = torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16)
+        elif kind == "fp8":
+            t = torch.from_numpy(np.ascontiguousarray(arr)).view(torch.float8_e4m3fn)
+        else:
+            t = torch.from_numpy(np.ascontiguousarray(arr))
+        out[name] = t.to(device)
+    return out
+
+
+def from_torch(t) -> np.ndarray:
+    """Device tensor -> numpy array of the stored bits (bf16 -> uint16, fp8 -> uint8)."""
+    import torch
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8).numpy()
+    return t.numpy()

@@ -1,0 +1,391 @@
+// Sparse MLA decode on gfx950 (the "MLA sparse decode" kernel group of "GLM-52 Runs on RTX
+// 4090", section "how did he do it"), over 576-wide compressed latent rows with V = the first
+// 512 values, weight-absorbed and without GQA (Show HN "Chay GLM 5.2 tren may tinh cham",
+// main-features section).
+//
+// mla_mfma_kernel: one workgroup = 4 waves = one query row x one chunk of its selected slots
+// (split-k).  Wave w owns heads [16w, 16w+16).  Per 32-token tile:
+//   * the tile's rows are gathered from HBM (16-byte loads, one row = 72 of them; fp8 rows are
+//     widened to bf16 in registers) into LDS, double-buffered so the next tile's loads are in
+//     flight while this one is computed;
+//   * S^T = rows . q^T on v_mfma_f32_16x16x32_bf16 (M = 16 tokens, N = 16 heads, K = 576 in 18
+//     steps, q held in registers).  The two 16-token blocks are chosen so that each lane ends
+//     up with 8 consecutive tokens of one head, exactly the K slice the P.V product needs;
+//   * online softmax in fp32 with exp2 (log2 e folded into the scale) and lazy rescaling: the
+//     running maximum moves only when a tile exceeds it by more than 2^8, so the 512-value
+//     accumulator is rarely touched;
+//   * O^T += V^T . P^T on the same MFMA with M = 16 latent dims, N = 16 heads, K = 32 tokens;
+//     the V^T operand comes from LDS with ds_read_b64_tr_b16 (a transposing LDS read), P from
+//     registers as bf16 (the fp8 per-token scale is folded into P and into the logits).
+// With n_split > 1 each chunk writes (m, l, o/l) partials and mla_combine_kernel merges them in
+// a fixed order.  mla_valu_kernel is the f32 path (any head count), one workgroup per (row, head).
+#include "dsa_internal.hpp"
+
+namespace dsa {
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------------------------------------
+// vector path (f32 q)
+
+template <typename KT> struct RowElt;
+template <> struct RowElt<float> {
+  static __device__ __forceinline__ float get(const void* p, int64_t i) { return ((const float*)p)[i]; }
+};
+template <> struct RowElt<__bf16> {
+  static __device__ __forceinline__ float get(const void* p, int64_t i) {
+    return bf16_bits_to_f32(((const uint16_t*)p)[i]);
+  }
+};
+struct Fp8Row {};
+template <> struct RowElt<Fp8Row> {
+  static __device__ __forceinline__ float get(const void* p, int64_t i) {
+    return fp8_to_f32(((const uint8_t*)p)[i]);
+  }
+};
+
+__device__ __forceinline__ float block_reduce_256(float v, float* red, bool is_max) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const float o = __shfl_xor(v, off);
+    v = is_max ? fmaxf(v, o) : v + o;
+  }
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int w = 1; w < 4; ++w) r = is_max ? fmaxf(r, red[w]) : r + red[w];
+  __syncthreads();
+  return r;
+}
+
+template <typename KT>
+__global__ __launch_bounds__(256) void mla_valu_kernel(MlaParams p) {
+  extern __shared__ float sm[];     // q [576] | e [k]
+  __shared__ float red[4];
+  const int r = blockIdx.x, h = blockIdx.y;
+  const float* q = (const float*)p.q + ((int64_t)r * p.H + h) * kRowDim;
+  float* e = sm + kRowDim;
+  for (int d = threadIdx.x; d < kRowDim; d += 256) sm[d] = q[d];
+  __syncthreads();
+  const int32_t* sl = p.slots + (int64_t)r * p.k;
+  float m = -INFINITY;
+  for (int j = threadIdx.x; j < p.k; j += 256) {
+    const int64_t s = sl[j];
+    float z = -INFINITY;
+    if (s >= 0) {
+      float dot = 0.f;
+      for (int d = 0; d < kRowDim; ++d) dot = fmaf(sm[d], RowElt<KT>::get(p.kv, s * kRowDim + d), dot);
+      if (p.kv_scale) dot *= p.kv_scale[s];
+      z = dot * p.sm_scale;
+    }
+    e[j] = z;
+    m = fmaxf(m, z);
+  }
+  m = block_reduce_256(m, red, true);
+  float* out = p.out + ((int64_t)r * p.H + h) * kVDim;
+  if (m == -INFINITY) {
+    for (int d = threadIdx.x; d < kVDim; d += 256) out[d] = 0.f;
+    if (p.lse && threadIdx.x == 0) p.lse[(int64_t)r * p.H + h] = -INFINITY;
+    return;
+  }
+  float l = 0.f;
+  for (int j = threadIdx.x; j < p.k; j += 256) {
+    const float z = e[j];
+    const float x = z == -INFINITY ? 0.f : expf(z - m);
+    e[j] = x;
+    l += x;
+  }
+  l = block_reduce_256(l, red, false);   // (the reduction's barrier also publishes e[])
+  for (int d = threadIdx.x; d < kVDim; d += 256) {
+    float acc = 0.f;
+    for (int j = 0; j < p.k; ++j) {
+      const int64_t s = sl[j];
+      if (s < 0) continue;
+      float v = RowElt<KT>::get(p.kv, s * kRowDim + d);
+      if (p.kv_scale) v *= p.kv_scale[s];
+      acc = fmaf(e[j], v, acc);
+    }
+    out[d] = acc / l;
+  }
+  if (p.lse && threadIdx.x == 0) p.lse[(int64_t)r * p.H + h] = m + logf(l);
+}
+
+// ---------------------------------------------------------------------------------------------
+// matrix-core path (bf16 q, bf16 or fp8 rows, H = 16 * active waves <= 64)
+
+constexpr int kTT = 32;                          // tokens per tile
+constexpr int kPitch = kRowDim * 2 + 16;          // LDS bytes per bf16 row (+16 against bank conflicts)
+constexpr int kNT = 256;                          // threads per workgroup
+constexpr int kChunksBf16 = kTT * (kRowDim * 2 / 16);   // 2304 16-byte pieces per tile
+constexpr int kChunksFp8 = kTT * (kRowDim / 16);        // 1152
+
+template <bool FP8>
+struct TileStage {
+  static constexpr int kPer = FP8 ? (kChunksFp8 + kNT - 1) / kNT : kChunksBf16 / kNT;   // 5 or 9
+  u32x4 v[kPer];
+};
+
+template <bool FP8>
+__device__ __forceinline__ void tile_load(TileStage<FP8>& st, const MlaParams& p, const int32_t* sl, int j_base,
+                                          int j_end) {
+  constexpr int kPiecesPerRow = FP8 ? kRowDim / 16 : kRowDim * 2 / 16;   // 36 or 72
+  const uint8_t* kv = (const uint8_t*)p.kv;
+#pragma unroll
+  for (int c = 0; c < TileStage<FP8>::kPer; ++c) {
+    const int g = c * kNT + threadIdx.x;
+    const int tk = g / kPiecesPerRow, piece = g - tk * kPiecesPerRow;
+    const int j = j_base + tk;
+    int64_t s = -1;
+    if (g < kTT * kPiecesPerRow && j < j_end) s = sl[j];
+    if (s >= 0)
+      st.v[c] = __builtin_nontemporal_load((const u32x4*)(kv + s * (FP8 ? kRowDim : 2 * kRowDim)) + piece);
+    else
+      st.v[c] = u32x4{0, 0, 0, 0};
+  }
+}
+
+template <bool FP8>
+__device__ __forceinline__ void tile_store(const TileStage<FP8>& st, uint8_t* lds) {
+  constexpr int kPiecesPerRow = FP8 ? kRowDim / 16 : kRowDim * 2 / 16;
+#pragma unroll
+  for (int c = 0; c < TileStage<FP8>::kPer; ++c) {
+    const int g = c * kNT + threadIdx.x;
+    if (g >= kTT * kPiecesPerRow) continue;
+    const int tk = g / kPiecesPerRow, piece = g - tk * kPiecesPerRow;
+    if constexpr (FP8) {
+      __bf16 tmp[16];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) fp8x4_to_bf16x4(st.v[c][d], tmp + 4 * d);
+      bf16x8 lo, hi;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        lo[e] = tmp[e];
+        hi[e] = tmp[8 + e];
+      }
+      bf16x8* dst = (bf16x8*)(lds + tk * kPitch + piece * 32);
+      dst[0] = lo;
+      dst[1] = hi;
+    } else {
+      *(u32x4*)(lds + tk * kPitch + piece * 16) = st.v[c];
+    }
+  }
+}
+
+template <bool FP8>
+__global__ __launch_bounds__(kNT) void mla_mfma_kernel(MlaParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t tile[2][kTT * kPitch];
+  __shared__ float tok_scale[2][kTT];             // per-token scale (fp8) or 1; 0 marks a skipped slot
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int r = blockIdx.y, split = blockIdx.x;
+  const int j0 = split * p.chunk;
+  const int j1 = min(p.k, j0 + p.chunk);
+  const int ntiles = j1 > j0 ? (j1 - j0 + kTT - 1) / kTT : 0;
+  const int32_t* sl = p.slots + (int64_t)r * p.k;
+  const bool active = wave * 16 < p.H;            // waves past the head count only help load
+  const int head = wave * 16 + (lane & 15);
+  const int grp = lane >> 4;                      // 16-lane group
+
+  // q fragments (B operand of S^T): head lane%16, dims s*32 + grp*8 .. +8
+  bf16x8 qf[18];
+  if (active) {
+    const bf16x8* qrow = (const bf16x8*)((const __bf16*)p.q + ((int64_t)r * p.H + head) * kRowDim);
+#pragma unroll
+    for (int s = 0; s < 18; ++s) qf[s] = qrow[s * 4 + grp];
+  }
+
+  f32x4 o[32];
+#pragma unroll
+  for (int db = 0; db < 32; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY;   // running max of z * log2(e), per head
+  float l_run = 0.f;         // this lane group's share of sum exp2(z - m_run)
+  const float scale2 = p.sm_scale * kLog2e;
+
+  TileStage<FP8> st;
+  auto stage_scales = [&](int buf, int jb) {
+    if (threadIdx.x < kTT) {
+      const int j = jb + threadIdx.x;
+      const int64_t s = j < j1 ? sl[j] : -1;
+      tok_scale[buf][threadIdx.x] = s < 0 ? 0.f : (FP8 ? p.kv_scale[s] : 1.f);
+    }
+  };
+  if (ntiles > 0) {
+    tile_load<FP8>(st, p, sl, j0, j1);
+    tile_store<FP8>(st, tile[0]);
+    stage_scales(0, j0);
+  }
+  __syncthreads();
+
+  for (int it = 0; it < ntiles; ++it) {
+    const int buf = it & 1;
+    const bool more = it + 1 < ntiles;
+    if (more) tile_load<FP8>(st, p, sl, j0 + (it + 1) * kTT, j1);
+    if (active) {
+      const uint8_t* T = tile[buf];
+      // ---- S^T for two 16-token blocks; block beta row m holds token 8*(m/4) + 4*beta + m%4
+      f32x4 sacc[2];
+#pragma unroll
+      for (int beta = 0; beta < 2; ++beta) {
+        const int m = lane & 15;
+        const int tok = 8 * (m >> 2) + 4 * beta + (m & 3);
+        const uint8_t* base = T + tok * kPitch + grp * 16;
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 18; ++s)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(base + s * 64), qf[s], acc, 0, 0, 0);
+        sacc[beta] = acc;
+      }
+      // this lane holds head `head`, tokens 8*grp + 4*beta + j
+      float z[8], sc[8];
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int beta = 0; beta < 2; ++beta)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int t = 8 * grp + 4 * beta + j;
+          const float tsc = tok_scale[buf][t];
+          sc[4 * beta + j] = tsc;
+          const float zz = tsc != 0.f ? sacc[beta][j] * tsc * scale2 : -INFINITY;
+          z[4 * beta + j] = zz;
+          tmax = fmaxf(tmax, zz);
+        }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      const bool need = tmax > m_run + 8.f || (m_run == -INFINITY && tmax > -INFINITY);
+      if (__any(need)) {
+        const float m_new = need ? tmax : m_run;
+        const float alpha = need ? (m_run == -INFINITY ? 0.f : exp2f(m_run - m_new)) : 1.f;
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < 32; ++db) o[db] *= alpha;
+      }
+      bf16x8 pb;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float pe = z[e] == -INFINITY ? 0.f : exp2f(z[e] - m_run);
+        l_run += pe;
+        pb[e] = (__bf16)(FP8 ? pe * sc[e] : pe);
+      }
+      // ---- O^T += V^T . P^T ; V^T operand via transposing LDS reads (4 tokens x 16 dims per read)
+      const int jl = lane & 15;
+      const uint8_t* vrow1 = T + (8 * grp + (jl >> 2)) * kPitch + (jl & 3) * 8;
+      const uint8_t* vrow2 = vrow1 + 4 * kPitch;
+#pragma unroll
+      for (int db = 0; db < 32; ++db) {
+        const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (__attribute__((address_space(3))) bf16x4*)(vrow1 + db * 32));
+        const bf16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (__attribute__((address_space(3))) bf16x4*)(vrow2 + db * 32));
+        const bf16x8 a = __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7);
+        o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, o[db], 0, 0, 0);
+      }
+    }
+    if (more) {
+      tile_store<FP8>(st, tile[buf ^ 1]);
+      stage_scales(buf ^ 1, j0 + (it + 1) * kTT);
+    }
+    __syncthreads();
+  }
+
+  if (!active) return;
+  float l_tot = l_run + __shfl_xor(l_run, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  // lane holds O^T[d = db*16 + grp*4 + j][head]
+  if (p.n_split == 1) {
+    float* dst = p.out + ((int64_t)r * p.H + head) * kVDim + grp * 4;
+#pragma unroll
+    for (int db = 0; db < 32; ++db) *(f32x4*)(dst + db * 16) = o[db] * inv;
+    if (p.lse && grp == 0)
+      p.lse[(int64_t)r * p.H + head] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+  } else {
+    const int64_t prow = ((int64_t)r * p.n_split + split) * p.H + head;
+    float* dst = p.part_o + prow * kVDim + grp * 4;
+#pragma unroll
+    for (int db = 0; db < 32; ++db) *(f32x4*)(dst + db * 16) = o[db] * inv;
+    if (grp == 0) {
+      p.part_m[prow] = l_tot > 0.f ? m_run * kLn2 : -INFINITY;
+      p.part_l[prow] = l_tot;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// split-k merge: one 128-thread workgroup per (row, head), 4 values per thread
+
+__global__ __launch_bounds__(128) void mla_combine_kernel(CombineParams p) {
+  const int r = blockIdx.x / p.H, h = blockIdx.x - (blockIdx.x / p.H) * p.H;
+  float M = -INFINITY;
+  for (int j = 0; j < p.n_split; ++j) {
+    const int64_t pr = ((int64_t)r * p.n_split + j) * p.H + h;
+    if (p.part_l[pr] > 0.f) M = fmaxf(M, p.part_m[pr]);
+  }
+  float* dst = p.out + ((int64_t)r * p.H + h) * kVDim + threadIdx.x * 4;
+  if (M == -INFINITY) {
+    *(f32x4*)dst = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (p.lse && threadIdx.x == 0) p.lse[(int64_t)r * p.H + h] = -INFINITY;
+    return;
+  }
+  float den = 0.f;
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < p.n_split; ++j) {
+    const int64_t pr = ((int64_t)r * p.n_split + j) * p.H + h;
+    const float lj = p.part_l[pr];
+    if (!(lj > 0.f)) continue;
+    const float a = expf(p.part_m[pr] - M) * lj;
+    den += a;
+    acc += a * *(const f32x4*)(p.part_o + pr * kVDim + threadIdx.x * 4);
+  }
+  *(f32x4*)dst = acc * (1.f / den);
+  if (p.lse && threadIdx.x == 0) p.lse[(int64_t)r * p.H + h] = M + logf(den);
+}
+
+}  // namespace
+
+int mla_default_split(int rows, int H, int k) {
+  (void)H;
+  // about one workgroup per compute unit, at least 64 selected rows per chunk
+  int ns = 256 / (rows > 0 ? rows : 1);
+  const int max_ns = (k + 63) / 64;
+  if (ns > max_ns) ns = max_ns;
+  if (ns < 1) ns = 1;
+  return ns;
+}
+
+hipError_t launch_mla(const MlaParams& p0, dsa_dtype_t q_dtype, dsa_dtype_t kv_dtype, hipStream_t s) {
+  MlaParams p = p0;
+  if (q_dtype == DSA_F32) {
+    p.n_split = 1;
+    const dim3 grid((unsigned)p.rows, (unsigned)p.H);
+    const size_t shm = (size_t)(kRowDim + p.k) * sizeof(float);
+    if (kv_dtype == DSA_F32) hipLaunchKernelGGL(mla_valu_kernel<float>, grid, dim3(256), shm, s, p);
+    else if (kv_dtype == DSA_BF16) hipLaunchKernelGGL(mla_valu_kernel<__bf16>, grid, dim3(256), shm, s, p);
+    else hipLaunchKernelGGL(mla_valu_kernel<Fp8Row>, grid, dim3(256), shm, s, p);
+    return hipGetLastError();
+  }
+  int chunk = (p.k + p.n_split - 1) / p.n_split;
+  chunk = (chunk + kTT - 1) / kTT * kTT;
+  p.chunk = chunk;
+  const dim3 grid((unsigned)p.n_split, (unsigned)p.rows);
+  if (kv_dtype == DSA_FP8_E4M3FN) hipLaunchKernelGGL(mla_mfma_kernel<true>, grid, dim3(kNT), 0, s, p);
+  else hipLaunchKernelGGL(mla_mfma_kernel<false>, grid, dim3(kNT), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.n_split == 1) return e;
+  CombineParams c{p.part_o, p.part_m, p.part_l, p.out, p.lse, p.rows, p.H, p.n_split};
+  return launch_combine(c, s);
+}
+
+hipError_t launch_combine(const CombineParams& c, hipStream_t s) {
+  if (c.rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)(c.rows * c.H)), dim3(128), 0, s, c);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

@@ -1,0 +1,141 @@
+"""The C ABI without a GPU: the library loads, exports every entry point include/dsa.h
+declares, and rejects bad arguments before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_attention_10_amd as dsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(dsa.LIB_PATH):
+        from sparse_attention_10_amd import build
+        build.build()
+    return dsa.lib()
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(dsa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_path(L):
+    names = _declared()
+    for n in ("dsa_indexer_scores", "dsa_topk", "dsa_page_map", "dsa_sparse_mla_decode", "dsa_decode_step",
+              "dsa_mla_combine"):
+        assert n in names
+    assert set(names) == set(dsa.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(L):
+    for n in _declared():
+        assert hasattr(L, n), n
+    assert L.dsa_abi_version() == 1
+    assert L.dsa_status_string(0) == b"DSA_OK"
+    assert L.dsa_status_string(3) == b"DSA_ERR_WORKSPACE_TOO_SMALL"
+
+
+def _batch(**kw):
+    b = dict(batch=1, q_per_seq=1, max_seq_len=4096, page_size=64, max_pages_per_seq=64, num_slots=4096,
+             seq_lens=256, page_table=512)
+    b.update(kw)
+    return dsa.DsaBatch(b["batch"], b["q_per_seq"], b["max_seq_len"], b["page_size"], b["max_pages_per_seq"],
+                        b["num_slots"], b["seq_lens"], b["page_table"])
+
+
+FAKE = 1 << 20   # an aligned non-NULL address; validation failures never dereference it
+
+
+def _indexer(L, batch, **kw):
+    a = dict(q=FAKE, qd=dsa.DSA_BF16, w=FAKE, k=FAKE, kd=dsa.DSA_BF16, ks=None, Hi=64, Di=128, s=FAKE, ld=4096)
+    a.update(kw)
+    return L.dsa_indexer_scores(ctypes.byref(batch), a["q"], a["qd"], a["w"], a["k"], a["kd"], a["ks"], a["Hi"],
+                                a["Di"], a["s"], a["ld"], None)
+
+
+@pytest.mark.parametrize("kw,bkw,status", [
+    (dict(q=None), {}, 1),
+    (dict(), dict(batch=0), 1),
+    (dict(), dict(q_per_seq=5000), 1),
+    (dict(), dict(page_size=0), 1),
+    (dict(), dict(max_pages_per_seq=10), 1),
+    (dict(), dict(seq_lens=None), 1),
+    (dict(kd=dsa.DSA_FP8_E4M3FN), {}, 1),            # fp8 keys without scales
+    (dict(qd=dsa.DSA_FP8_E4M3FN), {}, 1),            # fp8 q is not accepted
+    (dict(kd=7), {}, 1),
+    (dict(ld=100), {}, 1),
+    (dict(Hi=0), {}, 1),
+    (dict(Hi=200), {}, 2),
+    (dict(q=FAKE + 2), {}, 1),                        # matrix-core path needs 16-byte alignment
+])
+def test_indexer_rejects(L, kw, bkw, status):
+    assert _indexer(L, _batch(**bkw), **kw) == status
+    assert len(L.dsa_last_error()) > 0
+
+
+def test_topk_rejects(L):
+    b = _batch()
+    assert L.dsa_topk(ctypes.byref(b), FAKE, 4096, 0, FAKE, None, None, 0, None) == 1
+    assert L.dsa_topk(ctypes.byref(b), FAKE, 4096, 9000, FAKE, None, None, 0, None) == 2
+    assert L.dsa_topk(ctypes.byref(b), None, 4096, 16, FAKE, None, None, 0, None) == 1
+    assert L.dsa_topk(ctypes.byref(b), FAKE, 10, 16, FAKE, None, None, 0, None) == 1
+    big = _batch(max_seq_len=300000, max_pages_per_seq=5000)
+    assert L.dsa_topk(ctypes.byref(big), FAKE, 300000, 16, FAKE, None, None, 0, None) == 2
+    assert L.dsa_topk_workspace_size(ctypes.byref(b), 2048) == 0
+
+
+def _mla(L, **kw):
+    a = dict(B=1, Q=1, q=FAKE, qd=dsa.DSA_BF16, kv=FAKE, kvd=dsa.DSA_BF16, ks=None, ns_=4096, sl=FAKE, k=2048,
+             H=64, scale=0.04, out=FAKE, lse=None, split=0, ws=None, wsb=0)
+    a.update(kw)
+    return L.dsa_sparse_mla_decode(a["B"], a["Q"], a["q"], a["qd"], a["kv"], a["kvd"], a["ks"], a["ns_"], a["sl"],
+                                   a["k"], a["H"], a["scale"], a["out"], a["lse"], a["split"], a["ws"], a["wsb"],
+                                   None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(H=8), 2), (dict(H=100), 2), (dict(kvd=dsa.DSA_F32), 2),
+    (dict(kvd=dsa.DSA_FP8_E4M3FN), 1), (dict(k=0), 1), (dict(k=10000), 2), (dict(scale=float("nan")), 1),
+    (dict(split=-1), 1), (dict(out=FAKE + 4), 1), (dict(split=4), 3),
+])
+def test_mla_rejects(L, kw, status):
+    assert _mla(L, **kw) == status
+
+
+def test_mla_workspace_sizes(L):
+    # one chunk needs no workspace; k chunks need partial o, m and l per head
+    assert L.dsa_sparse_mla_workspace_size(1, 1, 64, 2048, 1, dsa.DSA_BF16) == 0
+    ns = L.dsa_sparse_mla_default_split(1, 1, 64, 2048)
+    assert 1 < ns <= 64
+    need = L.dsa_sparse_mla_workspace_size(1, 1, 64, 2048, 4, dsa.DSA_BF16)
+    assert need >= 4 * 64 * 512 * 4 + 2 * 4 * 64 * 4
+    assert L.dsa_sparse_mla_workspace_size(1, 1, 16, 2048, 4, dsa.DSA_F32) == 0   # vector path: no split
+
+
+def test_decode_step_workspace_and_rejects(L):
+    a = dsa.DsaDecodeStepArgs()
+    a.batch = _batch()
+    a.q_idx, a.q_idx_dtype, a.w, a.k_cache, a.k_dtype = FAKE, dsa.DSA_BF16, FAKE, FAKE, dsa.DSA_BF16
+    a.idx_heads, a.idx_dim, a.top_k = 64, 128, 2048
+    a.q_mla, a.q_mla_dtype, a.kv_cache, a.kv_dtype = FAKE, dsa.DSA_BF16, FAKE, dsa.DSA_BF16
+    a.mla_heads, a.sm_scale, a.out = 64, 1 / 24, FAKE
+    need = L.dsa_decode_step_workspace_size(ctypes.byref(a))
+    assert need >= 4096 * 4 + 2 * 2048 * 4
+    assert L.dsa_decode_step(ctypes.byref(a), FAKE, need - 1, None) == 3
+    a.top_k = 0
+    assert L.dsa_decode_step(ctypes.byref(a), FAKE, need, None) == 1
+    assert L.dsa_decode_step(None, FAKE, need, None) == 1
+
+
+def test_valid_call_without_gpu_reports_instead_of_crashing(L):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    st = _indexer(L, _batch())
+    assert st in (dsa.DSA_ERR_HIP, dsa.DSA_ERR_UNSUPPORTED)

@@ -1,0 +1,320 @@
+"""GPU parity of every stage of the DSA decode path against the fp64 oracle, through the C ABI.
+
+Sizes are chosen so the oracle finishes in seconds while the kernels still run several tiles
+and a ragged tail; the workload-sized cases live in test_gpu_fullsize.py.
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import dsa_inputs
+import sparse_attention_10_amd as dsa
+from oracle import dsa_oracle as O
+from tests.gpu_helpers import (DEV, batch_of, check_attention, check_indexer, gpu_mla, gpu_scores,
+                               oracle_mla, run_step)
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(name, lens, seed, **kw):
+    cfg = dsa_inputs.scaled_config(name, lens, seed=seed, **kw)
+    inp = dsa_inputs.make_inputs(cfg)
+    return cfg, inp, dsa_inputs.to_torch(inp, cfg, DEV)
+
+
+INDEXER_CASES = [
+    ("c1", [4096], dict()),                                           # f32, vector path
+    ("c2", [5000], dict()),                                           # bf16 matrix-core path, ragged tail
+    ("c3", [4133, 300, 1, 8191, 2050], dict()),                       # ragged batch
+    ("c5", [3000, 4097, 130], dict()),                                # fp8 keys, Q = 2
+    ("c4", [64 + 1000], dict(q_per_seq=64)),                          # prefill-style causal block
+    ("c2", [777, 65], dict(q_per_seq=3)),                             # odd Q (one row per block)
+    ("c2", [900], dict(idx_heads=8, idx_dim=32)),                     # vector path, bf16
+    ("c5", [700], dict(idx_heads=8, idx_dim=32, q_per_seq=1)),        # vector path, fp8
+    ("c2", [600], dict(page_size=16)),                                # another page size
+]
+
+
+@pytest.mark.parametrize("name,lens,kw", INDEXER_CASES, ids=[f"{c[0]}-{len(c[1])}x{max(c[1])}-{i}" for i, c in enumerate(INDEXER_CASES)])
+def test_indexer_parity(name, lens, kw):
+    cfg, inp, t = _case(name, lens, seed=101, **kw)
+    got = gpu_scores(cfg, t).cpu().numpy()
+    ref = O.indexer_scores(inp["q_idx"], cfg.q_idx_dtype, inp["w"], inp["k_cache"], cfg.key_dtype,
+                           inp["k_scale"], inp["seq_lens"], inp["page_table"], cfg.q_per_seq, cfg.page_size)
+    check_indexer(cfg, got, ref, inp["seq_lens"])
+    # columns at or past L_b are left untouched
+    for b, L in enumerate(cfg.seq_lens):
+        assert np.all(np.isnan(got[b, :, L:]))
+
+
+def _topk_gpu(scores_np, seq_lens, Q, k, page_table=None, P=64):
+    B = len(seq_lens)
+    ld = scores_np.shape[-1]
+    if page_table is None:
+        page_table = np.arange((ld + P - 1) // P, dtype=np.int32)[None, :].repeat(B, 0)
+    st = torch.from_numpy(np.ascontiguousarray(scores_np, dtype=np.float32)).to(DEV)
+    sl = torch.tensor(seq_lens, dtype=torch.int32, device=DEV)
+    pt = torch.from_numpy(np.ascontiguousarray(page_table)).to(DEV)
+    batch = dsa.make_batch(sl, pt, Q, P, ld, int(page_table.max() + 1) * P)
+    idx = torch.full((B, Q, k), -7, dtype=torch.int32, device=DEV)
+    slots = torch.full((B, Q, k), -7, dtype=torch.int32, device=DEV)
+    dsa.dsa_topk(batch, st, k, idx, slots)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), slots.cpu().numpy(), page_table
+
+
+def _topk_ref(scores_np, seq_lens, Q, k, page_table, P=64):
+    idx = O.topk(scores_np.astype(np.float64), seq_lens, Q, k)
+    return idx, O.page_map(idx, page_table, P)
+
+
+def _adversarial(kind, n, rng):
+    if kind == "levels":
+        return rng.choice(np.array([0.5, 0.25, 0.125, 1.0], np.float32), n)
+    if kind == "allequal":
+        return np.full(n, 0.375, np.float32)
+    if kind == "zeros":
+        return rng.choice(np.array([0.0, -0.0, 1e-30, -1e-30], np.float32), n)
+    if kind == "neginf":
+        x = rng.standard_normal(n).astype(np.float32)
+        x[rng.random(n) < 0.7] = -np.inf
+        return x
+    if kind == "mixedsign":
+        return (rng.standard_normal(n) * 1e3).astype(np.float32)
+    if kind == "narrow":   # scores in a narrow positive band, like the indexer's
+        return (0.0175 + 0.002 * rng.standard_normal(n)).astype(np.float32)
+    if kind == "dupes":    # two values dominate so the k-th value is heavily tied
+        x = np.full(n, 2.0, np.float32)
+        x[rng.random(n) < 0.01] = 3.0
+        return x
+    raise ValueError(kind)
+
+
+TOPK_CASES = [
+    ("narrow", [32768], 1, 2048), ("narrow", [70000], 1, 2048), ("narrow", [131072], 1, 2048),
+    ("levels", [5000, 3000], 1, 256), ("allequal", [4100], 1, 2048), ("zeros", [9000], 1, 1000),
+    ("neginf", [20000], 1, 2048), ("mixedsign", [12345], 1, 1), ("dupes", [50000], 1, 2048),
+    ("narrow", [2048, 2049, 10, 1], 1, 2048), ("narrow", [65536, 65536], 2, 2048),
+    ("mixedsign", [40000], 1, 8192), ("levels", [1025], 3, 1024),
+]
+
+
+@pytest.mark.parametrize("kind,lens,Q,k", TOPK_CASES, ids=[f"{c[0]}-{max(c[1])}-Q{c[2]}-k{c[3]}" for c in TOPK_CASES])
+def test_topk_bit_exact(kind, lens, Q, k):
+    rng = np.random.default_rng(zlib.crc32(f"{kind}-{lens}-{Q}-{k}".encode()))
+    ld = max(lens)
+    scores = np.stack([np.stack([_adversarial(kind, ld, rng) for _ in range(Q)]) for _ in lens])
+    B = len(lens)
+    pt = np.stack([rng.permutation((ld + 63) // 64).astype(np.int32) for _ in range(B)])
+    idx_g, slots_g, _ = _topk_gpu(scores, lens, Q, k, pt)
+    idx_r, slots_r = _topk_ref(scores, lens, Q, k, pt)
+    assert np.array_equal(idx_g, idx_r)
+    assert np.array_equal(slots_g, slots_r)
+
+
+def test_topk_on_indexer_scores_bit_exact():
+    cfg, inp, t = _case("c3", [9000, 4097, 70000], seed=102)
+    s = gpu_scores(cfg, t, fill=float("-inf"))
+    sn = s.cpu().numpy()
+    idx_g, slots_g, _ = _topk_gpu(sn, cfg.seq_lens, 1, cfg.top_k, inp["page_table"])
+    idx_r, slots_r = _topk_ref(sn, cfg.seq_lens, 1, cfg.top_k, inp["page_table"])
+    assert np.array_equal(idx_g, idx_r) and np.array_equal(slots_g, slots_r)
+
+
+def test_page_map_bit_exact():
+    rng = np.random.default_rng(5)
+    B, Q, k, P, maxP = 4, 2, 300, 64, 40
+    pt = rng.integers(0, 1000, (B, maxP)).astype(np.int32)
+    idx = rng.integers(-1, maxP * P, (B, Q, k)).astype(np.int32)
+    sl = torch.full((B,), maxP * P, dtype=torch.int32, device=DEV)
+    pt_d, idx_d = torch.from_numpy(pt).to(DEV), torch.from_numpy(idx).to(DEV)
+    batch = dsa.make_batch(sl, pt_d, Q, P, maxP * P, 1000 * P)
+    out = torch.full((B, Q, k), -7, dtype=torch.int32, device=DEV)
+    dsa.dsa_page_map(batch, idx_d, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), O.page_map(idx, pt, P))
+
+
+def _random_slots(cfg, rng, k, frac_invalid=0.0):
+    slots = np.stack([np.stack([rng.choice(cfg.num_slots, k, replace=False) for _ in range(cfg.q_per_seq)])
+                      for _ in range(cfg.batch)]).astype(np.int32)
+    if frac_invalid:
+        slots[rng.random(slots.shape) < frac_invalid] = -1
+    return slots
+
+
+MLA_CASES = [
+    # name, lens, k, H, n_split, invalid fraction
+    ("c2", [3000], 2048, 64, 1, 0.0),
+    ("c2", [3000], 2048, 64, 0, 0.0),
+    ("c2", [3000], 2048, 64, 7, 0.0),
+    ("c2", [3000], 2048, 64, 64, 0.0),
+    ("c2", [3000], 100, 64, 3, 0.1),
+    ("c3", [2500, 700, 4000], 512, 64, 0, 0.3),
+    ("c5", [3000, 2000], 2048, 64, 0, 0.0),
+    ("c5", [3000], 333, 64, 2, 0.05),
+    ("c2", [1500], 256, 16, 0, 0.0),
+    ("c2", [1500], 256, 32, 2, 0.0),
+    ("c2", [1500], 256, 48, 1, 0.0),
+    ("c1", [4096], 256, 16, 0, 0.0),
+    ("c1", [900], 300, 16, 0, 0.2),
+]
+
+
+@pytest.mark.parametrize("name,lens,k,H,ns,inv", MLA_CASES, ids=[f"{c[0]}-k{c[2]}-H{c[3]}-s{c[4]}-inv{c[5]}" for c in MLA_CASES])
+def test_sparse_mla_parity(name, lens, k, H, ns, inv):
+    Q = 2 if name == "c5" else 1
+    cfg, inp, t = _case(name, lens, seed=103, mla_heads=H, top_k=k, q_per_seq=Q)
+    rng = np.random.default_rng(7)
+    slots = _random_slots(cfg, rng, k, inv)
+    out, lse = gpu_mla(cfg, t, torch.from_numpy(slots).to(DEV), n_split=ns)
+    ro, rl = oracle_mla(cfg, inp, slots)
+    check_attention(out.cpu().numpy(), ro, lse.cpu().numpy(), rl)
+
+
+def test_sparse_mla_empty_selection_and_single_row():
+    cfg, inp, t = _case("c2", [500], seed=104, top_k=64)
+    slots = np.full((1, 1, 64), -1, np.int32)
+    out, lse = gpu_mla(cfg, t, torch.from_numpy(slots).to(DEV), n_split=2)
+    assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
+    slots[0, 0, 37] = 123
+    out, lse = gpu_mla(cfg, t, torch.from_numpy(slots).to(DEV), n_split=2)
+    ro, rl = oracle_mla(cfg, inp, slots)
+    check_attention(out.cpu().numpy(), ro, lse.cpu().numpy(), rl)
+    # one selected row: the output is that row's V (up to the bf16 P weight of exactly 1)
+    v = O.dequantize(inp["kv_cache"][123:124], "bf16")[0, :512]
+    assert np.abs(out.cpu().numpy()[0, 0] - v[None, :]).max() < 1e-6
+
+
+def test_split_combine_parity_direct():
+    rng = np.random.default_rng(9)
+    rows, ns, H = 3, 5, 64
+    m = rng.standard_normal((rows, ns, H)).astype(np.float32) * 3
+    l = (rng.random((rows, ns, H)) * 10).astype(np.float32)
+    l[0, 2, :] = 0.0
+    m[0, 2, :] = -np.inf
+    l[1, :, 5] = 0.0
+    m[1, :, 5] = -np.inf                      # (row 1, head 5) has no live chunk
+    o = rng.standard_normal((rows, ns, H, 512)).astype(np.float32)
+    out = torch.full((rows, H, 512), float("nan"), device=DEV)
+    lse = torch.full((rows, H), float("nan"), device=DEV)
+    dsa.dsa_mla_combine(torch.from_numpy(o).to(DEV), torch.from_numpy(m).to(DEV), torch.from_numpy(l).to(DEV),
+                        out, lse)
+    torch.cuda.synchronize()
+    for r in range(rows):
+        ro, rl = O.combine_splits(m[r].astype(np.float64), l[r].astype(np.float64), o[r].astype(np.float64))
+        assert np.abs(out[r].cpu().numpy() - ro).max() < 1e-5
+        lg = lse[r].cpu().numpy()
+        assert np.array_equal(np.isneginf(lg), np.isneginf(rl))
+        fin = np.isfinite(rl)
+        assert np.abs(lg[fin] - rl[fin]).max() < 1e-5
+
+
+@pytest.mark.parametrize("ns", [1, 2, 7, 32])
+def test_split_invariance_gpu(ns):
+    cfg, inp, t = _case("c2", [3000], seed=105)
+    slots = _random_slots(cfg, np.random.default_rng(11), cfg.top_k)
+    st = torch.from_numpy(slots).to(DEV)
+    out1, lse1 = gpu_mla(cfg, t, st, n_split=1)
+    outn, lsen = gpu_mla(cfg, t, st, n_split=ns)
+    assert torch.allclose(out1, outn, rtol=0, atol=1e-5)
+    assert torch.allclose(lse1, lsen, rtol=0, atol=1e-5)
+
+
+STEP_CASES = [("c1", [4096], dict()), ("c2", [6000], dict()), ("c3", [4100, 2500, 9000], dict()),
+              ("c5", [5000, 3000], dict()), ("c4", [64 + 3000], dict(q_per_seq=64, top_k=512))]
+
+
+@pytest.mark.parametrize("name,lens,kw", STEP_CASES, ids=[c[0] for c in STEP_CASES])
+def test_decode_step_staged(name, lens, kw):
+    """Staged protocol: (1) the step's scores against the oracle; (2) its selection against the
+    oracle's top-k run on the step's own f32 scores (bit-exact) and its slots against the page
+    map (bit-exact); (3) its attention output against the oracle on the step's own slots; and
+    (4) its selection against the oracle's fp64 selection, where every disagreement must sit
+    within 2e-5 * max|s| of the k-th score."""
+    cfg, inp, t = _case(name, lens, seed=106, **kw)
+    r = run_step(cfg, t)
+    s_g = r["scores"].cpu().numpy()
+    s_ref = O.indexer_scores(inp["q_idx"], cfg.q_idx_dtype, inp["w"], inp["k_cache"], cfg.key_dtype,
+                             inp["k_scale"], inp["seq_lens"], inp["page_table"], cfg.q_per_seq, cfg.page_size)
+    check_indexer(cfg, s_g, s_ref, inp["seq_lens"])
+    idx_g, slots_g = r["idx"].cpu().numpy(), r["slots"].cpu().numpy()
+    idx_r = O.topk(np.where(np.isnan(s_g), -np.inf, s_g).astype(np.float64), inp["seq_lens"], cfg.q_per_seq,
+                   cfg.top_k)
+    assert np.array_equal(idx_g, idx_r)
+    assert np.array_equal(slots_g, O.page_map(idx_g, inp["page_table"], cfg.page_size))
+    ro, rl = oracle_mla(cfg, inp, slots_g)
+    check_attention(r["out"].cpu().numpy(), ro, r["lse"].cpu().numpy(), rl)
+    # (4) the fp64 selection differs only near the k-th score
+    idx64 = O.topk(s_ref, inp["seq_lens"], cfg.q_per_seq, cfg.top_k)
+    pos = O.query_positions(inp["seq_lens"], cfg.q_per_seq)
+    for b in range(cfg.batch):
+        for i in range(cfg.q_per_seq):
+            a, c = set(idx_g[b, i][idx_g[b, i] >= 0]), set(idx64[b, i][idx64[b, i] >= 0])
+            if a == c:
+                continue
+            row = s_ref[b, i, :pos[b, i] + 1]
+            kth = np.sort(row)[::-1][cfg.top_k - 1]
+            for tok in a ^ c:
+                assert abs(row[tok] - kth) <= 2e-5 * np.abs(row).max()
+
+
+@pytest.mark.parametrize("name,lens,Q", [("c2", [1500], 1), ("c5", [700, 1200], 2), ("c1", [300], 1)])
+def test_decode_step_dense_when_k_covers_context(name, lens, Q):
+    """k >= context: the step must equal dense attention whatever the indexer's numerics."""
+    cfg, inp, t = _case(name, lens, seed=107, top_k=max(lens), q_per_seq=Q)
+    r = run_step(cfg, t, debug=False)
+    do, dl = O.dense_mla(inp["q_mla"], cfg.q_mla_dtype, inp["kv_cache"], cfg.kv_dtype, inp["kv_scale"],
+                         inp["seq_lens"], inp["page_table"], Q, cfg.page_size, cfg.sm_scale)
+    check_attention(r["out"].cpu().numpy(), do, r["lse"].cpu().numpy(), dl)
+
+
+def test_decode_step_deterministic():
+    cfg, inp, t = _case("c3", [5000, 3000, 7000], seed=108)
+    r1 = run_step(cfg, t)
+    r2 = run_step(cfg, t)
+    for key in ("out", "lse", "scores", "idx", "slots"):
+        a, b = r1[key].cpu(), r2[key].cpu()
+        assert torch.equal(a.view(torch.int32) if a.dtype == torch.float32 else a,
+                           b.view(torch.int32) if b.dtype == torch.float32 else b), key
+
+
+def test_decode_step_hip_graph_replay():
+    """The step captured in a HIP graph replays to the eager result, every replay."""
+    cfg, inp, t = _case("c2", [4000], seed=109)
+    B, Q, H, k = cfg.batch, cfg.q_per_seq, cfg.mla_heads, cfg.top_k
+    out = torch.zeros((B, Q, H, 512), dtype=torch.float32, device=DEV)
+    lse = torch.zeros((B, Q, H), dtype=torch.float32, device=DEV)
+    args = dsa.decode_step_args(batch_of(cfg, t), t["q_idx"], t["w"], t["k_cache"], t["k_scale"], k,
+                                t["q_mla"], t["kv_cache"], t["kv_scale"], cfg.sm_scale, out, lse)
+    ws = torch.empty(dsa.decode_step_workspace_bytes(args), dtype=torch.uint8, device=DEV)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        dsa.dsa_decode_step(args, ws, stream=s)
+    torch.cuda.synchronize()
+    eager_o, eager_l = out.clone(), lse.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        dsa.dsa_decode_step(args, ws, stream=s)
+    for rep in range(4):
+        out.zero_()
+        lse.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager_o), f"replay {rep}"
+        assert torch.equal(lse, eager_l), f"replay {rep}"
+
+
+def test_abi_errors_leave_outputs_untouched():
+    cfg, inp, t = _case("c2", [600], seed=110)
+    out = torch.full((1, 1, 64, 512), 3.0, device=DEV)
+    slots = torch.zeros((1, 1, 64), dtype=torch.int32, device=DEV)
+    with pytest.raises(dsa.DsaError) as e:
+        dsa.dsa_sparse_mla_decode(t["q_mla"][:, :, :8].contiguous(), t["kv_cache"], None, slots, 0.1,
+                                  out[:, :, :8].contiguous())
+    assert e.value.status == dsa.DSA_ERR_UNSUPPORTED
+    torch.cuda.synchronize()
+    assert torch.all(out == 3.0)
