@@ -4,8 +4,8 @@
 //
 // One 1024-thread workgroup per query row:
 //   1. scores -> order-preserving uint32 keys (-0.0 folded onto +0.0, so equal floats give
-//      equal keys); the first ITEMS*1024 keys of the row stay in registers, any rest is
-//      re-read from L2 on each pass.
+//      equal keys); the first ITEMS*1024 keys of the row (ITEMS <= 32) stay in registers, any
+//      rest is re-read from L2 on each pass.
 //   2. AND/OR reduction gives the bits all visible keys share; radix select then resolves
 //      the k-th largest key 11 bits at a time from the first bit that differs, with an LDS
 //      histogram per round.  If a round's winning bin holds exactly the missing count, the
@@ -286,10 +286,12 @@ __global__ __launch_bounds__(256) void page_map_kernel(const int32_t* idx, int64
 
 hipError_t launch_topk(const TopkParams& p, int rows, int max_seq_len, hipStream_t s) {
   const dim3 grid((unsigned)rows), block(kThreads);
+  // At most 32 keys per thread stay in registers (the 32-key variant already fills the 128
+  // VGPRs a 1024-thread workgroup allows); keys past 32K are re-read from L2 on each pass, so no
+  // variant needs scratch memory.
   if (max_seq_len <= 8 * kThreads) hipLaunchKernelGGL(topk_kernel<8>, grid, block, 0, s, p);
   else if (max_seq_len <= 16 * kThreads) hipLaunchKernelGGL(topk_kernel<16>, grid, block, 0, s, p);
-  else if (max_seq_len <= 32 * kThreads) hipLaunchKernelGGL(topk_kernel<32>, grid, block, 0, s, p);
-  else hipLaunchKernelGGL(topk_kernel<64>, grid, block, 0, s, p);
+  else hipLaunchKernelGGL(topk_kernel<32>, grid, block, 0, s, p);
   return hipGetLastError();
 }
 

@@ -18,9 +18,9 @@ from tests.gpu_helpers import (DEV, batch_of, check_attention, check_indexer, gp
 pytestmark = pytest.mark.gpu
 
 
-def _case(name, lens, seed, **kw):
+def _case(name, lens, seed, with_mla=True, with_indexer=True, **kw):
     cfg = dsa_inputs.scaled_config(name, lens, seed=seed, **kw)
-    inp = dsa_inputs.make_inputs(cfg)
+    inp = dsa_inputs.make_inputs(cfg, with_mla=with_mla, with_indexer=with_indexer)
     return cfg, inp, dsa_inputs.to_torch(inp, cfg, DEV)
 
 
@@ -34,12 +34,15 @@ INDEXER_CASES = [
     ("c2", [900], dict(idx_heads=8, idx_dim=32)),                     # vector path, bf16
     ("c5", [700], dict(idx_heads=8, idx_dim=32, q_per_seq=1)),        # vector path, fp8
     ("c2", [600], dict(page_size=16)),                                # another page size
+    # long contexts: several 128-token tiles per workgroup (work >= 4096 tiles)
+    ("c2", [131072, 131072, 60000, 60000, 60001, 59999, 4097, 77], dict()),
+    ("c5", [131072, 100000, 70000, 9000], dict()),                    # fp8, Q = 2, two tiles per workgroup
 ]
 
 
 @pytest.mark.parametrize("name,lens,kw", INDEXER_CASES, ids=[f"{c[0]}-{len(c[1])}x{max(c[1])}-{i}" for i, c in enumerate(INDEXER_CASES)])
 def test_indexer_parity(name, lens, kw):
-    cfg, inp, t = _case(name, lens, seed=101, **kw)
+    cfg, inp, t = _case(name, lens, seed=101, with_mla=False, **kw)
     got = gpu_scores(cfg, t).cpu().numpy()
     ref = O.indexer_scores(inp["q_idx"], cfg.q_idx_dtype, inp["w"], inp["k_cache"], cfg.key_dtype,
                            inp["k_scale"], inp["seq_lens"], inp["page_table"], cfg.q_per_seq, cfg.page_size)
@@ -98,6 +101,9 @@ TOPK_CASES = [
     ("neginf", [20000], 1, 2048), ("mixedsign", [12345], 1, 1), ("dupes", [50000], 1, 2048),
     ("narrow", [2048, 2049, 10, 1], 1, 2048), ("narrow", [65536, 65536], 2, 2048),
     ("mixedsign", [40000], 1, 8192), ("levels", [1025], 3, 1024),
+    # many long ragged rows at once: register part plus the streamed tail
+    ("narrow", [131072, 100000, 70001, 65537, 40000, 32769, 5000, 2049], 1, 2048),
+    ("dupes", [131072, 98304], 2, 2048),
 ]
 
 
@@ -115,7 +121,7 @@ def test_topk_bit_exact(kind, lens, Q, k):
 
 
 def test_topk_on_indexer_scores_bit_exact():
-    cfg, inp, t = _case("c3", [9000, 4097, 70000], seed=102)
+    cfg, inp, t = _case("c3", [9000, 4097, 70000], seed=102, with_mla=False)
     s = gpu_scores(cfg, t, fill=float("-inf"))
     sn = s.cpu().numpy()
     idx_g, slots_g, _ = _topk_gpu(sn, cfg.seq_lens, 1, cfg.top_k, inp["page_table"])
@@ -160,6 +166,9 @@ MLA_CASES = [
     ("c2", [1500], 256, 48, 1, 0.0),
     ("c1", [4096], 256, 16, 0, 0.0),
     ("c1", [900], 300, 16, 0, 0.2),
+    # many query rows at once (32 rows x 8 chunks; 64 sequences x 2 fp8 rows x 2 chunks)
+    ("c3", [200] * 32, 2048, 64, 0, 0.0),
+    ("c5", [300] * 64, 512, 64, 2, 0.0),
 ]
 
 
