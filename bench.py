@@ -48,6 +48,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time for the CPU baseline")
     ap.add_argument("--rotate", type=int, default=0, help="input replicas (0 = enough to exceed 512 MB)")
+    ap.add_argument("--n-split", type=int, default=0, help="MLA split-k chunks (0 = library default)")
     return ap.parse_args()
 
 
@@ -228,7 +229,8 @@ def main():
     for r in reps:
         batch = dsa.make_batch(r["seq_lens"], r["page_table"], Q, cfg.page_size, cfg.max_seq_len, big.num_slots)
         step_args.append(dsa.decode_step_args(batch, r["q_idx"], r["w"], r["k_cache"], r["k_scale"], k,
-                                               r["q_mla"], r["kv_cache"], r["kv_scale"], cfg.sm_scale, out, lse))
+                                               r["q_mla"], r["kv_cache"], r["kv_scale"], cfg.sm_scale, out, lse,
+                                               n_split=args.n_split))
     ws_bytes = max(dsa.decode_step_workspace_bytes(a) for a in step_args)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     lib = dsa.lib()
@@ -321,8 +323,8 @@ def main():
                                scores, stream=stream)
         dsa.dsa_topk(batches[0], scores, k, idx_t, slots_t, stream=stream)
     torch.cuda.synchronize()
-    ns = dsa.lib().dsa_sparse_mla_default_split(B, Q, H, k)
-    mla_ws_bytes = dsa.mla_workspace_bytes(B, Q, H, k, 0, dsa.dtype_code(reps[0]["q_mla"]))
+    ns = args.n_split or dsa.lib().dsa_sparse_mla_default_split(B, Q, H, k)
+    mla_ws_bytes = dsa.mla_workspace_bytes(B, Q, H, k, ns, dsa.dtype_code(reps[0]["q_mla"]))
     mla_ws = torch.empty(max(1, mla_ws_bytes), dtype=torch.uint8, device=dev)
     KS = max(20, min(K, 1000))
     # slots per replica (so the MLA stage alone gathers rows of the replica's own pages)
@@ -342,7 +344,7 @@ def main():
         "topk": lambda j: dsa.dsa_topk(batches[j % R], scores, k, idx_t, slots_t, stream=stream),
         "mla": lambda j: dsa.dsa_sparse_mla_decode(reps[j % R]["q_mla"], reps[j % R]["kv_cache"],
                                                    reps[j % R]["kv_scale"], rep_slots[j % R], cfg.sm_scale,
-                                                   out, lse, n_split=0, workspace=mla_ws, stream=stream),
+                                                   out, lse, n_split=ns, workspace=mla_ws, stream=stream),
     }
     for name, f in fns.items():
         _, ms = time_graph([(lambda j=j, f=f: f(j)) for j in range(KS)], stream)

@@ -307,6 +307,7 @@ dsa_status_t dsa_sparse_mla_decode(int32_t batch, int32_t q_per_seq, const void*
 dsa_status_t dsa_mla_combine(int32_t rows, int32_t n_heads, int32_t n_split, const float* part_o, const float* part_m,
                              const float* part_l, float* out, float* lse, void* stream) {
   DSA_REQUIRE(rows >= 0 && n_heads >= 1 && n_split >= 1, "combine: rows >= 0, n_heads >= 1, n_split >= 1");
+  DSA_SUPPORT(n_split <= 1024, "combine: n_split=%d above the supported maximum 1024", n_split);
   DSA_REQUIRE(part_o && part_m && part_l && out, "combine: partial arrays and out must be non-NULL");
   DSA_REQUIRE(aligned(part_o, 16) && aligned(out, 16) && aligned(part_m, 4) && aligned(part_l, 4) &&
                   (!lse || aligned(lse, 4)),

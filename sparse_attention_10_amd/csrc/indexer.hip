@@ -137,7 +137,7 @@ __global__ __launch_bounds__(256) void indexer_mfma_kernel(IndexerParams p) {
   const int tile_base = blockIdx.x * p.tiles_per_wg * kTile;
   if (tile_base >= L) return;                 // uniform early exit
   const int tile_end = min(L, tile_base + p.tiles_per_wg * kTile);
-  const int nrows = min(QB, p.Q - qb0);       // 1..QB valid query rows
+  const int nrows = QB;                       // the launcher picks QB dividing Q
   const int pos_last = L - p.Q + qb0 + nrows - 1;   // largest position in the block
 
   const int n_in_sub = lane & 31;
@@ -153,16 +153,20 @@ __global__ __launch_bounds__(256) void indexer_mfma_kernel(IndexerParams p) {
   KeyRaw<FP8> raw_cur;
   load_keys<FP8>(raw_cur, kc, s_cur, v_cur, half);
 
-  // stage q (bf16) and w for the block's query rows
+  // stage q (bf16) and w for the block's query rows (QB divides Q, so the block is always
+  // QB full rows); all loads are issued before the first LDS store
   {
     const int64_t row0 = (int64_t)b * p.Q + qb0;
     const u32x4* qsrc = (const u32x4*)((const __bf16*)p.q + row0 * kHi * kDi);
     u32x4* qdst = (u32x4*)&q_lds[0][0][0];
-    const int nvec = nrows * kHi * kDi / 8;
-    for (int e = threadIdx.x; e < QB * kHi * kDi / 8; e += 256)
-      qdst[e] = e < nvec ? qsrc[e] : u32x4{0, 0, 0, 0};
-    for (int e = threadIdx.x; e < QB * kHi; e += 256)
-      (&w_lds[0][0])[e] = e < nrows * kHi ? p.w[row0 * kHi + e] : 0.f;
+    constexpr int kPer = QB * kHi * kDi / 8 / 256;
+    u32x4 qv[kPer];
+#pragma unroll
+    for (int c = 0; c < kPer; ++c) qv[c] = qsrc[c * 256 + threadIdx.x];
+    const float wv = threadIdx.x < QB * kHi ? p.w[row0 * kHi + threadIdx.x] : 0.f;
+#pragma unroll
+    for (int c = 0; c < kPer; ++c) qdst[c * 256 + threadIdx.x] = qv[c];
+    if (threadIdx.x < QB * kHi) (&w_lds[0][0])[threadIdx.x] = wv;
   }
   __syncthreads();
 

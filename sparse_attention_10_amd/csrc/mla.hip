@@ -130,23 +130,32 @@ struct TileStage {
   u32x4 v[kPer];
 };
 
+// Gather one tile's rows into registers.  `sl_lds` is the workgroup's chunk of the slot list
+// staged in LDS (entry -1 for a skipped slot or a position past the chunk).  Every load is
+// issued unconditionally (a skipped slot reads row 0) so all of them are in flight together;
+// skipped rows are zeroed when the tile is stored.
 template <bool FP8>
-__device__ __forceinline__ void tile_load(TileStage<FP8>& st, const MlaParams& p, const int32_t* sl, int j_base,
-                                          int j_end) {
+__device__ __forceinline__ void tile_load(TileStage<FP8>& st, const MlaParams& p, const int32_t* sl_lds,
+                                          int tile_off) {
   constexpr int kPiecesPerRow = FP8 ? kRowDim / 16 : kRowDim * 2 / 16;   // 36 or 72
   const uint8_t* kv = (const uint8_t*)p.kv;
+  int64_t s[TileStage<FP8>::kPer];
 #pragma unroll
   for (int c = 0; c < TileStage<FP8>::kPer; ++c) {
     const int g = c * kNT + threadIdx.x;
-    const int tk = g / kPiecesPerRow, piece = g - tk * kPiecesPerRow;
-    const int j = j_base + tk;
-    int64_t s = -1;
-    if (g < kTT * kPiecesPerRow && j < j_end) s = sl[j];
-    if (s >= 0)
-      st.v[c] = __builtin_nontemporal_load((const u32x4*)(kv + s * (FP8 ? kRowDim : 2 * kRowDim)) + piece);
-    else
-      st.v[c] = u32x4{0, 0, 0, 0};
+    const int tk = min(g / kPiecesPerRow, kTT - 1);
+    s[c] = sl_lds[tile_off + tk];
   }
+#pragma unroll
+  for (int c = 0; c < TileStage<FP8>::kPer; ++c) {
+    const int g = c * kNT + threadIdx.x;
+    const int piece = g % kPiecesPerRow;
+    const int64_t row = s[c] < 0 ? 0 : s[c];
+    st.v[c] = __builtin_nontemporal_load((const u32x4*)(kv + row * (FP8 ? kRowDim : 2 * kRowDim)) + piece);
+  }
+#pragma unroll
+  for (int c = 0; c < TileStage<FP8>::kPer; ++c)
+    if (s[c] < 0) st.v[c] = u32x4{0, 0, 0, 0};
 }
 
 template <bool FP8>
@@ -180,6 +189,7 @@ template <bool FP8>
 __global__ __launch_bounds__(kNT) void mla_mfma_kernel(MlaParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t tile[2][kTT * kPitch];
   __shared__ float tok_scale[2][kTT];             // per-token scale (fp8) or 1; 0 marks a skipped slot
+  __shared__ int32_t sl_lds[kMaxTopK + kTT];      // this chunk's slots, -1 padded to whole tiles
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -207,25 +217,40 @@ __global__ __launch_bounds__(kNT) void mla_mfma_kernel(MlaParams p) {
   float l_run = 0.f;         // this lane group's share of sum exp2(z - m_run)
   const float scale2 = p.sm_scale * kLog2e;
 
+  // stage the chunk's slot list (one coalesced pass, every load issued before any is used)
+  {
+    const int span = ntiles * kTT;
+    for (int e0 = 0; e0 < span; e0 += 4 * kNT) {
+      int32_t v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = sl[min(j0 + e0 + u * kNT + (int)threadIdx.x, p.k - 1)];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = e0 + u * kNT + threadIdx.x;
+        if (e < span) sl_lds[e] = j0 + e < j1 ? v[u] : -1;
+      }
+    }
+  }
+  __syncthreads();
+
   TileStage<FP8> st;
-  auto stage_scales = [&](int buf, int jb) {
+  auto stage_scales = [&](int buf, int off) {
     if (threadIdx.x < kTT) {
-      const int j = jb + threadIdx.x;
-      const int64_t s = j < j1 ? sl[j] : -1;
+      const int64_t s = sl_lds[off + threadIdx.x];
       tok_scale[buf][threadIdx.x] = s < 0 ? 0.f : (FP8 ? p.kv_scale[s] : 1.f);
     }
   };
   if (ntiles > 0) {
-    tile_load<FP8>(st, p, sl, j0, j1);
+    tile_load<FP8>(st, p, sl_lds, 0);
+    stage_scales(0, 0);
     tile_store<FP8>(st, tile[0]);
-    stage_scales(0, j0);
   }
   __syncthreads();
 
   for (int it = 0; it < ntiles; ++it) {
     const int buf = it & 1;
     const bool more = it + 1 < ntiles;
-    if (more) tile_load<FP8>(st, p, sl, j0 + (it + 1) * kTT, j1);
+    if (more) tile_load<FP8>(st, p, sl_lds, (it + 1) * kTT);
     if (active) {
       const uint8_t* T = tile[buf];
       // ---- S^T for two 16-token blocks; block beta row m holds token 8*(m/4) + 4*beta + m%4
@@ -257,19 +282,23 @@ __global__ __launch_bounds__(kNT) void mla_mfma_kernel(MlaParams p) {
         }
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      const bool need = tmax > m_run + 8.f || (m_run == -INFINITY && tmax > -INFINITY);
+      // the running maximum moves when this tile exceeds it by more than 2^8 (or on the first
+      // live tile, where the accumulator is still zero and needs no rescale)
+      const bool first = m_run == -INFINITY && tmax > -INFINITY;
+      const bool need = tmax > m_run + 8.f && !first;
       if (__any(need)) {
         const float m_new = need ? tmax : m_run;
-        const float alpha = need ? (m_run == -INFINITY ? 0.f : exp2f(m_run - m_new)) : 1.f;
+        const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
         m_run = m_new;
         l_run *= alpha;
 #pragma unroll
         for (int db = 0; db < 32; ++db) o[db] *= alpha;
       }
+      m_run = first ? tmax : m_run;
       bf16x8 pb;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float pe = z[e] == -INFINITY ? 0.f : exp2f(z[e] - m_run);
+        const float pe = z[e] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(z[e] - m_run);
         l_run += pe;
         pb[e] = (__bf16)(FP8 ? pe * sc[e] : pe);
       }
@@ -288,8 +317,8 @@ __global__ __launch_bounds__(kNT) void mla_mfma_kernel(MlaParams p) {
       }
     }
     if (more) {
+      stage_scales(buf ^ 1, (it + 1) * kTT);
       tile_store<FP8>(st, tile[buf ^ 1]);
-      stage_scales(buf ^ 1, j0 + (it + 1) * kTT);
     }
     __syncthreads();
   }
@@ -318,33 +347,78 @@ __global__ __launch_bounds__(kNT) void mla_mfma_kernel(MlaParams p) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// split-k merge: one 128-thread workgroup per (row, head), 4 values per thread
+// split-k merge.  One 256-thread workgroup per (row, head, 128-value quarter of the output):
+// thread (g, q) sums chunks j = g, g+8, ... for output values 4q..4q+3 of the quarter, with its
+// loads issued in batches; the 8 per-group sums are then added in LDS in a fixed order, so the
+// result does not depend on scheduling.
 
-__global__ __launch_bounds__(128) void mla_combine_kernel(CombineParams p) {
-  const int r = blockIdx.x / p.H, h = blockIdx.x - (blockIdx.x / p.H) * p.H;
-  float M = -INFINITY;
-  for (int j = 0; j < p.n_split; ++j) {
-    const int64_t pr = ((int64_t)r * p.n_split + j) * p.H + h;
-    if (p.part_l[pr] > 0.f) M = fmaxf(M, p.part_m[pr]);
+constexpr int kCombGroups = 8;
+
+__global__ __launch_bounds__(256) void mla_combine_kernel(CombineParams p) {
+  __shared__ float w_lds[1024];                    // a_j = exp(m_j - M) * l_j (0 for empty chunks)
+  __shared__ float red[kCombGroups][128];
+  __shared__ float s_M, s_den;
+  const int dq = blockIdx.x & 3;
+  const int rh = blockIdx.x >> 2;
+  const int r = rh / p.H, h = rh - (rh / p.H) * p.H;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int ns = p.n_split;
+  const int64_t base = (int64_t)r * ns * p.H + h;  // partial row of chunk j: base + j * H
+
+  if (tid < 64) {                                  // wave 0: live maximum and denominator
+    float M = -INFINITY;
+    for (int j = lane; j < ns; j += 64) {
+      const float lj = p.part_l[base + (int64_t)j * p.H];
+      if (lj > 0.f) M = fmaxf(M, p.part_m[base + (int64_t)j * p.H]);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    float den = 0.f;
+    for (int j = lane; j < ns; j += 64) {
+      const float lj = p.part_l[base + (int64_t)j * p.H];
+      const float a = (lj > 0.f && M != -INFINITY) ? expf(p.part_m[base + (int64_t)j * p.H] - M) * lj : 0.f;
+      w_lds[j] = a;
+      den += a;
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) den += __shfl_xor(den, off);
+    if (lane == 0) {
+      s_M = M;
+      s_den = den;
+    }
   }
-  float* dst = p.out + ((int64_t)r * p.H + h) * kVDim + threadIdx.x * 4;
-  if (M == -INFINITY) {
-    *(f32x4*)dst = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (p.lse && threadIdx.x == 0) p.lse[(int64_t)r * p.H + h] = -INFINITY;
-    return;
-  }
-  float den = 0.f;
+  __syncthreads();
+  const int g = tid >> 5, q = tid & 31;
+  const int col = dq * 128 + q * 4;
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < p.n_split; ++j) {
-    const int64_t pr = ((int64_t)r * p.n_split + j) * p.H + h;
-    const float lj = p.part_l[pr];
-    if (!(lj > 0.f)) continue;
-    const float a = expf(p.part_m[pr] - M) * lj;
-    den += a;
-    acc += a * *(const f32x4*)(p.part_o + pr * kVDim + threadIdx.x * 4);
+  constexpr int kB = 4;
+  for (int j0 = g; j0 < ns; j0 += kB * kCombGroups) {
+    f32x4 v[kB];
+#pragma unroll
+    for (int u = 0; u < kB; ++u) {
+      const int j = min(j0 + u * kCombGroups, ns - 1);
+      v[u] = *(const f32x4*)(p.part_o + (base + (int64_t)j * p.H) * kVDim + col);
+    }
+#pragma unroll
+    for (int u = 0; u < kB; ++u) {
+      const int j = j0 + u * kCombGroups;
+      if (j < ns) {
+        const float a = w_lds[j];
+        if (a > 0.f) acc += a * v[u];              // (an empty chunk's values are never read)
+      }
+    }
   }
-  *(f32x4*)dst = acc * (1.f / den);
-  if (p.lse && threadIdx.x == 0) p.lse[(int64_t)r * p.H + h] = M + logf(den);
+  *(f32x4*)&red[g][q * 4] = acc;
+  __syncthreads();
+  if (g == 0) {
+    f32x4 t = *(const f32x4*)&red[0][q * 4];
+#pragma unroll
+    for (int gg = 1; gg < kCombGroups; ++gg) t += *(const f32x4*)&red[gg][q * 4];
+    float* dst = p.out + ((int64_t)r * p.H + h) * kVDim + col;
+    const bool live = s_M != -INFINITY;
+    *(f32x4*)dst = live ? t * (1.f / s_den) : f32x4{0.f, 0.f, 0.f, 0.f};
+    if (p.lse && dq == 0 && q == 0) p.lse[(int64_t)r * p.H + h] = live ? s_M + logf(s_den) : -INFINITY;
+  }
 }
 
 }  // namespace
@@ -384,7 +458,7 @@ hipError_t launch_mla(const MlaParams& p0, dsa_dtype_t q_dtype, dsa_dtype_t kv_d
 
 hipError_t launch_combine(const CombineParams& c, hipStream_t s) {
   if (c.rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)(c.rows * c.H)), dim3(128), 0, s, c);
+  hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)(c.rows * c.H * 4)), dim3(256), 0, s, c);
   return hipGetLastError();
 }
 
