@@ -390,6 +390,7 @@ def main():
         "storage_dtype": {"f32": "f32", "bf16": "bf16", "fp8": "fp8_e4m3fn"}[cfg.kv_dtype],
         "data": "synthetic (seeded, device-generated; pages rotated over %d replicas)" % R,
         "config": {"workload": {"c1": "tiny fp32 decode, 4K ctx", "c2": "single-stream decode layer, 32K ctx",
+                                "c2_128k": "single-stream decode layer, 128K ctx",
                                 "c3": "batch-32 ragged decode, 4K-128K ctx",
                                 "c4": "4096-token chunked prefill over 64K ctx",
                                 "c5": "fp8 decode, batch 64 x 2 verify rows, 64K ctx"}[cfg.name],

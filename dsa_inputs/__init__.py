@@ -79,9 +79,9 @@ def _std(d: int) -> float:
 
 
 def base_config(name: str, seed: Optional[int] = None) -> DsaConfig:
-    """The five workloads, by name: c1 (tiny fp32), c2 (32K single stream),
-    c3 (batch 32, ragged 4K-128K), c4 (4096-token chunked prefill over a 64K
-    prefix), c5 (fp8 caches, batch 64 x 2 speculative-verify rows at 64K)."""
+    """The workloads, by name: c1 (tiny fp32), c2 (32K single stream), c2_128k (the
+    same layer at 128K), c3 (batch 32, ragged 4K-128K), c4 (4096-token chunked prefill
+    over a 64K prefix), c5 (fp8 caches, batch 64 x 2 speculative-verify rows at 64K)."""
     name = name.lower()
     s = 1000 + int(name[1]) if seed is None else seed
     if name == "c1":
@@ -93,6 +93,9 @@ def base_config(name: str, seed: Optional[int] = None) -> DsaConfig:
                   sm_scale=1.0 / math.sqrt(576), seed=s)
     if name == "c2":
         return DsaConfig("c2", 1, 1, [32768], **common)
+    if name == "c2_128k":      # the single-stream decode layer at a 128K context
+        common["seed"] = 1006 if seed is None else seed
+        return DsaConfig("c2_128k", 1, 1, [131072], **common)
     if name == "c3":
         rng = np.random.default_rng([s, _T_LENS])
         lens = rng.integers(4096, 131072, size=32, endpoint=True).tolist()
