@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time for the CPU baseline")
     ap.add_argument("--rotate", type=int, default=0, help="input replicas (0 = enough to exceed 512 MB)")
     ap.add_argument("--n-split", type=int, default=0, help="MLA split-k chunks (0 = library default)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run 10 plain 1 GiB device copies (reference for the FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
 
 
@@ -200,8 +202,23 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def copy_calibration():
+    """10 device-to-device copies of 1 GiB: under rocprofv3 --pmc FETCH_SIZE (WRITE_SIZE) each
+    copy dispatch should read (write) 1 GiB = 1048576 KiB; the ratio scales the counters."""
+    import torch
+    src = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(10):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_dispatch": src.numel() * 4, "dispatches": 10}))
+
+
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (got --gpus {args.gpus}): the path is single-GPU, "
               "see the sharding notes in DESIGN.md", file=sys.stderr)
@@ -362,7 +379,9 @@ def main():
     fl = step_flops(cfg, lens)
     stage_info = {
         "indexer": dict(us=stage["indexer"] * 1e3, bytes=by["indexer"], flops=fl["indexer"]),
-        "topk": dict(us=stage["topk"] * 1e3, bytes=rows * ld * 4),
+        # top-k reads each visible score once and writes k indices and k slots per row
+        "topk": dict(us=stage["topk"] * 1e3,
+                     bytes=sum(sum(L - Q + i + 1 for i in range(Q)) for L in lens) * 4 + rows * k * 8),
         "mla": dict(us=stage["mla"] * 1e3, bytes=by["mla"], flops=fl["mla"]),
     }
     if "combine" in stage:
@@ -370,9 +389,11 @@ def main():
     for v in stage_info.values():
         v["GBps"] = round(v["bytes"] / (v["us"] * 1e-6) / 1e9, 1)
         v["us"] = round(v["us"], 3)
-    dom = max(("indexer", "mla"), key=lambda s: stage_info[s]["us"])
-    kern = {"indexer": "indexer_mfma_kernel", "mla": "mla_mfma_kernel"}[dom]
-    if cfg.name == "c4":
+    # the dominant kernel: the stage with the largest average launch time
+    dom = max(stage_info, key=lambda s: stage_info[s]["us"])
+    kern = {"indexer": "indexer_mfma_kernel", "mla": "mla_mfma_kernel", "topk": "topk_kernel",
+            "combine": "mla_combine_kernel"}[dom]
+    if cfg.name == "c4" and dom in ("indexer", "mla"):
         ach = stage_info[dom]["flops"] / (stage_info[dom]["us"] * 1e-6) / 1e12
         roof = dict(bound="mfma", achieved=round(ach, 2), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
                     frac=round(ach / BF16_PEAK_TFLOPS, 4))
