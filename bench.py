@@ -249,7 +249,7 @@ def main():
                                                r["q_mla"], r["kv_cache"], r["kv_scale"], cfg.sm_scale, out, lse,
                                                n_split=args.n_split))
     ws_bytes = max(dsa.decode_step_workspace_bytes(a) for a in step_args)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
     lib = dsa.lib()
     import ctypes
     sptr = stream.cuda_stream
@@ -274,7 +274,7 @@ def main():
         dbg = dsa.decode_step_args(a0._keep[0], reps[0]["q_idx"], reps[0]["w"], reps[0]["k_cache"],
                                    reps[0]["k_scale"], k, reps[0]["q_mla"], reps[0]["kv_cache"],
                                    reps[0]["kv_scale"], cfg.sm_scale, out, lse, debug_idx=idx)
-        dsa.dsa_decode_step(dbg, torch.empty(dsa.decode_step_workspace_bytes(dbg), dtype=torch.uint8, device=dev),
+        dsa.dsa_decode_step(dbg, torch.zeros(dsa.decode_step_workspace_bytes(dbg), dtype=torch.uint8, device=dev),
                             stream=stream)
         torch.cuda.synchronize()
         ii = idx.cpu().numpy()
@@ -334,11 +334,13 @@ def main():
     idx_t = torch.empty((B, Q, k), dtype=torch.int32, device=dev)
     slots_t = torch.empty((B, Q, k), dtype=torch.int32, device=dev)
     batches = [a._keep[0] for a in step_args]
+    topk_ws = torch.zeros(max(1, max(dsa.topk_workspace_bytes(bt, k) for bt in batches)), dtype=torch.uint8,
+                          device=dev)
     # fill scores / slots once so the isolated stages see realistic data
     with torch.cuda.stream(stream):
         dsa.dsa_indexer_scores(batches[0], reps[0]["q_idx"], reps[0]["w"], reps[0]["k_cache"], reps[0]["k_scale"],
                                scores, stream=stream)
-        dsa.dsa_topk(batches[0], scores, k, idx_t, slots_t, stream=stream)
+        dsa.dsa_topk(batches[0], scores, k, idx_t, slots_t, workspace=topk_ws, stream=stream)
     torch.cuda.synchronize()
     ns = args.n_split or dsa.lib().dsa_sparse_mla_default_split(B, Q, H, k)
     mla_ws_bytes = dsa.mla_workspace_bytes(B, Q, H, k, ns, dsa.dtype_code(reps[0]["q_mla"]))
@@ -351,14 +353,15 @@ def main():
         with torch.cuda.stream(stream):
             dsa.dsa_indexer_scores(batches[r], reps[r]["q_idx"], reps[r]["w"], reps[r]["k_cache"],
                                    reps[r]["k_scale"], scores, stream=stream)
-            dsa.dsa_topk(batches[r], scores, k, idx_t, sl, stream=stream)
+            dsa.dsa_topk(batches[r], scores, k, idx_t, sl, workspace=topk_ws, stream=stream)
         rep_slots.append(sl)
     torch.cuda.synchronize()
     fns = {
         "indexer": lambda j: dsa.dsa_indexer_scores(batches[j % R], reps[j % R]["q_idx"], reps[j % R]["w"],
                                                     reps[j % R]["k_cache"], reps[j % R]["k_scale"], scores,
                                                     stream=stream),
-        "topk": lambda j: dsa.dsa_topk(batches[j % R], scores, k, idx_t, slots_t, stream=stream),
+        "topk": lambda j: dsa.dsa_topk(batches[j % R], scores, k, idx_t, slots_t, workspace=topk_ws,
+                                       stream=stream),
         "mla": lambda j: dsa.dsa_sparse_mla_decode(reps[j % R]["q_mla"], reps[j % R]["kv_cache"],
                                                    reps[j % R]["kv_scale"], rep_slots[j % R], cfg.sm_scale,
                                                    out, lse, n_split=ns, workspace=mla_ws, stream=stream),

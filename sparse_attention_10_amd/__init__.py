@@ -148,12 +148,21 @@ def dsa_indexer_scores(batch: DsaBatch, q: torch.Tensor, w: torch.Tensor, k_cach
     return scores
 
 
+def topk_workspace_bytes(batch: DsaBatch, k: int) -> int:
+    return lib().dsa_topk_workspace_size(ctypes.byref(batch), k)
+
+
 def dsa_topk(batch: DsaBatch, scores: torch.Tensor, k: int, topk_idx: torch.Tensor,
-             topk_slots: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    ws = lib().dsa_topk_workspace_size(ctypes.byref(batch), k)
-    wst = torch.empty(ws, dtype=torch.uint8, device=scores.device) if ws else None
+             topk_slots: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+             stream=None) -> torch.Tensor:
+    """Top-k with the fused page map (see dsa.h).  A workspace passed in must be zero-filled
+    before its first use; the call leaves it zero-filled.  Without one a zeroed buffer is made."""
+    need = topk_workspace_bytes(batch, k)
+    if workspace is None and need:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=scores.device)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().dsa_topk(ctypes.byref(batch), _ptr(scores), scores.shape[-1], k, _ptr(topk_idx),
-                          _ptr(topk_slots), _ptr(wst), ws, _stream(stream)))
+                          _ptr(topk_slots), _ptr(workspace), nbytes, _stream(stream)))
     return topk_idx
 
 

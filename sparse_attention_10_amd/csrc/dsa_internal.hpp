@@ -94,7 +94,10 @@ struct CombineParams {
 hipError_t launch_indexer(const IndexerParams& p, dsa_dtype_t q_dtype, dsa_dtype_t k_dtype,
                           hipStream_t s);
 bool indexer_uses_mfma(int Hi, int Di, dsa_dtype_t q_dtype, dsa_dtype_t k_dtype);
-hipError_t launch_topk(const TopkParams& p, int rows, int max_seq_len, hipStream_t s);
+// Top-k: `ws` is topk_workspace_bytes(rows, max_seq_len) bytes of zero-filled device memory
+// (left zero-filled by the launch), or unused when that size is 0.
+size_t topk_workspace_bytes(int64_t rows, int max_seq_len);
+hipError_t launch_topk(const TopkParams& p, int rows, int max_seq_len, void* ws, hipStream_t s);
 hipError_t launch_page_map(const int32_t* idx, int64_t total, int k, int Q, const int32_t* pt,
                            int maxP, int P, int32_t* slots, hipStream_t s);
 hipError_t launch_mla(const MlaParams& p, dsa_dtype_t q_dtype, dsa_dtype_t kv_dtype, hipStream_t s);

@@ -99,7 +99,7 @@ def run_step(cfg, t, n_split=0, debug=True):
                                 t["q_mla"], t["kv_cache"], t["kv_scale"], cfg.sm_scale, out, lse, n_split,
                                 dbg_s, dbg_i, dbg_l)
     nbytes = dsa.decode_step_workspace_bytes(args)
-    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=DEV)
     dsa.dsa_decode_step(args, ws)
     torch.cuda.synchronize()
     return dict(out=out, lse=lse, scores=dbg_s, idx=dbg_i, slots=dbg_l)

@@ -52,7 +52,7 @@ def test_indexer_parity(name, lens, kw):
         assert np.all(np.isnan(got[b, :, L:]))
 
 
-def _topk_gpu(scores_np, seq_lens, Q, k, page_table=None, P=64):
+def _topk_gpu(scores_np, seq_lens, Q, k, page_table=None, P=64, workspace=None):
     B = len(seq_lens)
     ld = scores_np.shape[-1]
     if page_table is None:
@@ -63,7 +63,7 @@ def _topk_gpu(scores_np, seq_lens, Q, k, page_table=None, P=64):
     batch = dsa.make_batch(sl, pt, Q, P, ld, int(page_table.max() + 1) * P)
     idx = torch.full((B, Q, k), -7, dtype=torch.int32, device=DEV)
     slots = torch.full((B, Q, k), -7, dtype=torch.int32, device=DEV)
-    dsa.dsa_topk(batch, st, k, idx, slots)
+    dsa.dsa_topk(batch, st, k, idx, slots, workspace=workspace)
     torch.cuda.synchronize()
     return idx.cpu().numpy(), slots.cpu().numpy(), page_table
 
@@ -290,15 +290,43 @@ def test_decode_step_deterministic():
                            b.view(torch.int32) if b.dtype == torch.float32 else b), key
 
 
+# Long rows: the candidate path and the narrowing rounds (a bin of more than 4096 equal keys),
+# rows that need no selection in the same launch, a page size that is not a power of two, a k
+# above the candidate cap, and rows whose scores start off 16-byte alignment (Q = 2, odd ld).
+LONG_CASES = [
+    ("narrow", [40000, 1000, 23456], 1, 2048, 64),
+    ("zeros", [40000], 1, 2048, 64),
+    ("levels", [33000, 17000], 1, 3000, 48),
+    ("allequal", [65536], 1, 8192, 64),
+    ("mixedsign", [16384, 16385], 2, 1, 64),
+    ("narrow", [262144], 1, 2048, 64),
+    ("narrow", [30001, 29999, 777], 3, 2048, 64),
+    ("dupes", [70001, 5], 1, 100, 16),
+]
+
+
+@pytest.mark.parametrize("kind,lens,Q,k,P", LONG_CASES, ids=[f"{c[0]}-{len(c[1])}x{max(c[1])}-Q{c[2]}-k{c[3]}-P{c[4]}" for c in LONG_CASES])
+def test_topk_long_rows(kind, lens, Q, k, P):
+    rng = np.random.default_rng(zlib.crc32(f"coop-{kind}-{lens}-{Q}-{k}-{P}".encode()))
+    ld = max(lens)
+    scores = np.stack([np.stack([_adversarial(kind, ld, rng) for _ in range(Q)]) for _ in lens])
+    B = len(lens)
+    pt = np.stack([rng.permutation((ld + P - 1) // P).astype(np.int32) for _ in range(B)])
+    idx_g, slots_g, _ = _topk_gpu(scores, lens, Q, k, pt, P=P)
+    idx_r, slots_r = _topk_ref(scores, lens, Q, k, pt, P=P)
+    assert np.array_equal(idx_g, idx_r)
+    assert np.array_equal(slots_g, slots_r)
+
+
 def test_decode_step_hip_graph_replay():
     """The step captured in a HIP graph replays to the eager result, every replay."""
-    cfg, inp, t = _case("c2", [4000], seed=109)
+    cfg, inp, t = _case("c2", [40000], seed=109)
     B, Q, H, k = cfg.batch, cfg.q_per_seq, cfg.mla_heads, cfg.top_k
     out = torch.zeros((B, Q, H, 512), dtype=torch.float32, device=DEV)
     lse = torch.zeros((B, Q, H), dtype=torch.float32, device=DEV)
     args = dsa.decode_step_args(batch_of(cfg, t), t["q_idx"], t["w"], t["k_cache"], t["k_scale"], k,
                                 t["q_mla"], t["kv_cache"], t["kv_scale"], cfg.sm_scale, out, lse)
-    ws = torch.empty(dsa.decode_step_workspace_bytes(args), dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(dsa.decode_step_workspace_bytes(args), dtype=torch.uint8, device=DEV)
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
         dsa.dsa_decode_step(args, ws, stream=s)
