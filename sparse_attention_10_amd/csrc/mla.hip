@@ -3,11 +3,12 @@
 // 512 values, weight-absorbed and without GQA (Show HN "Chay GLM 5.2 tren may tinh cham",
 // main-features section).
 //
-// mla_mfma_kernel: one workgroup = 4 waves = one query row x one chunk of its selected slots
-// (split-k).  Wave w owns heads [16w, 16w+16).  Per 32-token tile:
+// mla_mfma_kernel: one workgroup = 8 waves = one query row x one chunk of its selected slots
+// (split-k).  A pair of waves owns 16 heads, one wave per half of the K dims (S^T) and of the
+// output dims (P.V).  Per 32-token tile:
 //   * the tile's rows are gathered from HBM (16-byte loads, one row = 72 of them; fp8 rows are
-//     widened to bf16 in registers) into LDS, double-buffered so the next tile's loads are in
-//     flight while this one is computed;
+//     widened to bf16 in registers) into LDS, double-buffered, with the next two tiles' loads
+//     in flight while this one is computed;
 //   * S^T = rows . q^T on v_mfma_f32_16x16x32_bf16 (M = 16 tokens, N = 16 heads, K = 576 in 18
 //     steps, q held in registers).  The two 16-token blocks are chosen so that each lane ends
 //     up with 8 consecutive tokens of one head, exactly the K slice the P.V product needs;
@@ -116,60 +117,69 @@ __global__ __launch_bounds__(256) void mla_valu_kernel(MlaParams p) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// matrix-core path (bf16 q, bf16 or fp8 rows, H = 16 * active waves <= 64)
+// matrix-core path (bf16 q, bf16 or fp8 rows, H = 16 * head groups <= 64)
+//
+// 512 threads = 8 waves, two per SIMD.  Wave w works on head group hg = w % 4 (heads
+// 16hg..16hg+15) and half kh = w / 4: for S^T it covers the K dims [288kh, 288kh+288), for
+// P.V the output dims [256kh, 256kh+256).  The two waves of a head group add their S^T halves
+// through LDS in a fixed order (half 0 + half 1), so both hold identical logits and run the
+// same online softmax.
 
 constexpr int kTT = 32;                          // tokens per tile
 constexpr int kPitch = kRowDim * 2 + 16;          // LDS bytes per bf16 row (+16 against bank conflicts)
-constexpr int kNT = 256;                          // threads per workgroup
+constexpr int kNT = 512;                          // threads per workgroup
 constexpr int kChunksBf16 = kTT * (kRowDim * 2 / 16);   // 2304 16-byte pieces per tile
 constexpr int kChunksFp8 = kTT * (kRowDim / 16);        // 1152
+constexpr int kKSteps = kRowDim / 32 / 2;               // 9 K steps of 32 per half
+constexpr int kDBlocks = kVDim / 16 / 2;                // 16 output blocks of 16 per half
 
 template <bool FP8>
 struct TileStage {
-  static constexpr int kPer = FP8 ? (kChunksFp8 + kNT - 1) / kNT : kChunksBf16 / kNT;   // 5 or 9
+  static constexpr int kPer = ((FP8 ? kChunksFp8 : kChunksBf16) + kNT - 1) / kNT;   // 3 or 5
   u32x4 v[kPer];
 };
 
 // Gather one tile's rows into registers.  `sl_lds` is the workgroup's chunk of the slot list
 // staged in LDS (entry -1 for a skipped slot or a position past the chunk).  Every load is
-// issued unconditionally (a skipped slot reads row 0) so all of them are in flight together;
-// skipped rows are zeroed when the tile is stored.
+// issued unconditionally (a skipped slot, or a piece past the tile, reads row 0) and nothing
+// here reads the results, so the loads stay in flight until the tile is stored, which is also
+// where skipped rows are zeroed.
 template <bool FP8>
 __device__ __forceinline__ void tile_load(TileStage<FP8>& st, const MlaParams& p, const int32_t* sl_lds,
                                           int tile_off) {
   constexpr int kPiecesPerRow = FP8 ? kRowDim / 16 : kRowDim * 2 / 16;   // 36 or 72
+  constexpr int kPieces = kTT * kPiecesPerRow;
   const uint8_t* kv = (const uint8_t*)p.kv;
   int64_t s[TileStage<FP8>::kPer];
 #pragma unroll
   for (int c = 0; c < TileStage<FP8>::kPer; ++c) {
-    const int g = c * kNT + threadIdx.x;
-    const int tk = min(g / kPiecesPerRow, kTT - 1);
-    s[c] = sl_lds[tile_off + tk];
+    const int g = min(c * kNT + (int)threadIdx.x, kPieces - 1);
+    s[c] = sl_lds[tile_off + g / kPiecesPerRow];
   }
 #pragma unroll
   for (int c = 0; c < TileStage<FP8>::kPer; ++c) {
-    const int g = c * kNT + threadIdx.x;
+    const int g = min(c * kNT + (int)threadIdx.x, kPieces - 1);
     const int piece = g % kPiecesPerRow;
     const int64_t row = s[c] < 0 ? 0 : s[c];
     st.v[c] = __builtin_nontemporal_load((const u32x4*)(kv + row * (FP8 ? kRowDim : 2 * kRowDim)) + piece);
   }
-#pragma unroll
-  for (int c = 0; c < TileStage<FP8>::kPer; ++c)
-    if (s[c] < 0) st.v[c] = u32x4{0, 0, 0, 0};
 }
 
 template <bool FP8>
-__device__ __forceinline__ void tile_store(const TileStage<FP8>& st, uint8_t* lds) {
+__device__ __forceinline__ void tile_store(const TileStage<FP8>& st, uint8_t* lds, const int32_t* sl_lds,
+                                           int tile_off) {
   constexpr int kPiecesPerRow = FP8 ? kRowDim / 16 : kRowDim * 2 / 16;
 #pragma unroll
   for (int c = 0; c < TileStage<FP8>::kPer; ++c) {
     const int g = c * kNT + threadIdx.x;
     if (g >= kTT * kPiecesPerRow) continue;
     const int tk = g / kPiecesPerRow, piece = g - tk * kPiecesPerRow;
+    const bool skip = sl_lds[tile_off + tk] < 0;
+    const u32x4 v = skip ? u32x4{0, 0, 0, 0} : st.v[c];
     if constexpr (FP8) {
       __bf16 tmp[16];
 #pragma unroll
-      for (int d = 0; d < 4; ++d) fp8x4_to_bf16x4(st.v[c][d], tmp + 4 * d);
+      for (int d = 0; d < 4; ++d) fp8x4_to_bf16x4(v[d], tmp + 4 * d);
       bf16x8 lo, hi;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -180,7 +190,7 @@ __device__ __forceinline__ void tile_store(const TileStage<FP8>& st, uint8_t* ld
       dst[0] = lo;
       dst[1] = hi;
     } else {
-      *(u32x4*)(lds + tk * kPitch + piece * 16) = st.v[c];
+      *(u32x4*)(lds + tk * kPitch + piece * 16) = v;
     }
   }
 }
@@ -188,31 +198,33 @@ __device__ __forceinline__ void tile_store(const TileStage<FP8>& st, uint8_t* ld
 template <bool FP8>
 __global__ __launch_bounds__(kNT) void mla_mfma_kernel(MlaParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t tile[2][kTT * kPitch];
+  __shared__ __attribute__((aligned(16))) f32x4 xs[8][2][64];   // each wave's S^T half, per lane
   __shared__ float tok_scale[2][kTT];             // per-token scale (fp8) or 1; 0 marks a skipped slot
   __shared__ int32_t sl_lds[kMaxTopK + kTT];      // this chunk's slots, -1 padded to whole tiles
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
+  const int hg = wave & 3, kh = wave >> 2;
   const int r = blockIdx.y, split = blockIdx.x;
   const int j0 = split * p.chunk;
   const int j1 = min(p.k, j0 + p.chunk);
   const int ntiles = j1 > j0 ? (j1 - j0 + kTT - 1) / kTT : 0;
   const int32_t* sl = p.slots + (int64_t)r * p.k;
-  const bool active = wave * 16 < p.H;            // waves past the head count only help load
-  const int head = wave * 16 + (lane & 15);
+  const bool active = hg * 16 < p.H;              // head groups past the head count only help load
+  const int head = hg * 16 + (lane & 15);
   const int grp = lane >> 4;                      // 16-lane group
 
-  // q fragments (B operand of S^T): head lane%16, dims s*32 + grp*8 .. +8
-  bf16x8 qf[18];
+  // q fragments (B operand of S^T): head lane%16, dims (9kh + s)*32 + grp*8 .. +8
+  bf16x8 qf[kKSteps];
   if (active) {
     const bf16x8* qrow = (const bf16x8*)((const __bf16*)p.q + ((int64_t)r * p.H + head) * kRowDim);
 #pragma unroll
-    for (int s = 0; s < 18; ++s) qf[s] = qrow[s * 4 + grp];
+    for (int s = 0; s < kKSteps; ++s) qf[s] = qrow[(kKSteps * kh + s) * 4 + grp];
   }
 
-  f32x4 o[32];
+  f32x4 o[kDBlocks];
 #pragma unroll
-  for (int db = 0; db < 32; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int db = 0; db < kDBlocks; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY;   // running max of z * log2(e), per head
   float l_run = 0.f;         // this lane group's share of sum exp2(z - m_run)
   const float scale2 = p.sm_scale * kLog2e;
@@ -233,39 +245,64 @@ __global__ __launch_bounds__(kNT) void mla_mfma_kernel(MlaParams p) {
   }
   __syncthreads();
 
-  TileStage<FP8> st;
+  // tile t waits in register stage t % 2: while tile it is computed, tile it+1 sits in one stage
+  // (loaded an iteration ago) and tile it+2 is being loaded into the other.  The loop is unrolled
+  // by two so that the stages swap roles without a register copy (a copy would wait for loads
+  // still in flight).
+  TileStage<FP8> stage0, stage1;
   auto stage_scales = [&](int buf, int off) {
     if (threadIdx.x < kTT) {
-      const int64_t s = sl_lds[off + threadIdx.x];
-      tok_scale[buf][threadIdx.x] = s < 0 ? 0.f : (FP8 ? p.kv_scale[s] : 1.f);
+      const int64_t sv = sl_lds[off + threadIdx.x];
+      tok_scale[buf][threadIdx.x] = sv < 0 ? 0.f : (FP8 ? p.kv_scale[sv] : 1.f);
     }
   };
   if (ntiles > 0) {
-    tile_load<FP8>(st, p, sl_lds, 0);
+    tile_load<FP8>(stage0, p, sl_lds, 0);
+    if (ntiles > 1) tile_load<FP8>(stage1, p, sl_lds, kTT);
     stage_scales(0, 0);
-    tile_store<FP8>(st, tile[0]);
+    tile_store<FP8>(stage0, tile[0], sl_lds, 0);
   }
   __syncthreads();
 
-  for (int it = 0; it < ntiles; ++it) {
+  // one tile: `ld` receives tile it+2, `sv` holds tile it+1
+  auto step = [&](int it, TileStage<FP8>& ld, const TileStage<FP8>& sv) {
     const int buf = it & 1;
-    const bool more = it + 1 < ntiles;
-    if (more) tile_load<FP8>(st, p, sl_lds, (it + 1) * kTT);
+    if (it + 2 < ntiles) tile_load<FP8>(ld, p, sl_lds, (it + 2) * kTT);
+    const uint8_t* T = tile[buf];
+    // ---- S^T half for two 16-token blocks; block beta row m holds token 8*(m/4) + 4*beta + m%4.
+    // The blocks' K steps are interleaved (independent accumulators) and their LDS operands are
+    // read kAhead steps before use.
+    f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
     if (active) {
-      const uint8_t* T = tile[buf];
-      // ---- S^T for two 16-token blocks; block beta row m holds token 8*(m/4) + 4*beta + m%4
-      f32x4 sacc[2];
+      constexpr int kAhead = 3;
+      const int m = lane & 15;
+      const uint8_t* base0 = T + (8 * (m >> 2) + (m & 3)) * kPitch + grp * 16 + kh * (kKSteps * 64);
+      const uint8_t* base1 = base0 + 4 * kPitch;
+      bf16x8 a0[kAhead], a1[kAhead];
 #pragma unroll
-      for (int beta = 0; beta < 2; ++beta) {
-        const int m = lane & 15;
-        const int tok = 8 * (m >> 2) + 4 * beta + (m & 3);
-        const uint8_t* base = T + tok * kPitch + grp * 16;
-        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < 18; ++s)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(base + s * 64), qf[s], acc, 0, 0, 0);
-        sacc[beta] = acc;
+      for (int s = 0; s < kAhead; ++s) {
+        a0[s] = *(const bf16x8*)(base0 + s * 64);
+        a1[s] = *(const bf16x8*)(base1 + s * 64);
       }
+#pragma unroll
+      for (int s = 0; s < kKSteps; ++s) {
+        const bf16x8 x0 = a0[s % kAhead], x1 = a1[s % kAhead];
+        if (s + kAhead < kKSteps) {
+          a0[s % kAhead] = *(const bf16x8*)(base0 + (s + kAhead) * 64);
+          a1[s % kAhead] = *(const bf16x8*)(base1 + (s + kAhead) * 64);
+        }
+        sacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x0, qf[s], sacc[0], 0, 0, 0);
+        sacc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x1, qf[s], sacc[1], 0, 0, 0);
+      }
+      xs[wave][0][lane] = sacc[0];
+      xs[wave][1][lane] = sacc[1];
+    }
+    __syncthreads();
+    if (active) {
+      // the full logits: half 0 + half 1, the same sum in both waves of the head group
+      const int w0 = hg, w1 = hg + 4;
+      const f32x4 s0 = xs[w0][0][lane] + xs[w1][0][lane];
+      const f32x4 s1 = xs[w0][1][lane] + xs[w1][1][lane];
       // this lane holds head `head`, tokens 8*grp + 4*beta + j
       float z[8], sc[8];
       float tmax = -INFINITY;
@@ -276,7 +313,8 @@ __global__ __launch_bounds__(kNT) void mla_mfma_kernel(MlaParams p) {
           const int t = 8 * grp + 4 * beta + j;
           const float tsc = tok_scale[buf][t];
           sc[4 * beta + j] = tsc;
-          const float zz = tsc != 0.f ? sacc[beta][j] * tsc * scale2 : -INFINITY;
+          const float sv = beta == 0 ? s0[j] : s1[j];
+          const float zz = tsc != 0.f ? sv * tsc * scale2 : -INFINITY;
           z[4 * beta + j] = zz;
           tmax = fmaxf(tmax, zz);
         }
@@ -292,7 +330,7 @@ __global__ __launch_bounds__(kNT) void mla_mfma_kernel(MlaParams p) {
         m_run = m_new;
         l_run *= alpha;
 #pragma unroll
-        for (int db = 0; db < 32; ++db) o[db] *= alpha;
+        for (int db = 0; db < kDBlocks; ++db) o[db] *= alpha;
       }
       m_run = first ? tmax : m_run;
       bf16x8 pb;
@@ -302,44 +340,49 @@ __global__ __launch_bounds__(kNT) void mla_mfma_kernel(MlaParams p) {
         l_run += pe;
         pb[e] = (__bf16)(FP8 ? pe * sc[e] : pe);
       }
-      // ---- O^T += V^T . P^T ; V^T operand via transposing LDS reads (4 tokens x 16 dims per read)
+      // ---- O^T += V^T . P^T over this wave's 256 output dims; V^T operand via transposing
+      // LDS reads (4 tokens x 16 dims per read)
       const int jl = lane & 15;
-      const uint8_t* vrow1 = T + (8 * grp + (jl >> 2)) * kPitch + (jl & 3) * 8;
+      const uint8_t* vrow1 = T + (8 * grp + (jl >> 2)) * kPitch + (jl & 3) * 8 + kh * (kDBlocks * 32);
       const uint8_t* vrow2 = vrow1 + 4 * kPitch;
 #pragma unroll
-      for (int db = 0; db < 32; ++db) {
+      for (int db = 0; db < kDBlocks; ++db) {
         const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
             (__attribute__((address_space(3))) bf16x4*)(vrow1 + db * 32));
         const bf16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
             (__attribute__((address_space(3))) bf16x4*)(vrow2 + db * 32));
-        const bf16x8 a = __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, o[db], 0, 0, 0);
+        const bf16x8 av = __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7);
+        o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb, o[db], 0, 0, 0);
       }
     }
-    if (more) {
+    if (it + 1 < ntiles) {
       stage_scales(buf ^ 1, (it + 1) * kTT);
-      tile_store<FP8>(st, tile[buf ^ 1]);
+      tile_store<FP8>(sv, tile[buf ^ 1], sl_lds, (it + 1) * kTT);
     }
     __syncthreads();
+  };
+  for (int it = 0; it < ntiles; it += 2) {
+    step(it, stage0, stage1);
+    if (it + 1 < ntiles) step(it + 1, stage1, stage0);
   }
 
   if (!active) return;
   float l_tot = l_run + __shfl_xor(l_run, 16);
   l_tot += __shfl_xor(l_tot, 32);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  // lane holds O^T[d = db*16 + grp*4 + j][head]
+  // lane holds O^T[d = 256kh + db*16 + grp*4 + j][head]
   if (p.n_split == 1) {
-    float* dst = p.out + ((int64_t)r * p.H + head) * kVDim + grp * 4;
+    float* dst = p.out + ((int64_t)r * p.H + head) * kVDim + kh * (kDBlocks * 16) + grp * 4;
 #pragma unroll
-    for (int db = 0; db < 32; ++db) *(f32x4*)(dst + db * 16) = o[db] * inv;
-    if (p.lse && grp == 0)
+    for (int db = 0; db < kDBlocks; ++db) *(f32x4*)(dst + db * 16) = o[db] * inv;
+    if (p.lse && grp == 0 && kh == 0)
       p.lse[(int64_t)r * p.H + head] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
   } else {
     const int64_t prow = ((int64_t)r * p.n_split + split) * p.H + head;
-    float* dst = p.part_o + prow * kVDim + grp * 4;
+    float* dst = p.part_o + prow * kVDim + kh * (kDBlocks * 16) + grp * 4;
 #pragma unroll
-    for (int db = 0; db < 32; ++db) *(f32x4*)(dst + db * 16) = o[db] * inv;
-    if (grp == 0) {
+    for (int db = 0; db < kDBlocks; ++db) *(f32x4*)(dst + db * 16) = o[db] * inv;
+    if (grp == 0 && kh == 0) {
       p.part_m[prow] = l_tot > 0.f ? m_run * kLn2 : -INFINITY;
       p.part_l[prow] = l_tot;
     }
