@@ -151,8 +151,9 @@ int32_t dsa_sparse_mla_default_split(int32_t batch, int32_t q_per_seq, int32_t n
  * For each row r and head h, over chunks j with l[r,j,h] > 0:
  *   M = max_j m_j,  a_j = exp(m_j - M) * l_j,
  *   out[r,h,:] = sum_j a_j * o[r,j,h,:] / sum_j a_j,   lse[r,h] = M + log sum_j a_j.
- * m is in natural-log units.  If no chunk has l > 0: out = 0, lse = -inf.  The sum runs in
- * a fixed order (j ascending), so results are deterministic.
+ * m is in natural-log units.  If no chunk has l > 0: out = 0, lse = -inf.  The kernel keeps
+ * running (max, sum) pairs over fixed groups of chunks and merges them in a fixed order, which
+ * equals the formula up to rounding and makes results deterministic.
  *   part_o [rows, n_split, n_heads, 512] f32 (each chunk normalised by its own l)
  *   part_m, part_l [rows, n_split, n_heads] f32
  *   out [rows, n_heads, 512] f32;  lse [rows, n_heads] f32 or NULL

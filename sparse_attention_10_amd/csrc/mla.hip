@@ -390,77 +390,74 @@ __global__ __launch_bounds__(kNT) void mla_mfma_kernel(MlaParams p) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// split-k merge.  One 256-thread workgroup per (row, head, 128-value quarter of the output):
-// thread (g, q) sums chunks j = g, g+8, ... for output values 4q..4q+3 of the quarter, with its
-// loads issued in batches; the 8 per-group sums are then added in LDS in a fixed order, so the
-// result does not depend on scheduling.
+// split-k merge.  One 128-thread workgroup per (row, head, 128-value quarter of the output).
+// Thread (g, q) merges chunks j = g, g+4, g+8, ... for output values 4q..4q+3 of the quarter: it
+// issues the loads of m_j, l_j and o_j for up to 8 chunks at once, keeps a running
+// (max, denominator, weighted sum) in fixed j order, and the 4 groups are merged in LDS in a
+// fixed order, so the result does not depend on scheduling.  Chunks with l_j = 0 (no live slot)
+// are skipped; if none is live the output is 0 and lse = -inf.
 
-constexpr int kCombGroups = 8;
+constexpr int kCombGroups = 4;
+constexpr int kCombBatch = 8;
 
-__global__ __launch_bounds__(256) void mla_combine_kernel(CombineParams p) {
-  __shared__ float w_lds[1024];                    // a_j = exp(m_j - M) * l_j (0 for empty chunks)
-  __shared__ float red[kCombGroups][128];
-  __shared__ float s_M, s_den;
+__device__ __forceinline__ void lse_merge(float& M, float& den, f32x4& acc, float m2, float den2, const f32x4& acc2) {
+  // merges (m2, den2, acc2) into (M, den, acc): both are sums scaled by exp(-max)
+  if (den2 <= 0.f) return;
+  if (den <= 0.f) {
+    M = m2;
+    den = den2;
+    acc = acc2;
+    return;
+  }
+  const float Mn = fmaxf(M, m2);
+  const float a = expf(M - Mn), b = expf(m2 - Mn);
+  den = den * a + den2 * b;
+  acc = acc * a + acc2 * b;
+  M = Mn;
+}
+
+__global__ __launch_bounds__(128) void mla_combine_kernel(CombineParams p) {
+  __shared__ float s_m[kCombGroups][32], s_d[kCombGroups][32];
+  __shared__ f32x4 s_a[kCombGroups][32];
   const int dq = blockIdx.x & 3;
   const int rh = blockIdx.x >> 2;
   const int r = rh / p.H, h = rh - (rh / p.H) * p.H;
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = threadIdx.x;
+  const int g = tid >> 5, q = tid & 31;
   const int ns = p.n_split;
   const int64_t base = (int64_t)r * ns * p.H + h;  // partial row of chunk j: base + j * H
-
-  if (tid < 64) {                                  // wave 0: live maximum and denominator
-    float M = -INFINITY;
-    for (int j = lane; j < ns; j += 64) {
-      const float lj = p.part_l[base + (int64_t)j * p.H];
-      if (lj > 0.f) M = fmaxf(M, p.part_m[base + (int64_t)j * p.H]);
-    }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-    float den = 0.f;
-    for (int j = lane; j < ns; j += 64) {
-      const float lj = p.part_l[base + (int64_t)j * p.H];
-      const float a = (lj > 0.f && M != -INFINITY) ? expf(p.part_m[base + (int64_t)j * p.H] - M) * lj : 0.f;
-      w_lds[j] = a;
-      den += a;
-    }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) den += __shfl_xor(den, off);
-    if (lane == 0) {
-      s_M = M;
-      s_den = den;
-    }
-  }
-  __syncthreads();
-  const int g = tid >> 5, q = tid & 31;
   const int col = dq * 128 + q * 4;
+
+  float M = -INFINITY, den = 0.f;
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  constexpr int kB = 4;
-  for (int j0 = g; j0 < ns; j0 += kB * kCombGroups) {
-    f32x4 v[kB];
+  for (int j0 = g; j0 < ns; j0 += kCombBatch * kCombGroups) {
+    float mv[kCombBatch], lv[kCombBatch];
+    f32x4 ov[kCombBatch];
 #pragma unroll
-    for (int u = 0; u < kB; ++u) {
-      const int j = min(j0 + u * kCombGroups, ns - 1);
-      v[u] = *(const f32x4*)(p.part_o + (base + (int64_t)j * p.H) * kVDim + col);
+    for (int u = 0; u < kCombBatch; ++u) {
+      const int64_t pr = base + (int64_t)min(j0 + u * kCombGroups, ns - 1) * p.H;
+      mv[u] = p.part_m[pr];
+      lv[u] = p.part_l[pr];
+      ov[u] = *(const f32x4*)(p.part_o + pr * kVDim + col);
     }
 #pragma unroll
-    for (int u = 0; u < kB; ++u) {
-      const int j = j0 + u * kCombGroups;
-      if (j < ns) {
-        const float a = w_lds[j];
-        if (a > 0.f) acc += a * v[u];              // (an empty chunk's values are never read)
-      }
+    for (int u = 0; u < kCombBatch; ++u) {
+      const bool live = j0 + u * kCombGroups < ns && lv[u] > 0.f;
+      // o_j is normalised by l_j: its weight in the merged sum is l_j exp(m_j - M)
+      if (live) lse_merge(M, den, acc, mv[u], lv[u], ov[u] * lv[u]);
     }
   }
-  *(f32x4*)&red[g][q * 4] = acc;
+  s_m[g][q] = M;
+  s_d[g][q] = den;
+  s_a[g][q] = acc;
   __syncthreads();
   if (g == 0) {
-    f32x4 t = *(const f32x4*)&red[0][q * 4];
 #pragma unroll
-    for (int gg = 1; gg < kCombGroups; ++gg) t += *(const f32x4*)&red[gg][q * 4];
+    for (int gg = 1; gg < kCombGroups; ++gg) lse_merge(M, den, acc, s_m[gg][q], s_d[gg][q], s_a[gg][q]);
     float* dst = p.out + ((int64_t)r * p.H + h) * kVDim + col;
-    const bool live = s_M != -INFINITY;
-    *(f32x4*)dst = live ? t * (1.f / s_den) : f32x4{0.f, 0.f, 0.f, 0.f};
-    if (p.lse && dq == 0 && q == 0) p.lse[(int64_t)r * p.H + h] = live ? s_M + logf(s_den) : -INFINITY;
+    const bool live = den > 0.f;
+    *(f32x4*)dst = live ? acc * (1.f / den) : f32x4{0.f, 0.f, 0.f, 0.f};
+    if (p.lse && dq == 0 && q == 0) p.lse[(int64_t)r * p.H + h] = live ? M + logf(den) : -INFINITY;
   }
 }
 
@@ -501,7 +498,7 @@ hipError_t launch_mla(const MlaParams& p0, dsa_dtype_t q_dtype, dsa_dtype_t kv_d
 
 hipError_t launch_combine(const CombineParams& c, hipStream_t s) {
   if (c.rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)(c.rows * c.H * 4)), dim3(256), 0, s, c);
+  hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)(c.rows * c.H * 4)), dim3(128), 0, s, c);
   return hipGetLastError();
 }
 
