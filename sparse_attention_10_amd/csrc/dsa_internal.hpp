@@ -55,6 +55,8 @@ struct IndexerParams {
   int32_t B, Q, max_seq_len, P, maxP;
   int32_t Hi, Di;
   int32_t tiles_per_wg;   // matrix-core path: 128-token tiles per workgroup
+  int32_t groups_padded;  // matrix-core path: tile groups per sequence, rounded up to 8
+  int32_t p_shift;        // log2(P) when the page size is a power of two, else -1
 };
 
 struct TopkParams {

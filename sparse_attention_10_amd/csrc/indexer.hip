@@ -71,158 +71,268 @@ __global__ __launch_bounds__(256) void indexer_valu_kernel(IndexerParams p) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// matrix-core path: Hi = 64, Di = 128, QB query rows per workgroup (M = 64 * QB)
+// matrix-core path: Hi = 64, Di = 128, QB = 1 or 2 query rows per workgroup
+//
+// 8 waves (two per SIMD) stream the keys of one token range through an LDS ring of NB stages.
+// A stage holds ST = 32 * 8 / QB tokens; it is filled by direct-to-LDS loads in which
+// consecutive lanes fetch consecutive 16-byte pieces of key rows, so each load instruction moves
+// 1 KB in few cache lines, and piece p of row r is stored at slot p ^ swz(r) of its LDS row so
+// that the MFMA operand reads are free of bank conflicts.  Every key is read from memory once
+// per workgroup: with QB = 2 the waves 0-3 score row 0 and the waves 4-7 row 1 on the same
+// 32-token sub-tiles.  One barrier per stage: after it the stage has landed for every wave and
+// the stage read before it is free to be refilled.
 
 constexpr int kHi = 64, kDi = 128;
-constexpr int kSub = 32;                  // tokens per wave sub-tile (the MFMA N)
-constexpr int kWaves = 4;
-constexpr int kTile = kSub * kWaves;      // tokens per workgroup tile
+constexpr int kSub = 32;                  // tokens per sub-tile (the MFMA N)
+constexpr int kWaves = 8;
+constexpr int kThreadsI = 64 * kWaves;
+constexpr int kTile = 256;                // grid granularity: tokens per tile
+constexpr int kMaxTpwAny = 8;             // tiles per workgroup, any page size
+constexpr int kMaxTpwContig = 64;         // tiles per workgroup when 32 | P (pages of >= 32 tokens)
+constexpr int kMaxWgPages = kMaxTpwAny * kTile + 1;   // page-table entries a workgroup can span
+static_assert(kMaxTpwContig * kTile / 32 + 1 <= kMaxWgPages, "page-table staging covers both layouts");
 
-template <bool FP8>
-struct KeyFrag {
-  // 8 k-steps of 8 bf16 (B operand), covering dims [h*64, h*64+64) of the lane's token
-  bf16x8 v[8];
+template <bool FP8, int QB>
+struct Geo {
+  static constexpr int RB = FP8 ? kDi : 2 * kDi;       // key row bytes
+  static constexpr int SPS = kWaves / QB;              // sub-tiles per stage
+  static constexpr int ST = kSub * SPS;                // tokens per stage
+  static constexpr int SB = ST * RB;                   // stage bytes
+  static constexpr int ND = SB / (kThreadsI * 16);     // 16-byte loads per thread per stage
+  static constexpr int NB = FP8 ? (QB == 2 ? 4 : 3) : (QB == 2 ? 3 : 2);   // ring depth (<= 128 KB)
+  static constexpr int NSW = FP8 ? ST / 64 : 0;        // waves that also load the stage's scales
 };
-
-// Issue the loads of one sub-tile's key fragment.  Raw bits are kept so the fp8 widening can
-// run after the loads have landed.
 template <bool FP8>
-struct KeyRaw {
-  u32x4 r[FP8 ? 4 : 8];
-};
+__device__ __forceinline__ int swz(int r) { return FP8 ? ((r >> 1) & 7) : (r & 15); }
 
-template <bool FP8>
-__device__ __forceinline__ void load_keys(KeyRaw<FP8>& raw, const uint8_t* kc, int64_t slot, bool valid,
-                                          int half) {
-  if (valid) {
-    const u32x4* src = (const u32x4*)(kc + slot * (FP8 ? kDi : 2 * kDi) + half * (FP8 ? 64 : 128));
-#pragma unroll
-    for (int c = 0; c < (FP8 ? 4 : 8); ++c) raw.r[c] = __builtin_nontemporal_load(src + c);
-  } else {
-#pragma unroll
-    for (int c = 0; c < (FP8 ? 4 : 8); ++c) raw.r[c] = u32x4{0, 0, 0, 0};
-  }
+__device__ __forceinline__ void lds_dma16(const void* src, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
+__device__ __forceinline__ void lds_dma4(const void* src, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_base, 4, 0, 0);
 }
 
-template <bool FP8>
-__device__ __forceinline__ void widen_keys(const KeyRaw<FP8>& raw, KeyFrag<FP8>& f) {
-  if constexpr (FP8) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      __bf16 tmp[16];
-#pragma unroll
-      for (int d = 0; d < 4; ++d) fp8x4_to_bf16x4(raw.r[c][d], tmp + 4 * d);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        f.v[2 * c][j] = tmp[j];
-        f.v[2 * c + 1][j] = tmp[8 + j];
-      }
-    }
-  } else {
-#pragma unroll
-    for (int s = 0; s < 8; ++s) f.v[s] = __builtin_bit_cast(bf16x8, raw.r[s]);
-  }
+// s_waitcnt with only the vector-memory count limited (gfx9 encoding: vmcnt bits 3:0 and 15:14,
+// expcnt 6:4 and lgkmcnt 11:8 at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int QB, bool FP8>
-__global__ __launch_bounds__(256) void indexer_mfma_kernel(IndexerParams p) {
+// CONTIG (32 divides P): a sub-tile's 32 tokens are one 32-aligned run inside one page, so its
+// key rows are contiguous in the cache and one page lookup per sub-tile gives every address.
+template <bool FP8, bool CONTIG, int QB>
+__global__ __launch_bounds__(kThreadsI) void indexer_mfma_kernel(IndexerParams p) {
+  using G = Geo<FP8, QB>;
+  constexpr int NB = G::NB;
+  static_assert(NB >= 2 && NB <= 4, "ring depth");
+  __shared__ __attribute__((aligned(16))) uint8_t ring[NB][G::SB];
+  __shared__ __attribute__((aligned(16))) float sring[FP8 ? NB : 1][FP8 ? G::ST : 1];   // fp8 token scales
   __shared__ __attribute__((aligned(16))) __bf16 q_lds[QB][kHi][kDi];
-  __shared__ float w_lds[QB][kHi];
+  __shared__ __attribute__((aligned(16))) float w_lds[QB][kHi];
+  __shared__ int32_t pt_lds[kMaxWgPages];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int b = blockIdx.z;
-  const int qb0 = blockIdx.y * QB;            // first query row of this block within the sequence
+  // One workgroup = QB query rows x one range of p.tiles_per_wg tiles.  The grid is ordered so
+  // that the Q/QB row groups of one key range get ids 8 apart (ids go to the 8 XCDs round-robin):
+  // they run on one XCD, close together, and the groups after the first read the keys from its
+  // L2.   id = b*(Gp*NQ) + 8NQ*m + 8*i + j  ->  row group i, key range g = 8m + j
+  const int nq = p.Q / QB;
+  const int per_b = p.groups_padded * nq;
+  const int b = (int)blockIdx.x / per_b;
+  const int local = (int)blockIdx.x - b * per_b;
+  const int qb0 = ((local >> 3) % nq) * QB;           // first query row of the block
+  const int grp_id = 8 * (local / (8 * nq)) + (local & 7);
   const int L = min(p.seq_lens[b], p.max_seq_len);
-  const int tile_base = blockIdx.x * p.tiles_per_wg * kTile;
+  const int tile_base = grp_id * p.tiles_per_wg * kTile;
   if (tile_base >= L) return;                 // uniform early exit
   const int tile_end = min(L, tile_base + p.tiles_per_wg * kTile);
-  const int nrows = QB;                       // the launcher picks QB dividing Q
-  const int pos_last = L - p.Q + qb0 + nrows - 1;   // largest position in the block
+  const int pos_last = L - p.Q + qb0 + QB - 1;  // the block's largest position
+  const int t_stop = min(tile_end, pos_last + 1);  // tokens at or past this are never scored
+  const int nstage = t_stop > tile_base ? (t_stop - tile_base + G::ST - 1) / G::ST : 0;
 
+  const int ri = wave / G::SPS;               // the row this wave scores
+  const int si = wave - ri * G::SPS;          // its sub-tile within a stage
+  const int pos = L - p.Q + qb0 + ri;         // that row sees tokens t <= pos
   const int n_in_sub = lane & 31;
   const int half = lane >> 5;
+  const int page0 = tile_base / p.P;
+  const int npg = (t_stop > tile_base) ? (t_stop - 1) / p.P - page0 + 1 : 0;
+  const int32_t* ptab_g = p.page_table + (int64_t)b * p.maxP;
   const uint8_t* kc = (const uint8_t*)p.k_cache;
-  const int32_t* ptab = p.page_table + (int64_t)b * p.maxP;
 
-  // first sub-tile's keys are requested before q is staged, so both latencies overlap
-  int t_cur = tile_base + wave * kSub + n_in_sub;
-  auto slot_of = [&](int t) -> int64_t { return (int64_t)ptab[t / p.P] * p.P + t % p.P; };
-  bool v_cur = t_cur < tile_end && t_cur <= pos_last;
-  int64_t s_cur = v_cur ? slot_of(t_cur) : 0;
-  KeyRaw<FP8> raw_cur;
-  load_keys<FP8>(raw_cur, kc, s_cur, v_cur, half);
+  // Stage v covers tokens tile_base + v*ST ..; this thread's load c fills LDS bytes
+  // [off, off+16) of the stage, off = ((c*8 + wave)*64 + lane)*16: row r = off / RB and slot
+  // off % RB / 16, fetched from piece (slot ^ swz(r)) of that token's key row.
+  int lane_off[G::ND];     // byte offset inside the (contiguous) 32-token sub-tile
+  int lane_row[G::ND];
+#pragma unroll
+  for (int c = 0; c < G::ND; ++c) {
+    const int off = ((c * kWaves + wave) * 64 + lane) * 16;
+    const int r = off / G::RB, q = (off % G::RB) / 16;
+    lane_row[c] = r;
+    lane_off[c] = (r & (kSub - 1)) * G::RB + 16 * (q ^ swz<FP8>(r));
+  }
+  const bool scale_wave = FP8 && wave < G::NSW;
+  auto issue = [&](int v, auto&& slot_of) {
+    const int t0 = tile_base + v * G::ST;
+    uint8_t* stg = &ring[v % NB][0];
+#pragma unroll
+    for (int c = 0; c < G::ND; ++c) {
+      const int r = lane_row[c];
+      const int off = ((c * kWaves + wave) * 64) * 16;     // this load's 1-KB block of the stage
+      if constexpr (CONTIG) {
+        // the 1-KB block lies in one sub-tile: rows t0 + (r & ~31) .. +31 are contiguous
+        // (the run never leaves its page, so rows past the sequence are still allocated cache
+        // rows; their scores are never written)
+        const int ts = t0 + (r & ~(kSub - 1));
+        const int64_t slot0 = ts < t_stop ? slot_of(ts) : 0;
+        lds_dma16(kc + slot0 * G::RB + lane_off[c], stg + off);
+      } else {
+        const int t = t0 + r;
+        const int q = (((c * kWaves + wave) * 64 + lane) * 16 % G::RB) / 16;
+        const int64_t slot = t < t_stop ? slot_of(t) : 0;   // row 0 (valid) for unscored tokens
+        lds_dma16(kc + slot * G::RB + 16 * (q ^ swz<FP8>(r)), stg + off);
+      }
+    }
+    if constexpr (FP8) {
+      if (scale_wave) {
+        const int t = t0 + wave * 64 + lane;
+        const int64_t slot = t < t_stop ? slot_of(t) : 0;
+        lds_dma4(p.k_scale + slot, &sring[v % NB][wave * 64]);
+      }
+    }
+  };
+  // the first NB-1 stages are requested before q is staged, from page-table entries read
+  // straight from global memory
+  auto slot_global = [&](int t) { return (int64_t)ptab_g[t / p.P] * p.P + t % p.P; };
+#pragma unroll
+  for (int v = 0; v < NB - 1; ++v)
+    if (v < nstage) issue(v, slot_global);
 
-  // stage q (bf16) and w for the block's query rows (QB divides Q, so the block is always
-  // QB full rows); all loads are issued before the first LDS store
+  // stage q (bf16), w and the page-table entries of this workgroup's tokens
   {
     const int64_t row0 = (int64_t)b * p.Q + qb0;
     const u32x4* qsrc = (const u32x4*)((const __bf16*)p.q + row0 * kHi * kDi);
     u32x4* qdst = (u32x4*)&q_lds[0][0][0];
-    constexpr int kPer = QB * kHi * kDi / 8 / 256;
+    constexpr int kPer = QB * kHi * kDi / 8 / kThreadsI;
     u32x4 qv[kPer];
 #pragma unroll
-    for (int c = 0; c < kPer; ++c) qv[c] = qsrc[c * 256 + threadIdx.x];
+    for (int c = 0; c < kPer; ++c) qv[c] = qsrc[c * kThreadsI + threadIdx.x];
     const float wv = threadIdx.x < QB * kHi ? p.w[row0 * kHi + threadIdx.x] : 0.f;
+    constexpr int kPtPer = (kMaxWgPages + kThreadsI - 1) / kThreadsI;
+    int32_t pv[kPtPer];
 #pragma unroll
-    for (int c = 0; c < kPer; ++c) qdst[c * 256 + threadIdx.x] = qv[c];
+    for (int c = 0; c < kPtPer; ++c)   // (uniform: only the blocks of entries the workgroup spans)
+      pv[c] = c * kThreadsI < npg ? ptab_g[page0 + min(c * kThreadsI + (int)threadIdx.x, npg - 1)] : 0;
+#pragma unroll
+    for (int c = 0; c < kPer; ++c) qdst[c * kThreadsI + threadIdx.x] = qv[c];
     if (threadIdx.x < QB * kHi) (&w_lds[0][0])[threadIdx.x] = wv;
+#pragma unroll
+    for (int c = 0; c < kPtPer; ++c)
+      if (c * kThreadsI + (int)threadIdx.x < npg) pt_lds[c * kThreadsI + threadIdx.x] = pv[c];
   }
   __syncthreads();
 
-  // A fragments: lane (head m = lane%32 of M-block mb, half h) holds, for k-step s,
-  // q dims [h*64 + s*8, +8)
-  bf16x8 afrag[2 * QB][8];
+  // A fragments of this wave's row: lane (head m = lane%32 of M-block mb, half h) holds, for
+  // k-step s, q dims [h*64 + s*8, +8) (the contraction index is permuted the same way for keys)
+  bf16x8 afrag[2][8];
 #pragma unroll
-  for (int mb = 0; mb < 2 * QB; ++mb)
+  for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
     for (int s = 0; s < 8; ++s)
-      afrag[mb][s] = *(const bf16x8*)&q_lds[mb >> 1][(mb & 1) * 32 + n_in_sub][half * 64 + s * 8];
-
-  // heads held by this lane in each 32-row M-block: m(j) = (j/4)*8 + half*4 + j%4
-  for (int sub = tile_base + wave * kSub; sub < tile_end; sub += kTile) {
-    const int t_nxt = sub + kTile + n_in_sub;
-    const bool v_nxt = t_nxt < tile_end && t_nxt <= pos_last;
-    const int64_t s_nxt = v_nxt ? slot_of(t_nxt) : 0;
-    KeyRaw<FP8> raw_nxt;
-    load_keys<FP8>(raw_nxt, kc, s_nxt, v_nxt, half);   // prefetch the next sub-tile
-
-    KeyFrag<FP8> kf;
-    widen_keys<FP8>(raw_cur, kf);
-    f32x16 acc[2 * QB];
+      afrag[mb][s] = *(const bf16x8*)&q_lds[ri][mb * 32 + n_in_sub][half * 64 + s * 8];
+  float wr[2][4][4];   // head weights of the heads this lane holds: m = mb*32 + g*8 + half*4 + j
 #pragma unroll
-    for (int mb = 0; mb < 2 * QB; ++mb) {
-      acc[mb] = f32x16{};
+  for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int s = 0; s < 8; ++s)
-        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag[mb][s], kf.v[s], acc[mb], 0, 0, 0);
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 wv = *(const f32x4*)&w_lds[ri][mb * 32 + g * 8 + half * 4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) wr[mb][g][j] = wv[j];
     }
-    const float kscale = (FP8 && v_cur) ? p.k_scale[s_cur] : 1.f;
+
+  const int P = p.P;
+  auto slot_lds = [&](int t) {
+    const int pg = p.p_shift >= 0 ? t >> p.p_shift : t / P;   // (uniform: power-of-two pages shift)
+    return (int64_t)pt_lds[pg - page0] * P + (t - pg * P);
+  };
+  float* dst = p.scores + ((int64_t)b * p.Q + qb0 + ri) * p.ld;
+
+  // this wave's sub-tile of stage v: B fragments (lane: token n, half h) from LDS, 32x32x16
+  // MFMAs over the two 32-head M-blocks, then ReLU, head weights and the head sum
+  auto compute = [&](int v) {
+    const int t = tile_base + v * G::ST + si * kSub + n_in_sub;
+    if (tile_base + v * G::ST + si * kSub > pos) {   // (uniform) the whole sub-tile is unseen
+      if (half == 0 && t < tile_end) dst[t] = -INFINITY;
+      return;
+    }
+    const uint8_t* rows = &ring[v % NB][si * kSub * G::RB];
+    bf16x8 kf[8];
+    if constexpr (FP8) {
 #pragma unroll
-    for (int qi = 0; qi < QB; ++qi) {
-      float part = 0.f;
+      for (int s2 = 0; s2 < 4; ++s2) {          // dims h*64 + 16*s2 .. +16 = piece 4h + s2
+        const u32x4 raw = *(const u32x4*)(rows + n_in_sub * G::RB + 16 * ((4 * half + s2) ^ swz<FP8>(n_in_sub)));
+        __bf16 tmp[16];
 #pragma unroll
-      for (int mbl = 0; mbl < 2; ++mbl) {
-        const int mb = 2 * qi + mbl;
+        for (int d = 0; d < 4; ++d) fp8x4_to_bf16x4(raw[d], tmp + 4 * d);
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x4 wv = *(const f32x4*)&w_lds[qi][mbl * 32 + g * 8 + half * 4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) part = fmaf(wv[j], fmaxf(acc[mb][4 * g + j], 0.f), part);
+        for (int e = 0; e < 8; ++e) {
+          kf[2 * s2][e] = tmp[e];
+          kf[2 * s2 + 1][e] = tmp[8 + e];
         }
       }
-      part += __shfl_xor(part, 32);
-      if (half == 0 && qi < nrows && t_cur < tile_end) {
-        const int pos = L - p.Q + qb0 + qi;
-        float* dst = p.scores + ((int64_t)b * p.Q + qb0 + qi) * p.ld;
-        dst[t_cur] = t_cur <= pos ? part * kscale : -INFINITY;
-      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < 8; ++s)               // dims h*64 + 8s .. +8 = piece 8h + s
+        kf[s] = *(const bf16x8*)(rows + n_in_sub * G::RB + 16 * ((8 * half + s) ^ swz<FP8>(n_in_sub)));
     }
-    raw_cur = raw_nxt;
-    t_cur = t_nxt;
-    v_cur = v_nxt;
-    s_cur = s_nxt;
+    f32x16 acc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag[mb][s], kf[s], acc[mb], 0, 0, 0);
+    float part = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)   // ReLU as one integer max on the bits (negatives -> +0)
+          part = fmaf(wr[mb][g][jj], __int_as_float(max(__float_as_int(acc[mb][4 * g + jj]), 0)), part);
+    part += __shfl_xor(part, 32);
+    if (half == 0 && t < tile_end) {
+      const float kscale = FP8 ? sring[FP8 ? v % NB : 0][FP8 ? si * kSub + n_in_sub : 0] : 1.f;
+      dst[t] = t <= pos ? part * kscale : -INFINITY;
+    }
+  };
+
+  // loads of this wave per stage (its 16-byte pieces, plus the scales for some waves)
+  for (int v = 0; v < nstage; ++v) {
+    // stage v must have landed: at most the loads of the later stages requested so far
+    // (v+1 .. v+NB-2) may still be outstanding (vector-memory loads complete in order)
+    const int later = min(NB - 2, nstage - 1 - v);
+    if (scale_wave) {
+      if (later >= 2) wait_vmcnt<2 * (G::ND + 1)>();
+      else if (later == 1) wait_vmcnt<G::ND + 1>();
+      else wait_vmcnt<0>();
+    } else {
+      if (later >= 2) wait_vmcnt<2 * G::ND>();
+      else if (later == 1) wait_vmcnt<G::ND>();
+      else wait_vmcnt<0>();
+    }
+    __syncthreads();   // stage v landed for every wave; stage v-1 is no longer read
+    if (v + NB - 1 < nstage) issue(v + NB - 1, slot_lds);
+    compute(v);
   }
+  // tokens of [tile_base, tile_end) past the block's last position: -inf (their stages are not
+  // computed)
+  for (int t = max(t_stop, tile_base) + (int)threadIdx.x; t < tile_end; t += kThreadsI)
+#pragma unroll
+    for (int qq = 0; qq < QB; ++qq) p.scores[((int64_t)b * p.Q + qb0 + qq) * p.ld + t] = -INFINITY;
 }
 
 }  // namespace
@@ -234,22 +344,30 @@ bool indexer_uses_mfma(int Hi, int Di, dsa_dtype_t q_dtype, dsa_dtype_t k_dtype)
 hipError_t launch_indexer(const IndexerParams& p0, dsa_dtype_t q_dtype, dsa_dtype_t k_dtype, hipStream_t s) {
   IndexerParams p = p0;
   if (indexer_uses_mfma(p.Hi, p.Di, q_dtype, k_dtype)) {
-    const int QB = (p.Q % 2 == 0) ? 2 : 1;
     const int64_t tiles = ((int64_t)p.max_seq_len + kTile - 1) / kTile;
-    const int64_t work = tiles * p.B * ((p.Q + QB - 1) / QB);
-    // keep >= ~4 workgroups per compute unit, then give each workgroup several tiles
-    int tpw = (int)(work / 2048);
-    tpw = tpw < 1 ? 1 : (tpw > 8 ? 8 : tpw);
+    // about two rounds of the 256 workgroups the GPU holds at once (one per CU), each with as
+    // many steps as that allows: longer workgroups pay their q / page-table staging less often
+    const bool contig = p.P % kSub == 0;
+    const int QB = (p.Q % 2 == 0) ? 2 : 1;
+    const int64_t work = tiles * p.B * (p.Q / QB);
+    const int max_tpw = contig ? kMaxTpwContig : kMaxTpwAny;
+    int tpw = (int)(work / 512);
+    tpw = tpw < 1 ? 1 : (tpw > max_tpw ? max_tpw : tpw);
     p.tiles_per_wg = tpw;
-    dim3 grid((unsigned)((tiles + tpw - 1) / tpw), (unsigned)((p.Q + QB - 1) / QB), (unsigned)p.B);
+    p.p_shift = (p.P & (p.P - 1)) == 0 ? __builtin_ctz((unsigned)p.P) : -1;
+    const int64_t groups = (tiles + tpw - 1) / tpw;
+    p.groups_padded = (int32_t)((groups + 7) / 8 * 8);
+    const dim3 grid((unsigned)((int64_t)p.groups_padded * (p.Q / QB) * p.B));
     const bool f8 = k_dtype == DSA_FP8_E4M3FN;
+#define DSA_IDX_MFMA(F8, CT, QBV) hipLaunchKernelGGL((indexer_mfma_kernel<F8, CT, QBV>), grid, dim3(kThreadsI), 0, s, p)
     if (QB == 2) {
-      if (f8) hipLaunchKernelGGL((indexer_mfma_kernel<2, true>), grid, dim3(256), 0, s, p);
-      else hipLaunchKernelGGL((indexer_mfma_kernel<2, false>), grid, dim3(256), 0, s, p);
+      if (contig) { if (f8) DSA_IDX_MFMA(true, true, 2); else DSA_IDX_MFMA(false, true, 2); }
+      else { if (f8) DSA_IDX_MFMA(true, false, 2); else DSA_IDX_MFMA(false, false, 2); }
     } else {
-      if (f8) hipLaunchKernelGGL((indexer_mfma_kernel<1, true>), grid, dim3(256), 0, s, p);
-      else hipLaunchKernelGGL((indexer_mfma_kernel<1, false>), grid, dim3(256), 0, s, p);
+      if (contig) { if (f8) DSA_IDX_MFMA(true, true, 1); else DSA_IDX_MFMA(false, true, 1); }
+      else { if (f8) DSA_IDX_MFMA(true, false, 1); else DSA_IDX_MFMA(false, false, 1); }
     }
+#undef DSA_IDX_MFMA
     return hipGetLastError();
   }
   dim3 grid((unsigned)((p.max_seq_len + 255) / 256), (unsigned)p.Q, (unsigned)p.B);
