@@ -4,24 +4,24 @@
 //
 // One 512-thread workgroup per query row.  The selection is exact: equal scores go to the
 // lower token index, -0.0 equals +0.0, winners come out in ascending token order.  The work is
-// bound by the vector ALU of the one CU, so the kernel touches every key only twice:
+// bound by the instruction issue and LDS of the one CU, so every pass is written for few
+// instructions per key.  A "key row" is one 32-bit register across a wave: 64 consecutive
+// columns, one per lane.  Wave w holds RV consecutive key rows of the row's first 512*RV
+// columns in registers; later columns are streamed from L2 in segments.
 //   pass 1  Scores become order-preserving uint32 keys (larger score <-> larger key; key 0
 //           marks a column outside the row) and are counted into an LDS histogram of their top
-//           15 bits.  Two scans (256 coarse bins of 128, then the 128 bins of the chosen coarse
-//           bin) find the bin b holding the k-th largest key.  A bin holding more than
-//           kCandCap keys is narrowed by 11-bit radix rounds over the keys of that bin.
-//   pass 2  Every key is classified against the bin: the ballot masks "above the bin" and
-//           "inside the bin" are kept per 256 columns in LDS, and the keys inside the bin (the
-//           candidates) are gathered with their columns.  The exact threshold key T is then
-//           selected among the candidates in LDS, and the candidates' mask bits are corrected
-//           in place (above T -> "above", below T -> cleared, equal stays).
-//   output  A scan of the mask popcounts in column order gives each 256-column chunk its
-//           output offset; a thread walks its chunk's set bits in ascending column order,
-//           taking every key above T and the lowest-column keys equal to T until k are taken,
-//           and writes the token index and (fused page map) its cache slot.
-// Scores are read as aligned float4: a row that starts off 16-byte alignment is read from the
-// aligned address below it, as if it had 1-3 leading columns that hold no score.  The first
-// 32K columns stay in registers; columns past that are re-read from L2 in each pass.
+//           15 bits.  A scan of per-thread bin sums, then of the chosen thread's bins, finds the
+//           bin b holding the k-th largest key.  A bin holding more than kCandCap keys is
+//           narrowed by 11-bit radix rounds over the keys of that bin.
+//   pass 2  Per unit (one wave's key rows of the register block, or of one streamed segment)
+//           the keys above the bin are counted, and the keys inside the bin (the candidates)
+//           are gathered with their columns.  The exact threshold key T is then found among the
+//           candidates (one key bit at a time by ballot counts when they are few), and the
+//           candidates above and equal to T are added to their units' counts.
+//   output  Every wave scans the units' counts (keys equal to T are taken in column order until
+//           k are taken).  Each key row's winners get their output offsets from one ballot and
+//           mbcnt and their columns go to an LDS list; the whole workgroup then writes the k
+//           token indices and (fused page map) cache slots with coalesced stores.
 #include "dsa_internal.hpp"
 
 namespace dsa {
@@ -33,30 +33,35 @@ namespace {
 #endif
 constexpr int kThreads = DSA_TOPK_THREADS;
 constexpr int kWaves = kThreads / 64;
-constexpr int kChunkCols = 256;                          // columns of one (iteration, wave) chunk
-constexpr int kMaxChunks = (kMaxTopkSeq + 3 + kChunkCols - 1) / kChunkCols;
 constexpr int kHistBins = 1 << 15;                       // first digit: top 15 key bits
-constexpr int kBinsPerThread = kHistBins / kThreads;    // bins summed by one thread
+constexpr int kBinsPerThread = kHistBins / kThreads;     // bins summed by one thread
 constexpr int kBinShift = __builtin_ctz(kBinsPerThread);
-constexpr int kHistWords = kHistBins + kHistBins / kBinsPerThread;   // a pad word after each thread's bins
+constexpr int kHistStride = kBinsPerThread + 4;          // words per thread's bins (16-byte pad)
+constexpr int kHistWords = kHistStride * kThreads;
 constexpr int kCandCap = 4096;                           // candidates gathered into LDS
 constexpr int kCandPerWave = kCandCap / kWaves;          // per-wave candidate regions
 constexpr int kPtabCache = 4096;                         // page-table entries cached in LDS
 constexpr int kSmallBits = 11;                           // digit of the narrowing rounds
 constexpr int kSmallBins = 1 << kSmallBits;
-constexpr int kTailBatch = 8;                            // float4 loads in flight per thread
+constexpr int kTailRows = 16;                            // key rows per wave of one streamed segment
+constexpr int kSegCols = 64 * kTailRows * kWaves;        // columns of one streamed segment
+// units: each wave's key rows of the register block, then of each streamed segment
+constexpr int kMaxUnits = kWaves * (1 + (kMaxTopkSeq + kSegCols - 1) / kSegCols);
+constexpr int kUnitsPerLane = (kMaxUnits + 63) / 64;
 
 // Word offsets in the one LDS array: the histogram in pass 1, then these regions.
-constexpr int kOffGt = 0;                                // u64 [4 * kMaxChunks]
-constexpr int kOffEq = kOffGt + 8 * kMaxChunks;          // u64 [4 * kMaxChunks]
-constexpr int kOffCandKey = kOffEq + 8 * kMaxChunks;     // u32 [kCandCap]
+constexpr int kOffCandKey = 0;                           // u32 [kCandCap]
 constexpr int kOffCandCol = kOffCandKey + kCandCap;      // u32 [kCandCap]
 constexpr int kOffPtab = kOffCandCol + kCandCap;         // i32 [kPtabCache]
 constexpr int kOffSmall = kOffPtab + kPtabCache;         // u32 [kSmallBins]
-constexpr int kOffCnt = kOffSmall + kSmallBins;          // u32 [2 * kMaxChunks] chunk counts
-static_assert(kOffCnt + 2 * kMaxChunks <= kHistWords, "LDS regions must fit in the histogram's space");
-static_assert(kWaves * 256 <= kSmallBins, "one 256-bin histogram per wave fits the small region");
-static_assert(2 * kMaxChunks <= kCandCap, "chunk offsets reuse the candidate region");
+constexpr int kOffGCnt = kOffSmall + kSmallBins;         // u32 [kMaxUnits] per-unit counts
+constexpr int kOffECnt = kOffGCnt + kMaxUnits;           // u32 [kMaxUnits]
+constexpr int kOffOut = kOffECnt + kMaxUnits;            // i32 [kMaxTopK] winners' columns
+constexpr int kFineWords = kSmallBins + kSmallBins / 32; // second-digit histogram (padded layout)
+constexpr int kOffFine = kOffOut + kMaxTopK;             // u32 [kFineWords]
+static_assert(kOffFine + kFineWords <= kHistWords, "LDS regions must fit in the histogram's space");
+static_assert(kUnitsPerLane <= 6, "unit scan layout");
+static_assert(kBinsPerThread % 4 == 0 && kBinsPerThread <= 64, "histogram layout");
 
 // Order-preserving key of a float score: larger float <-> larger unsigned key.  Adding +0.0
 // turns -0.0 into +0.0 (so the two compare equal) and leaves every other value unchanged.
@@ -67,15 +72,23 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 
-// Word of bin (key >> 17) in the first-digit histogram.  With B = kBinsPerThread, bin b sits at
-// word b + b/B, so that thread t sums its B bins [Bt, Bt+B) at words (B+1)t.. with no two
-// lanes of a wave on one LDS bank.
-__device__ __forceinline__ uint32_t hist_word(uint32_t key) { return (key >> 17) + (key >> (17 + kBinShift)); }
+// Word of bin (key >> 17) in the first-digit histogram.  Thread t's B = kBinsPerThread bins
+// [Bt, Bt+B) sit at words kHistStride*t.., 16-byte aligned, so that the per-thread sums are
+// read as b128 and the 16 lanes of one LDS pass start on distinct banks.
+__device__ __forceinline__ uint32_t hist_word(uint32_t key) {
+  return (key >> 17) + (kHistStride - kBinsPerThread) * (key >> (17 + kBinShift));
+}
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
-__device__ __forceinline__ uint32_t mbcnt(uint64_t m) {
-  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+// A compile-time flag, so that a uniform run-time choice is taken once outside a row loop.
+template <bool B>
+struct Flag {
+  static constexpr bool value = B;
+};
+
+__device__ __forceinline__ uint32_t mbcnt(uint64_t m, uint32_t add = 0u) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, add));
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave: shifts by 1, 2, 4, 8 inside each row of
@@ -136,9 +149,14 @@ __device__ __forceinline__ uint32_t select_bin(const uint32_t* hist, int nb, uin
   return bin;
 }
 
-// One wave: among the 64*M bins h[0..64M) scanned from the top, the bin holding the kr-th
-// largest key.  Lane l owns the bins 64M-1-Ml .. 64M-M-Ml.  Every lane gets the bin, the count
-// of keys above it and the bin's own count.
+// Padded layout of 64*M bins for wave_select: bin b at word b + b/M, so that the M bins a
+// lane reads lie M+1 words (an odd stride) from its neighbours' and no two lanes share a bank.
+template <int M>
+__device__ __forceinline__ uint32_t pad_word(uint32_t b) { return b + b / M; }
+
+// One wave: among the 64*M bins of h (padded layout) scanned from the top, the bin holding the
+// kr-th largest key.  Lane l owns the bins 64M-1-Ml .. 64M-M-Ml.  Every lane gets the bin, the
+// count of keys above it and the bin's own count.
 template <int M>
 __device__ __forceinline__ void wave_select(const uint32_t* h, uint32_t kr, uint32_t& bin, uint32_t& above,
                                             uint32_t& cnt) {
@@ -146,7 +164,7 @@ __device__ __forceinline__ void wave_select(const uint32_t* h, uint32_t kr, uint
   uint32_t c[M], tot = 0;
 #pragma unroll
   for (int j = 0; j < M; ++j) {
-    c[j] = h[64 * M - 1 - M * lane - j];
+    c[j] = h[pad_word<M>(64 * M - 1 - M * lane - j)];
     tot += c[j];
   }
   uint32_t acc = wave_incl_scan(tot) - tot;
@@ -184,29 +202,18 @@ __device__ __forceinline__ uint32_t radix_round(KeysFn&& keys_fn, uint32_t pmask
   return select_bin(hist, nb, kr, red, sel, above, cnt);
 }
 
-// Keys of one float4 at virtual columns v0..v0+3 (real column = virtual - o).  `full`
-// (uniform in the wave) says that all of the wave's columns lie inside the row.
-__device__ __forceinline__ void to_keys(const f32x4& x, int v0, int o, int n, bool full, uint32_t (&key)[4]) {
-  if (full) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) key[j] = order_key(x[j]);
-  } else {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) key[j] = (uint32_t)(v0 + j - o) < (uint32_t)n ? order_key(x[j]) : 0u;
-  }
-}
-
-template <int V>
+template <int RV>
 __global__ __launch_bounds__(kThreads) void topk_kernel(TopkParams p) {
   __shared__ __attribute__((aligned(16))) uint32_t big[kHistWords];   // histogram, then the regions above
-  __shared__ uint32_t tsum[kThreads];
+  __shared__ uint32_t tsum[kThreads + kThreads / 8];   // padded layout of wave_select<8>
   __shared__ uint32_t red[kWaves];
   __shared__ uint32_t sel[4];
   __shared__ uint32_t wave_cnt[kWaves];
   __shared__ uint32_t cand_n;
 
   const int tid = threadIdx.x;
-  const int lane = lane_id(), wave = tid >> 6;
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform (kept in a scalar register)
   const int row = blockIdx.x;
   const int b = row / p.Q, i = row - b * p.Q;
   int n = p.seq_lens[b] - p.Q + i + 1;             // visible tokens of this row
@@ -227,24 +234,41 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkParams p) {
   }
 
   // ---- pass 1: keys (registers), page-table row (registers), first-digit histogram
+  constexpr int kRegRows = RV * kWaves;              // key rows held in registers
   const float* srow = p.scores + (int64_t)row * p.ld;
-  const int o = (int)(((uintptr_t)srow >> 2) & 3);  // leading columns of the aligned view
-  const f32x4* vrow = (const f32x4*)(srow - o);
-  const int nv = n + o;                              // virtual columns
-  const int nvec = (nv + 3) >> 2;
+  const int nrows = (n + 63) >> 6;
+  const int nseg = nrows > kRegRows ? (nrows - kRegRows + kTailRows * kWaves - 1) / (kTailRows * kWaves) : 0;
   const int npages = (n + p.P - 1) / p.P;
   const bool cache_pages = slot_out != nullptr && npages <= kPtabCache;
-  // a wave's 256 columns of vector index vi lie inside the row: chunk >= 1 and not past nv
-  auto full_chunk = [&](int vi) { return (vi >> 6) > 0 && ((vi >> 6) + 1) * kChunkCols <= nv; };
-  uint32_t key[V][4];
+  // key row r (uniform) holds columns 64r .. 64r+63; register row j of wave w is row w*RV + j
+  auto key_of = [&](float x, int r) -> uint32_t {
+    return ((r + 1) << 6) <= n || (r << 6) + lane < n ? order_key(x) : 0u;
+  };
+  // the register block lies wholly inside the row (the common case): no per-row clamps
+  const bool reg_full = (kRegRows << 6) <= n;
+  uint32_t key[RV];
   {
-    f32x4 x[V];
+    float x[RV];
+    if (reg_full) {
+      const float* wrow = srow + ((wave * RV) << 6);   // uniform base, lane offset, constant row offsets
 #pragma unroll
-    for (int it = 0; it < V; ++it) x[it] = vrow[min(it * kThreads + tid, nvec - 1)];
+      for (int j = 0; j < RV; ++j) x[j] = wrow[(j << 6) + lane];
+    } else {
 #pragma unroll
-    for (int it = 0; it < V; ++it) {
-      const int vi = it * kThreads + tid;
-      to_keys(x[it], 4 * vi, o, n, full_chunk(vi), key[it]);
+      for (int j = 0; j < RV; ++j) x[j] = srow[min(((wave * RV + j) << 6) + lane, n - 1)];
+    }
+    // the histogram is cleared while the loads are in flight
+    u32x4* l4 = (u32x4*)big;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < (kHistWords / 4 + kThreads - 1) / kThreads; ++j)
+      if (j * kThreads + tid < kHistWords / 4) l4[j * kThreads + tid] = z;
+    if (reg_full) {
+#pragma unroll
+      for (int j = 0; j < RV; ++j) key[j] = order_key(x[j]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < RV; ++j) key[j] = key_of(x[j], wave * RV + j);
     }
   }
   int32_t pv[kPtabCache / kThreads];
@@ -252,41 +276,52 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkParams p) {
 #pragma unroll
     for (int u = 0; u < kPtabCache / kThreads; ++u) pv[u] = ptab[min(u * kThreads + tid, npages - 1)];
   }
-  {
-    u32x4* l4 = (u32x4*)big;
-    const u32x4 z = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int j = 0; j < (kHistWords / 4 + kThreads - 1) / kThreads; ++j)
-      if (j * kThreads + tid < kHistWords / 4) l4[j * kThreads + tid] = z;
-  }
 
-  // the streamed columns: f(keys of one float4, vector index) for every vector index >= V*512,
-  // in batches of kTailBatch loads per thread; called uniformly (it may hold ballots)
-  auto tail_pass = [&, vrow](auto&& f) {
-    for (int base = V * kThreads; base < nvec; base += kTailBatch * kThreads) {
-      f32x4 x[kTailBatch];
+  // The streamed key rows (from kRegRows on), in segments of kTailRows rows per wave.
+  // begin(s) and end(s) bracket this wave's rows of segment s; f(key, key row) is called
+  // uniformly per wave (it may hold ballots).
+  // Segment s+1 is loaded while segment s is processed (two register buffers).
+  auto tail_pass = [&, srow](auto&& f, auto&& begin, auto&& end) {
+    auto load = [&](float (&x)[kTailRows], int s) {
+      const int r0 = kRegRows + (s * kWaves + wave) * kTailRows;
+      if (((r0 + kTailRows) << 6) <= n) {
+        const float* wrow = srow + (r0 << 6);
 #pragma unroll
-      for (int u = 0; u < kTailBatch; ++u) x[u] = vrow[min(base + u * kThreads + tid, nvec - 1)];
+        for (int u = 0; u < kTailRows; ++u) x[u] = wrow[(u << 6) + lane];
+      } else {
 #pragma unroll
-      for (int u = 0; u < kTailBatch; ++u) {
-        if (base + u * kThreads < nvec) {          // uniform
-          uint32_t kk[4];
-          const int vi = base + u * kThreads + tid;
-          to_keys(x[u], 4 * vi, o, n, full_chunk(vi), kk);
-          f(kk, vi);
-        }
+        for (int u = 0; u < kTailRows; ++u) x[u] = srow[min(((r0 + u) << 6) + lane, n - 1)];
+      }
+    };
+    auto run = [&](const float (&x)[kTailRows], int s) {
+      const int r0 = kRegRows + (s * kWaves + wave) * kTailRows;
+      begin(s);
+      if (((r0 + kTailRows) << 6) <= n) {
+#pragma unroll
+        for (int u = 0; u < kTailRows; ++u) f(order_key(x[u]), r0 + u);
+      } else {
+#pragma unroll
+        for (int u = 0; u < kTailRows; ++u)
+          if (r0 + u < nrows) f(key_of(x[u], r0 + u), r0 + u);   // uniform
+      }
+      end(s);
+    };
+    float xa[kTailRows], xb[kTailRows];
+    if (nseg > 0) load(xa, 0);
+    for (int s = 0; s < nseg; s += 2) {
+      if (s + 1 < nseg) load(xb, s + 1);
+      run(xa, s);
+      if (s + 1 < nseg) {
+        if (s + 2 < nseg) load(xa, s + 2);
+        run(xb, s + 1);
       }
     }
   };
+  auto nop = [](int) {};
   auto all_keys = [&](auto&& visit) {
 #pragma unroll
-    for (int it = 0; it < V; ++it)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) visit(key[it][j]);
-    tail_pass([&](const uint32_t (&kk)[4], int) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) visit(kk[j]);
-    });
+    for (int j = 0; j < RV; ++j) visit(key[j]);
+    tail_pass([&](uint32_t kk, int) { visit(kk); }, nop, nop);
   };
 
   __syncthreads();
@@ -294,18 +329,18 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkParams p) {
     // a column outside the row counts into one of the bins 1..32, which no score uses (spread
     // so that a short row does not pile onto one LDS address)
     const uint32_t dummy = (uint32_t)(lane & 31) + 1u;
-    auto count = [&](const uint32_t (&kk)[4], int vi) {
-      if (full_chunk(vi)) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) atomicAdd(&big[hist_word(kk[j])], 1u);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) atomicAdd(&big[kk[j] ? hist_word(kk[j]) : dummy], 1u);
-      }
+    auto count = [&](uint32_t kk, int r) {
+      if (((r + 1) << 6) <= n) atomicAdd(&big[hist_word(kk)], 1u);
+      else if ((r << 6) < n) atomicAdd(&big[kk ? hist_word(kk) : dummy], 1u);
     };
+    if (reg_full) {
 #pragma unroll
-    for (int it = 0; it < V; ++it) count(key[it], it * kThreads + tid);
-    tail_pass(count);
+      for (int j = 0; j < RV; ++j) atomicAdd(&big[hist_word(key[j])], 1u);
+    } else {
+#pragma unroll
+      for (int j = 0; j < RV; ++j) count(key[j], wave * RV + j);
+    }
+    tail_pass(count, nop, nop);
   }
   __syncthreads();
   if (tid < 63) big[tid] = 0u;                       // bins 0..62 (words 0..62) hold no score
@@ -313,22 +348,21 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkParams p) {
 
   // ---- the first-digit bin: sums of kBinsPerThread bins per thread, then the bins of the chosen sum
   {
-    uint32_t s = 0;
-    const uint32_t* h = big + (kBinsPerThread + 1) * tid;
+    const u32x4* h4 = (const u32x4*)(big + kHistStride * tid);
+    u32x4 acc = h4[0];
 #pragma unroll
-    for (int j = 0; j < kBinsPerThread; ++j) s += h[j];
-    tsum[tid] = s;
+    for (int j = 1; j < kBinsPerThread / 4; ++j) acc += h4[j];
+    tsum[pad_word<kThreads / 64>(tid)] = acc[0] + acc[1] + acc[2] + acc[3];
   }
   __syncthreads();
   // every wave finds the same bin on its own (no further barrier)
-  static_assert(kThreads % 64 == 0 && kBinsPerThread <= 64, "wave selection layout");
   uint32_t r1, above, cnt;
   wave_select<kThreads / 64>(tsum, (uint32_t)k, r1, above, cnt);
   uint32_t kr = (uint32_t)k - above;
   uint32_t fb, above1;
   {
-    // the thread range's kBinsPerThread bins (padded layout), scanned from the top by one wave
-    const uint32_t* h = big + (kBinsPerThread + 1) * r1;
+    // the thread range's kBinsPerThread bins, scanned from the top by one wave
+    const uint32_t* h = big + kHistStride * r1;
     const uint32_t c1 = lane < kBinsPerThread ? h[kBinsPerThread - 1 - lane] : 0u;
     const uint32_t incl = wave_incl_scan(c1);
     const uint64_t m = __ballot(lane < kBinsPerThread && incl - c1 < kr && incl >= kr);
@@ -358,152 +392,157 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkParams p) {
     pval |= bin << shift;
     take_all = cnt == kr;
   }
-  // gather the bin's keys (<= kCandCap), unless the whole bin is taken or it is one key value
+  // Three cases: the whole bin is taken; the bin is one key value (its first kr keys in column
+  // order are taken); or the bin's keys are gathered and the exact threshold found among them.
   const bool gather = !take_all && plen < 32;
+  const bool count_eq = !take_all && plen == 32;
   const bool per_wave = cnt <= (uint32_t)kCandPerWave;   // no wave can overflow its region
   const uint32_t t_lo = pval, t_hi = pval | ~pmask;
-  // "above" threshold of pass 2: above the bin, or (whole bin taken) inside it too
-  const uint32_t t_gt = take_all ? t_lo - 1u : t_hi;
-  const bool store_eq = !gather && !take_all;       // the bin is one key value: store its masks
+  const uint32_t t_gt = take_all ? t_lo - 1u : t_hi;  // keys above t_gt are taken for sure
 
-  // ---- pass 2: classify every column; gather the bin's keys
-  uint64_t* m_gt = (uint64_t*)(big + kOffGt);
-  uint64_t* m_eq = (uint64_t*)(big + kOffEq);
+  // ---- pass 2: per unit, the count of keys above t_gt (and, for a one-value bin, inside it);
+  // gather the bin's keys
   uint32_t* cand_key = big + kOffCandKey;
   uint32_t* cand_col = big + kOffCandCol;
   int32_t* ptab_s = (int32_t*)(big + kOffPtab);
-  const int nch = (nv + kChunkCols - 1) / kChunkCols;
+  uint32_t* g_cnt = big + kOffGCnt;                  // per unit: keys taken as "above"
+  uint32_t* e_cnt = big + kOffECnt;                  // per unit: keys equal to the threshold
   if (cache_pages) {
 #pragma unroll
     for (int u = 0; u < kPtabCache / kThreads; ++u) ptab_s[u * kThreads + tid] = pv[u];
   }
-  uint32_t* g_cnt = big + kOffCnt;                  // per chunk: keys taken as "above"
-  uint32_t* e_cnt = g_cnt + kMaxChunks;              // per chunk: keys equal to the threshold
-  if (!store_eq)
-    for (int j = tid; j < 4 * nch; j += kThreads) m_eq[j] = 0ull;
+  // second digit: the D2 key bits below the bin's prefix, counted over the gathered keys
+  const int D2 = min(kSmallBits, 32 - plen);
+  const int sh2 = 32 - plen - D2;
+  uint32_t* fhist = big + kOffFine;
+  for (int j = tid; j < kFineWords; j += kThreads) fhist[j] = 0u;
   if (tid == 0) cand_n = 0u;
   __syncthreads();
   uint32_t wcount = 0;                               // candidates of this wave so far (uniform)
+  uint32_t ug = 0, ue = 0;                           // this lane's counts in the current unit
   // (the LDS region pointers are captured by value so that they stay in registers)
-  auto classify = [&, m_gt, m_eq, cand_key, cand_col, g_cnt, e_cnt](const uint32_t (&kk)[4], int vi) {
-    uint64_t mg[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) mg[j] = __ballot(kk[j] > t_gt);
-    const int e = vi >> 6;                           // chunk of 256 columns (uniform in the wave)
+  auto unit_done = [&, g_cnt, e_cnt](int u) {
+    const uint32_t gs = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(ug), 63);
+    const uint32_t es = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(ue), 63);
     if (lane == 0) {
-      g_cnt[e] = (uint32_t)(__popcll(mg[0]) + __popcll(mg[1]) + __popcll(mg[2]) + __popcll(mg[3]));
-      if (!store_eq) e_cnt[e] = 0u;
-      u32x4* g4 = (u32x4*)(m_gt + 4 * e);
-      g4[0] = u32x4{(uint32_t)mg[0], (uint32_t)(mg[0] >> 32), (uint32_t)mg[1], (uint32_t)(mg[1] >> 32)};
-      g4[1] = u32x4{(uint32_t)mg[2], (uint32_t)(mg[2] >> 32), (uint32_t)mg[3], (uint32_t)(mg[3] >> 32)};
+      g_cnt[u] = gs;
+      e_cnt[u] = es;
     }
-    if (gather || store_eq) {
-      bool in[4];
-      uint64_t me[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        in[j] = kk[j] - t_lo <= t_hi - t_lo;         // t_lo <= key <= t_hi (key 0 < t_lo wraps high)
-        me[j] = __ballot(in[j]);
-      }
-      if (store_eq) {
-        if (lane == 0) {
-          e_cnt[e] = (uint32_t)(__popcll(me[0]) + __popcll(me[1]) + __popcll(me[2]) + __popcll(me[3]));
-          u32x4* e4 = (u32x4*)(m_eq + 4 * e);
-          e4[0] = u32x4{(uint32_t)me[0], (uint32_t)(me[0] >> 32), (uint32_t)me[1], (uint32_t)(me[1] >> 32)};
-          e4[1] = u32x4{(uint32_t)me[2], (uint32_t)(me[2] >> 32), (uint32_t)me[3], (uint32_t)(me[3] >> 32)};
-        }
-      } else {
-        const uint32_t c0 = (uint32_t)__popcll(me[0]), c1 = (uint32_t)__popcll(me[1]);
-        const uint32_t c2 = (uint32_t)__popcll(me[2]), c3 = (uint32_t)__popcll(me[3]);
-        const uint32_t tot = c0 + c1 + c2 + c3;
-        if (tot) {                                   // uniform
-          uint32_t base;
-          if (per_wave) {
-            base = wave * kCandPerWave + wcount;
-            wcount += tot;
-          } else {
-            uint32_t b0 = 0;
-            if (lane == 0) b0 = atomicAdd(&cand_n, tot);
-            base = __builtin_amdgcn_readfirstlane(b0);
-          }
-          const uint32_t pre[4] = {base, base + c0, base + c0 + c1, base + c0 + c1 + c2};
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            if (in[j]) {
-              const uint32_t pos = pre[j] + mbcnt(me[j]);
-              cand_key[pos] = kk[j];
-              cand_col[pos] = (uint32_t)(4 * vi + j);
-            }
-          }
-        }
-      }
-    }
+    ug = 0u;
+    ue = 0u;
   };
+  // G: gather the bin's keys; PW: into per-wave regions; CE: count the keys equal to t_lo
+  auto pass2 = [&, cand_key, cand_col](auto G, auto PW, auto CE) {
+    auto classify = [&](uint32_t kk, int r) {
+      ug += kk > t_gt ? 1u : 0u;
+      if constexpr (decltype(CE)::value) ue += kk == t_lo ? 1u : 0u;
+      if constexpr (decltype(G)::value) {
+        const bool in = kk - t_lo <= t_hi - t_lo;   // t_lo <= key <= t_hi (key 0 < t_lo wraps high)
+        const uint64_t me = __ballot(in);
+        if constexpr (decltype(PW)::value) {
+          if (in) {
+            const uint32_t pos = mbcnt(me, wave * kCandPerWave + wcount);
+            cand_key[pos] = kk;
+            cand_col[pos] = (uint32_t)((r << 6) + lane);
+          }
+          wcount += (uint32_t)__popcll(me);
+        } else if (me) {                             // uniform
+          uint32_t b0 = 0;
+          if (lane == 0) b0 = atomicAdd(&cand_n, (uint32_t)__popcll(me));
+          const uint32_t base = __builtin_amdgcn_readfirstlane(b0);
+          if (in) {
+            const uint32_t pos = base + mbcnt(me);
+            cand_key[pos] = kk;
+            cand_col[pos] = (uint32_t)((r << 6) + lane);
+          }
+        }
+      }
+    };
 #pragma unroll
-  for (int it = 0; it < V; ++it) classify(key[it], it * kThreads + tid);
-  tail_pass(classify);
+    for (int j = 0; j < RV; ++j) classify(key[j], wave * RV + j);
+    unit_done(wave);
+    tail_pass(classify, nop, [&](int s) { unit_done(kWaves * (1 + s) + wave); });
+  };
+  if (gather) {
+    if (per_wave) pass2(Flag<true>(), Flag<true>(), Flag<false>());
+    else pass2(Flag<true>(), Flag<false>(), Flag<false>());
+  } else if (count_eq) {
+    pass2(Flag<false>(), Flag<false>(), Flag<true>());
+  } else {
+    pass2(Flag<false>(), Flag<false>(), Flag<false>());
+  }
   if (lane == 0) wave_cnt[wave] = wcount;
   __syncthreads();
 
-  // ---- the exact threshold among the candidates, and the candidates' mask bits and counts
+  // ---- the exact threshold among the candidates; their counts are added to their units
+  uint32_t Tg = t_gt, quota = 0u;                    // taken: key > Tg, or key == Tg among the first quota
+  if (count_eq) {
+    Tg = t_lo;
+    quota = kr;
+  }
   if (gather) {
     uint32_t T;
     auto fix = [&, cand_key, cand_col](int j) {
       const uint32_t u = cand_key[j], v = cand_col[j];
-      const int mi = (int)(v >> 8) * 4 + (int)(v & 3);
-      const uint64_t bit = 1ull << ((v >> 2) & 63);
-      if (u >= T) {   // one LDS word offset picks the mask and count array (no pointer select)
-        const int which = u > T ? 0 : 1;
-        atomicOr((unsigned long long*)&big[kOffGt + which * (kOffEq - kOffGt) + 2 * mi], bit);
-        atomicAdd(&big[kOffCnt + which * kMaxChunks + (int)(v >> 8)], 1u);
+      if (u >= T) {   // one LDS word offset picks the count array (no pointer select)
+        const int r = (int)(v >> 6);
+        const int unit = r < kRegRows ? r / RV
+                                      : kWaves * (1 + (r - kRegRows) / (kTailRows * kWaves)) +
+                                            ((r - kRegRows) % (kTailRows * kWaves)) / kTailRows;
+        atomicAdd(&big[(u > T ? kOffGCnt : kOffECnt) + unit], 1u);
       }
     };
     if (per_wave) {
-      // every wave selects T on its own from all <= kCandPerWave candidates (8 per lane at most),
-      // then fixes up the candidates of its own region
+      // every wave finds T on its own from all <= kCandPerWave candidates (up to kPerLane per
+      // lane), one key bit at a time with ballot counts, then counts its own region's candidates
       uint32_t rb[kWaves + 1];
       rb[0] = 0;
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) rb[w + 1] = rb[w] + wave_cnt[w];
+      // the second digit (the D2 key bits below the prefix): one candidate per thread is counted
+      static_assert(kCandPerWave <= kThreads, "one candidate per thread");
+      if ((uint32_t)tid < cnt) {
+        int w = 0;
+#pragma unroll
+        for (int ww = 1; ww < kWaves; ++ww) w += (uint32_t)tid >= rb[ww];
+        const uint32_t u = cand_key[w * kCandPerWave + ((uint32_t)tid - rb[w])];
+        atomicAdd(&fhist[pad_word<kSmallBins / 64>(__builtin_amdgcn_ubfe(u, sh2, D2))], 1u);
+      }
       constexpr int kPerLane = (kCandPerWave + 63) / 64;
       uint32_t c[kPerLane];
 #pragma unroll
-      for (int r = 0; r < kPerLane; ++r) {
-        const uint32_t g = (uint32_t)(r * 64 + lane);
+      for (int q = 0; q < kPerLane; ++q) {
+        const uint32_t g = (uint32_t)(q * 64 + lane);
         int w = 0;
 #pragma unroll
         for (int ww = 1; ww < kWaves; ++ww) w += g >= rb[ww];
-        c[r] = g < cnt ? cand_key[w * kCandPerWave + (g - rb[w])] : 0u;
+        c[q] = g < cnt ? cand_key[w * kCandPerWave + (g - rb[w])] : 0u;   // 0 never matches a prefix
       }
-      if (cnt <= 64u) {
-        uint32_t cgt = 0, cge = 0;
-        for (int j = 0; j < (int)cnt; ++j) {         // lane j's key, read into a scalar register
-          const uint32_t q = (uint32_t)__builtin_amdgcn_readlane((int)c[0], j);
-          cgt += q > c[0];
-          cge += q >= c[0];
-        }
-        const uint64_t m = __ballot(lane < (int)cnt && cgt < kr && kr <= cge);
-        const int src = (int)__builtin_ctzll(m | (1ull << 63));
-        T = (uint32_t)__builtin_amdgcn_readlane((int)c[0], src);
-        kr -= (uint32_t)__builtin_amdgcn_readlane((int)cgt, src);
-      } else {
-        uint32_t* wh = shist + wave * 256;           // this wave's 256-bin histogram
-        while (plen < 32) {
-          const int D = min(8, 32 - plen);
-          const int shift = 32 - plen - D;
-          ((u32x4*)wh)[lane] = u32x4{0u, 0u, 0u, 0u};
+      __syncthreads();
+      // the second digit's bin (bins past 2^D2 are empty)
+      {
+        uint32_t bin2, ab2, c2;
+        wave_select<kSmallBins / 64>(fhist, kr, bin2, ab2, c2);
+        kr -= ab2;
+        plen += D2;
+        pmask = plen == 32 ? ~0u : ~0u << (32 - plen);
+        pval |= bin2 << sh2;
+      }
+      // the bit search visits only the candidate rows that hold keys of the prefix
+      bool live[kPerLane];
 #pragma unroll
-          for (int r = 0; r < kPerLane; ++r)
-            if (c[r] && (c[r] & pmask) == pval) atomicAdd(&wh[__builtin_amdgcn_ubfe(c[r], shift, D)], 1u);
-          uint32_t bin, ab, bc;
-          wave_select<4>(wh, kr, bin, ab, bc);       // bins past 2^D hold nothing
-          kr -= ab;
-          plen += D;
-          pmask = plen == 32 ? ~0u : ~0u << (32 - plen);
-          pval |= bin << shift;
-        }
-        T = pval;
+      for (int q = 0; q < kPerLane; ++q) live[q] = __ballot((c[q] & pmask) == pval) != 0ull;
+      for (int bit = 31 - plen; bit >= 0; --bit) {
+        const uint32_t m = pmask | (1u << bit), v = pval | (1u << bit);
+        uint32_t cb = 0;
+#pragma unroll
+        for (int q = 0; q < kPerLane; ++q)
+          if (live[q]) cb += (uint32_t)__popcll(__ballot((c[q] & m) == v));
+        if (cb >= kr) pval = v;
+        else kr -= cb;
+        pmask = m;
       }
+      T = pval;
       for (int j = lane; j < (int)wave_cnt[wave]; j += 64) fix(wave * kCandPerWave + j);
     } else {
       auto cand_keys = [&](auto&& visit) {
@@ -513,8 +552,8 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkParams p) {
       while (plen < 32) {
         const int D = min(kSmallBits, 32 - plen);
         const int shift = 32 - plen - D;
-        uint32_t ab, c;
-        const uint32_t bin = radix_round(cand_keys, pmask, pval, shift, D, kr, shist, red, sel, &ab, &c);
+        uint32_t ab, cc;
+        const uint32_t bin = radix_round(cand_keys, pmask, pval, shift, D, kr, shist, red, sel, &ab, &cc);
         kr -= ab;
         plen += D;
         pmask = plen == 32 ? ~0u : ~0u << (32 - plen);
@@ -524,92 +563,100 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkParams p) {
       const int nc = (int)cand_n;
       for (int j = tid; j < nc; j += kThreads) fix(j);
     }
+    Tg = T;
+    quota = kr;
     __syncthreads();
   }
 
-  // ---- order-preserving output.  Chunk offsets: a scan of the chunks' counts in column
-  // order.  Then 64-column groups (chunk e, lane bit j: columns e*256 + 4l + j) are walked one
-  // per thread; a winner's offset in its chunk counts the chunk's set bits in lower lanes and
-  // in lower j of its own lane.
-  uint32_t* pre_g = big + kOffCandKey;               // the candidates are no longer needed
-  uint32_t* pre_e = pre_g + kMaxChunks;
+  // ---- order-preserving output.  Every wave scans all units' counts (no barrier): a unit's
+  // output offset counts the keys taken in earlier units, where the keys equal to Tg are taken
+  // in column order until quota of them are.
+  constexpr int U = kUnitsPerLane;
+  const int nunits = kWaves * (1 + nseg);
+  uint32_t u_base[U], u_eq[U], e_total;
   {
-    // thread t scans the chunks [t*C, t*C + C) in one block-wide pass
-    constexpr int C = (kMaxChunks + kThreads - 1) / kThreads;
-    uint32_t gc[C], ec[C], gs = 0, es = 0;
+    uint32_t gc[U], ec[U], es = 0;
 #pragma unroll
-    for (int c = 0; c < C; ++c) {
-      const int e = tid * C + c;
-      gc[c] = e < nch ? g_cnt[e] : 0u;
-      ec[c] = e < nch ? e_cnt[e] : 0u;
-      gs += gc[c];
-      es += ec[c];
+    for (int a = 0; a < U; ++a) {
+      const int u = lane * U + a;
+      gc[a] = u < nunits ? g_cnt[u] : 0u;
+      ec[a] = u < nunits ? e_cnt[u] : 0u;
+      es += ec[a];
     }
-    uint32_t gb = block_incl_scan(gs, red) - gs;
-    uint32_t eb = block_incl_scan(es, red) - es;
+    uint32_t eb = wave_incl_scan(es);
+    e_total = (uint32_t)__builtin_amdgcn_readlane((int)eb, 63);
+    eb -= es;
+    uint32_t tk[U], ts = 0;
 #pragma unroll
-    for (int c = 0; c < C; ++c) {
-      const int e = tid * C + c;
-      if (e < nch) {
-        pre_g[e] = gb;
-        pre_e[e] = eb;
-      }
-      gb += gc[c];
-      eb += ec[c];
+    for (int a = 0; a < U; ++a) {
+      u_eq[a] = eb;
+      tk[a] = gc[a] + min(ec[a], quota - min(eb, quota));
+      eb += ec[a];
+      ts += tk[a];
     }
-    __syncthreads();
+    uint32_t tb = wave_incl_scan(ts) - ts;
+#pragma unroll
+    for (int a = 0; a < U; ++a) {
+      u_base[a] = tb;
+      tb += tk[a];
+    }
   }
+  // (taken before, equal keys before) of unit u, uniform: read from lane u/U, then the element
+  // picked among scalars (a run-time index into the per-lane arrays would move them to memory)
+  auto unit_start = [&](int u, uint32_t& tb, uint32_t& eb) {
+    const int l = u / U, a = u - l * U;
+    tb = (uint32_t)__builtin_amdgcn_readlane((int)u_base[0], l);
+    eb = (uint32_t)__builtin_amdgcn_readlane((int)u_eq[0], l);
+#pragma unroll
+    for (int aa = 1; aa < U; ++aa) {
+      const uint32_t tv = (uint32_t)__builtin_amdgcn_readlane((int)u_base[aa], l);
+      const uint32_t ev = (uint32_t)__builtin_amdgcn_readlane((int)u_eq[aa], l);
+      tb = a == aa ? tv : tb;
+      eb = a == aa ? ev : eb;
+    }
+  };
+  // When every key equal to Tg is taken (no tie to break) a key is taken iff key >= t_take.
+  const bool ties = quota < e_total;
+  const uint32_t t_take = quota == 0u ? Tg + 1u : Tg;
+  int32_t* out_s = (int32_t*)(big + kOffOut);
+  auto emit_all = [&, out_s](auto TIES) {
+    uint32_t obase, eqr;                             // uniform: taken so far, equal keys so far
+    auto emit = [&](uint32_t kk, int r) {
+      bool take;
+      if constexpr (decltype(TIES)::value) {
+        const bool eq = kk == Tg;
+        const uint64_t me = __ballot(eq);
+        take = kk > Tg || (eq && mbcnt(me, eqr) < quota);
+        eqr += (uint32_t)__popcll(me);
+      } else {
+        take = kk >= t_take;
+      }
+      const uint64_t mt = __ballot(take);
+      if (take) out_s[min(mbcnt(mt, obase), (uint32_t)kMaxTopK - 1u)] = (r << 6) + lane;
+      obase += (uint32_t)__popcll(mt);
+    };
+    unit_start(wave, obase, eqr);
+#pragma unroll
+    for (int j = 0; j < RV; ++j) emit(key[j], wave * RV + j);
+    tail_pass(emit, [&](int s) { unit_start(kWaves * (1 + s) + wave, obase, eqr); }, nop);
+  };
+  if (ties) emit_all(Flag<true>());
+  else emit_all(Flag<false>());
+  __syncthreads();
+  // the k winners, in column order, with their cache slots (fused page map)
   const int P = p.P;
   const bool p_pow2 = (P & (P - 1)) == 0;
   const int p_shift = __ffs(P) - 1;
-  // the page lookup is chosen once for the whole walk (LDS copy or global row), so that each
-  // load keeps its own address space
-  auto walk = [&](auto page_of) {
-  for (int q = tid; q < 4 * nch; q += kThreads) {
-    const int e = q >> 2, j = q & 3;
-    uint64_t mg[4], me[4];
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      mg[jj] = m_gt[4 * e + jj];
-      me[jj] = m_eq[4 * e + jj];
-    }
-    const uint32_t G = pre_g[e], E = pre_e[e];
-    const uint64_t mgj = j == 0 ? mg[0] : j == 1 ? mg[1] : j == 2 ? mg[2] : mg[3];
-    const uint64_t mej = j == 0 ? me[0] : j == 1 ? me[1] : j == 2 ? me[2] : me[3];
-    uint64_t bits = mgj | mej;
-    while (bits) {
-      const int l = __builtin_ctzll(bits);
-      bits &= bits - 1;
-      const uint64_t lt = (1ull << l) - 1;
-      uint32_t gb = G, eb = E;
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        gb += (uint32_t)__popcll(mg[jj] & lt) + (jj < j ? (uint32_t)(mg[jj] >> l) & 1u : 0u);
-        eb += (uint32_t)__popcll(me[jj] & lt) + (jj < j ? (uint32_t)(me[jj] >> l) & 1u : 0u);
-      }
-      bool take;
-      uint32_t pos;
-      if ((mgj >> l) & 1) {
-        take = true;
-        pos = gb + min(eb, kr);
-      } else {
-        take = eb < kr;
-        pos = gb + eb;
-      }
-      if (take && pos < (uint32_t)k) {
-        const int t = e * kChunkCols + 4 * l + j - o;
-        idx_out[pos] = t;
-        if (slot_out) {
-          const int pg = p_pow2 ? t >> p_shift : t / P;
-          const int off = t - pg * P;
-          slot_out[pos] = page_of(pg) * P + off;
-        }
-      }
+  for (int j = tid; j < k; j += kThreads) {
+    const int t = out_s[j];
+    idx_out[j] = t;
+    if (slot_out) {
+      int pg = p_pow2 ? t >> p_shift : t / P;
+      pg = min(max(pg, 0), npages - 1);            // (t is always in [0, n); the clamp only guards the lookup)
+      const int pe = cache_pages ? big[kOffPtab + pg] : ptab[pg];
+      slot_out[j] = pe * P + (t - pg * P);
     }
   }
-  };
-  if (cache_pages) walk([&](int pg) { return big[kOffPtab + pg]; });
-  else walk([&](int pg) { return ptab[pg]; });
 }
 
 __global__ __launch_bounds__(256) void page_map_kernel(const int32_t* idx, int64_t total, int k, int Q,
@@ -632,14 +679,14 @@ size_t topk_workspace_bytes(int64_t rows, int max_seq_len) {
 
 hipError_t launch_topk(const TopkParams& p, int rows, int max_seq_len, void* ws, hipStream_t s) {
   (void)ws;
-  // 4, 8 or 16 float4 per thread stay in registers (up to 32K columns, plus up to 3 leading
-  // columns of the aligned view); columns past that are re-read from L2 in each pass.
+  // 8, 16, 32 or 64 key rows per wave stay in registers (up to 32K columns); rows past that
+  // are re-read from L2 in each pass.
   const dim3 grid((unsigned)rows), block(kThreads);
-  const int nv = max_seq_len + 3;
-  constexpr int kMaxV = kThreads >= 1024 ? 8 : 16;
-  if (nv <= 4 * 4 * kThreads) hipLaunchKernelGGL(topk_kernel<4>, grid, block, 0, s, p);
-  else if (nv <= 8 * 4 * kThreads || kMaxV == 8) hipLaunchKernelGGL(topk_kernel<8>, grid, block, 0, s, p);
-  else hipLaunchKernelGGL(topk_kernel<kMaxV>, grid, block, 0, s, p);
+  const int need = (max_seq_len + 64 * kWaves - 1) / (64 * kWaves);   // key rows per wave
+  if (need <= 8) hipLaunchKernelGGL(topk_kernel<8>, grid, block, 0, s, p);
+  else if (need <= 16) hipLaunchKernelGGL(topk_kernel<16>, grid, block, 0, s, p);
+  else if (need <= 32) hipLaunchKernelGGL(topk_kernel<32>, grid, block, 0, s, p);
+  else hipLaunchKernelGGL(topk_kernel<64>, grid, block, 0, s, p);
   return hipGetLastError();
 }
 
