@@ -175,7 +175,7 @@ int32_t effective_split(int64_t rows, int32_t H, int32_t k, int32_t n_split, dsa
 }
 
 dsa_status_t run_mla(int64_t rows, const void* q, dsa_dtype_t q_dtype, const void* kv, dsa_dtype_t kv_dtype,
-                     const float* kv_scale, const int32_t* slots, int32_t k, int32_t H, float sm_scale, float* out,
+                     const float* kv_scale, int64_t num_slots, const int32_t* slots, int32_t k, int32_t H, float sm_scale, float* out,
                      float* lse, int32_t ns, void* ws, size_t ws_bytes, hipStream_t s) {
   MlaWs w = mla_ws(rows, H, ns);
   if (ws_bytes < w.total || (w.total > 0 && ws == nullptr))
@@ -185,6 +185,7 @@ dsa_status_t run_mla(int64_t rows, const void* q, dsa_dtype_t q_dtype, const voi
   p.q = q;
   p.kv = kv;
   p.kv_scale = kv_dtype == DSA_FP8_E4M3FN ? kv_scale : nullptr;
+  p.num_slots = num_slots;
   p.slots = slots;
   p.out = out;
   p.lse = lse;
@@ -303,7 +304,7 @@ dsa_status_t dsa_sparse_mla_decode(int32_t batch, int32_t q_per_seq, const void*
   if (workspace_bytes < w.total || (w.total > 0 && workspace == nullptr))
     return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "mla: workspace needs %zu bytes (got %zu)", w.total, workspace_bytes);
   DSA_TRY(check_device());
-  return run_mla(rows, q, q_dtype, kv_cache, kv_dtype, kv_scale, slots, k, n_heads, sm_scale, out, lse, ns,
+  return run_mla(rows, q, q_dtype, kv_cache, kv_dtype, kv_scale, num_slots, slots, k, n_heads, sm_scale, out, lse, ns,
                  workspace, workspace_bytes, (hipStream_t)stream);
 }
 
@@ -405,7 +406,7 @@ dsa_status_t dsa_decode_step(const dsa_decode_step_args_t* a, void* workspace, s
 
   const int64_t rows = (int64_t)b->batch * b->q_per_seq;
   const size_t mla_bytes = workspace_bytes - w.mla_off;
-  return run_mla(rows, a->q_mla, a->q_mla_dtype, a->kv_cache, a->kv_dtype, a->kv_scale, slots, a->top_k,
+  return run_mla(rows, a->q_mla, a->q_mla_dtype, a->kv_cache, a->kv_dtype, a->kv_scale, b->num_slots, slots, a->top_k,
                  a->mla_heads, a->sm_scale, a->out, a->lse, w.ns, ws + w.mla_off, mla_bytes, s);
 }
 

@@ -40,6 +40,60 @@ __device__ __forceinline__ float fp8_to_f32(uint32_t code) {
   return __builtin_amdgcn_cvt_f32_fp8(code, 0);
 }
 
+// 8 e4m3fn bytes (two words) -> 8 bf16, exact
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// Direct global -> LDS copies: every lane reads `size` bytes at its own address and lane i's
+// bytes land at lds_base + i*size (lds_base must be uniform).  Tracked by the vector-memory
+// count like any load.
+__device__ __forceinline__ void lds_dma16(const void* src, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
+__device__ __forceinline__ void lds_dma4(const void* src, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_base, 4, 0, 0);
+}
+
+// The same copy through a buffer resource over `rows` records of `stride` bytes: lane i reads
+// 16 (or 4) bytes at record `row`, byte `off` inside it, and they land at lds_base + i*16 (i*4).
+// A record index past the resource's last record reads zeros.  Unlike the global form, the
+// compiler does not count these copies as pending LDS operations, so the waits it places for
+// later LDS reads stay partial.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, int stride, int64_t rows) {
+  const int n = rows > 0x7fffffffLL ? 0x7fffffff : (int)rows;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)stride, n, 0x00020000);
+}
+__device__ __forceinline__ void lds_dma16_row(__amdgpu_buffer_rsrc_t rsrc, int row, int off, void* lds_base) {
+  __builtin_amdgcn_struct_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds_base, 16, row, off, 0, 0,
+                                              0);
+}
+__device__ __forceinline__ void lds_dma4_row(__amdgpu_buffer_rsrc_t rsrc, int row, void* lds_base) {
+  __builtin_amdgcn_struct_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds_base, 4, row, 0, 0, 0, 0);
+}
+
+// s_waitcnt with only the vector-memory count limited (gfx9 encoding: vmcnt bits 3:0 and 15:14,
+// expcnt 6:4 and lgkmcnt 11:8 at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier for rings filled by direct-to-LDS copies.  It waits only for this wave's
+// LDS operations (lgkmcnt 0), not for vector-memory operations in flight, which the caller
+// bounds with wait_vmcnt beforehand: a __syncthreads also orders global memory, which here
+// means waiting for every load in flight, copies into later ring slots included.  The memory
+// clobber keeps the compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);   // vmcnt 63, expcnt 7, lgkmcnt 0
+  asm volatile("s_barrier" ::: "memory");
+}
+
 // ---------------------------------------------------------------------------------------------
 // launch parameter blocks (plain structs passed by value to the kernels)
 
@@ -74,6 +128,7 @@ struct MlaParams {
   const void* kv;
   const float* kv_scale;
   const int32_t* slots;
+  int64_t num_slots; // rows of kv (and kv_scale)
   float* out;        // [rows, H, 512] when n_split == 1
   float* lse;        // [rows, H] or null (n_split == 1)
   float* part_o;     // [rows, n_split, H, 512] when n_split > 1

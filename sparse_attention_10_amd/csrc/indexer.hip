@@ -105,20 +105,6 @@ struct Geo {
 template <bool FP8>
 __device__ __forceinline__ int swz(int r) { return FP8 ? ((r >> 1) & 7) : (r & 15); }
 
-__device__ __forceinline__ void lds_dma16(const void* src, void* lds_base) {
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
-}
-__device__ __forceinline__ void lds_dma4(const void* src, void* lds_base) {
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_base, 4, 0, 0);
-}
-
-// s_waitcnt with only the vector-memory count limited (gfx9 encoding: vmcnt bits 3:0 and 15:14,
-// expcnt 6:4 and lgkmcnt 11:8 at their maxima)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
 
 // CONTIG (32 divides P): a sub-tile's 32 tokens are one 32-aligned run inside one page, so its
 // key rows are contiguous in the cache and one page lookup per sub-tile gives every address.

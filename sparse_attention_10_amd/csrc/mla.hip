@@ -390,6 +390,551 @@ __global__ __launch_bounds__(kNT) void mla_mfma_kernel(MlaParams p) {
 }
 
 // ---------------------------------------------------------------------------------------------
+// fp8 rows: the same wave roles as mla_mfma_kernel, but the tile stays in e4m3fn in LDS and is
+// widened to bf16 only as MFMA operands, which halves the LDS bytes written and read per token.
+//   * Loads go straight from HBM into a ring of kRing tile buffers (direct-to-LDS copies, 16
+//     bytes per lane, no register staging); kRing-1 tiles are in flight while one is computed.
+//     Each 1 KiB copy reads whole rows (consecutive lanes, consecutive 16-byte pieces).
+//   * Layout of a tile buffer: token t's row at t*576, its piece p (16 latent values) in slot
+//     p ^ swz(t), swz(t) = bit 2 of t | (bit 3 ^ bit 4 of t) << 1 (a permutation inside each
+//     aligned group of 4 pieces).  The S^T operand reads (16 tokens of one block, one piece)
+//     and the transposing V^T reads (tokens 4g..4g+3 and 16+4g..16+4g+3 of lane group g) then
+//     each cover all 64 LDS banks once per 32 lanes.
+//   * S^T block beta holds tokens 16*beta .. 16*beta+15; lane group g of the S^T result holds
+//     tokens 4g+j of both blocks, so the P.V contraction runs over the tokens in the order
+//     tau(g, e) = 4g + e (e < 4), 16 + 4g + e - 4 (e >= 4), the same order in which the
+//     transposing 8-bit read (ds_read_b64_tr_b8: the 16 lanes of a group supply 8 rows of 16
+//     bytes, lane L gets column L) hands each lane its 8 V values.
+//   * A token past the chunk or with slot -1 loads row 0 and is then zeroed in LDS, and its
+//     logit is -inf.
+
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+constexpr int kRing = 4;                                  // tile buffers (kRing-1 tiles in flight)
+constexpr int kFp8Pieces = kRowDim / 16;                  // 36 pieces of 16 values per row
+constexpr int kFp8TileBytes = kFp8Pieces * kTT * 16;      // 18432
+constexpr int kFp8Dma = kFp8Pieces / 2;                   // 18 wave-wide 1 KiB copies per tile
+
+__device__ __forceinline__ int fp8_swz(int t) { return ((t >> 2) & 1) | ((((t >> 3) ^ (t >> 4)) & 1) << 1); }
+// LDS byte offset of logical piece p of token t inside a tile buffer
+__device__ __forceinline__ int fp8_pos(int t, int p) { return t * kRowDim + ((p ^ fp8_swz(t)) << 4); }
+
+// loads one wave issues per tile: copies wave, wave+8, wave+16 (< 18), plus the scales (wave 2)
+__device__ __forceinline__ int fp8_loads_of_wave(int wave) { return (wave < 2 || wave == 2) ? 3 : 2; }
+
+__global__ __launch_bounds__(kNT) void mla_fp8_kernel(MlaParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kRing][kFp8TileBytes];
+  __shared__ __attribute__((aligned(16))) float sring[kRing][64];     // per-token scales (token t at t)
+  __shared__ __attribute__((aligned(16))) f32x4 xs[8][2][64];         // each wave's S^T half, per lane
+  __shared__ int32_t sl_lds[kMaxTopK + kTT];                          // this chunk's slots, -1 padded
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hg = wave & 3, kh = wave >> 2;
+  const int r = blockIdx.y, split = blockIdx.x;
+  const int j0 = split * p.chunk;
+  const int j1 = min(p.k, j0 + p.chunk);
+  const int ntiles = j1 > j0 ? (j1 - j0 + kTT - 1) / kTT : 0;
+  const int32_t* sl = p.slots + (int64_t)r * p.k;
+  const bool active = hg * 16 < p.H;
+  const int head = hg * 16 + (lane & 15);
+  const int grp = lane >> 4;
+  const uint8_t* kv = (const uint8_t*)p.kv;
+
+  // stage the chunk's slot list (one coalesced pass, every load issued before any is used)
+  {
+    const int span = ntiles * kTT;
+    for (int e0 = 0; e0 < span; e0 += 4 * kNT) {
+      int32_t v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = sl[min(j0 + e0 + u * kNT + (int)threadIdx.x, p.k - 1)];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = e0 + u * kNT + threadIdx.x;
+        if (e < span) sl_lds[e] = j0 + e < j1 ? v[u] : -1;
+      }
+    }
+  }
+  __syncthreads();
+
+  // copies of tile v: lane i of copy c fills LDS slot q = 64c + i, i.e. token q/36, slot q%36,
+  // which holds logical piece (q%36) ^ swz(token)
+  auto issue = [&](int v) {
+    uint8_t* base = ring[v % kRing];
+#pragma unroll
+    for (int c = 0; c < 3; ++c) {
+      const int cc = wave + 8 * c;
+      if (cc < kFp8Dma) {
+        const int q = cc * 64 + lane;
+        const int t = q / kFp8Pieces, sp = q - t * kFp8Pieces;
+        const int32_t sv = sl_lds[v * kTT + t];
+        const uint8_t* src = kv + (int64_t)(sv < 0 ? 0 : sv) * kRowDim + ((sp ^ fp8_swz(t)) << 4);
+        lds_dma16(src, base + cc * 1024);
+      }
+    }
+    if (wave == 2) {
+      const int32_t ss = sl_lds[v * kTT + (lane & 31)];
+      lds_dma4(p.kv_scale + (ss < 0 ? 0 : ss), sring[v % kRing]);
+    }
+  };
+
+  // q fragments (B operand of S^T): head lane%16, dims (9kh + s)*32 + grp*8 .. +8
+  bf16x8 qf[kKSteps];
+  if (active) {
+    const bf16x8* qrow = (const bf16x8*)((const __bf16*)p.q + ((int64_t)r * p.H + head) * kRowDim);
+#pragma unroll
+    for (int s = 0; s < kKSteps; ++s) qf[s] = qrow[(kKSteps * kh + s) * 4 + grp];
+  }
+#pragma unroll
+  for (int v = 0; v < kRing - 1; ++v)
+    if (v < ntiles) issue(v);
+
+  f32x4 o[kDBlocks];
+#pragma unroll
+  for (int db = 0; db < kDBlocks; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY;   // running max of z * log2(e), per head
+  float l_run = 0.f;         // this lane group's share of sum exp2(z - m_run)
+  const float scale2 = p.sm_scale * kLog2e;
+
+  // per-lane LDS offsets inside a tile buffer
+  const int m16 = lane & 15;
+  // S^T operand of block beta, K step s: logical piece P0 + 2s (P0 = 18kh + grp/2), half grp%2
+  // of token 16beta + m16.  Steps of one parity differ by 32 bytes per step (the swizzle only
+  // permutes inside aligned groups of 4 pieces), so two bases per block cover all 9 steps.
+  const int P0 = 18 * kh + (grp >> 1);
+  int a_base[2][2];
+#pragma unroll
+  for (int beta = 0; beta < 2; ++beta) {
+    a_base[beta][0] = fp8_pos(16 * beta + m16, P0) + 8 * (grp & 1);
+    a_base[beta][1] = fp8_pos(16 * beta + m16, P0 + 2) + 8 * (grp & 1) - 32;
+  }
+  // V^T operand of dim block db (logical piece 16kh + db): row e = m16/2 of the group's 8x16
+  // block is token tau(grp, e); blocks 4 apart differ by 64 bytes
+  const int e_row = m16 >> 1;
+  const int tau = e_row < 4 ? 4 * grp + e_row : 16 + 4 * grp + (e_row - 4);
+  int v_base[4];
+#pragma unroll
+  for (int d4 = 0; d4 < 4; ++d4) v_base[d4] = fp8_pos(tau, 16 * kh + d4) + 8 * (m16 & 1);
+  const int wl = fp8_loads_of_wave(wave);
+
+  for (int v = 0; v < ntiles; ++v) {
+    const int later = min(kRing - 2, ntiles - 1 - v);   // tiles whose loads were issued after v's
+    if (wl == 3) {
+      if (later >= 2) wait_vmcnt<6>();
+      else if (later == 1) wait_vmcnt<3>();
+      else wait_vmcnt<0>();
+    } else {
+      if (later >= 2) wait_vmcnt<4>();
+      else if (later == 1) wait_vmcnt<2>();
+      else wait_vmcnt<0>();
+    }
+    lds_barrier();   // tile v landed for every wave; buffer (v-1) % kRing is no longer read
+    if (v + kRing - 1 < ntiles) issue(v + kRing - 1);
+    const int buf = v % kRing;
+    uint8_t* T = ring[buf];
+    const int toff = v * kTT;
+    // skipped tokens (past the chunk, or slot -1) read row 0: zero their rows
+    // (every wave reads the same slot list, so the choice is uniform over the workgroup)
+    if (__ballot(lane < kTT && sl_lds[toff + (lane & (kTT - 1))] < 0)) {
+      for (int e = threadIdx.x; e < kTT * kFp8Pieces; e += kNT) {
+        const int t = e / kFp8Pieces, pc = e - t * kFp8Pieces;
+        if (sl_lds[toff + t] < 0) *(u32x4*)(T + t * kRowDim + pc * 16) = u32x4{0u, 0u, 0u, 0u};
+      }
+      lds_barrier();
+    }
+
+    // ---- S^T half for the two 16-token blocks, K steps interleaved, operands read ahead
+    f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    if (active) {
+      constexpr int kAhead = 3;
+      u32x2 a0[kAhead], a1[kAhead];
+#pragma unroll
+      for (int s = 0; s < kAhead; ++s) {
+        a0[s] = *(const u32x2*)(T + a_base[0][s & 1] + 32 * s);
+        a1[s] = *(const u32x2*)(T + a_base[1][s & 1] + 32 * s);
+      }
+#pragma unroll
+      for (int s = 0; s < kKSteps; ++s) {
+        const u32x2 x0 = a0[s % kAhead], x1 = a1[s % kAhead];
+        if (s + kAhead < kKSteps) {
+          a0[s % kAhead] = *(const u32x2*)(T + a_base[0][(s + kAhead) & 1] + 32 * (s + kAhead));
+          a1[s % kAhead] = *(const u32x2*)(T + a_base[1][(s + kAhead) & 1] + 32 * (s + kAhead));
+        }
+        sacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16x8(x0[0], x0[1]), qf[s], sacc[0], 0, 0, 0);
+        sacc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16x8(x1[0], x1[1]), qf[s], sacc[1], 0, 0, 0);
+      }
+      xs[wave][0][lane] = sacc[0];
+      xs[wave][1][lane] = sacc[1];
+    }
+    lds_barrier();
+    if (active) {
+      // the full logits: half 0 + half 1, the same sum in both waves of the head group
+      const f32x4 s0 = xs[hg][0][lane] + xs[hg + 4][0][lane];
+      const f32x4 s1 = xs[hg][1][lane] + xs[hg + 4][1][lane];
+      // this lane holds head `head`, tokens 16*beta + 4*grp + j (K index 4*beta + j of P.V)
+      float z[8], sc[8];
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int beta = 0; beta < 2; ++beta)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int t = 16 * beta + 4 * grp + j;
+          const bool live = sl_lds[toff + t] >= 0;
+          const float tsc = sring[buf][t];
+          sc[4 * beta + j] = tsc;
+          const float sv = beta == 0 ? s0[j] : s1[j];
+          const float zz = live ? sv * tsc * scale2 : -INFINITY;
+          z[4 * beta + j] = zz;
+          tmax = fmaxf(tmax, zz);
+        }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      const bool first = m_run == -INFINITY && tmax > -INFINITY;
+      const bool need = tmax > m_run + 8.f && !first;
+      if (__any(need)) {
+        const float m_new = need ? tmax : m_run;
+        const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < kDBlocks; ++db) o[db] *= alpha;
+      }
+      m_run = first ? tmax : m_run;
+      bf16x8 pb;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float pe = z[e] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(z[e] - m_run);
+        l_run += pe;
+        pb[e] = (__bf16)(pe * sc[e]);
+      }
+      // ---- O^T += V^T . P^T over this wave's 256 output dims (pieces 16kh .. 16kh+15)
+#pragma unroll
+      for (int db = 0; db < kDBlocks; ++db) {
+        const u32x2 raw = __builtin_bit_cast(
+            u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)(T + v_base[db & 3] + 64 * (db >> 2))));
+        o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16x8(raw[0], raw[1]), pb, o[db], 0, 0, 0);
+      }
+    }
+  }
+
+  if (!active) return;
+  float l_tot = l_run + __shfl_xor(l_run, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  // lane holds O^T[d = 256kh + db*16 + grp*4 + j][head]
+  if (p.n_split == 1) {
+    float* dst = p.out + ((int64_t)r * p.H + head) * kVDim + kh * (kDBlocks * 16) + grp * 4;
+#pragma unroll
+    for (int db = 0; db < kDBlocks; ++db) *(f32x4*)(dst + db * 16) = o[db] * inv;
+    if (p.lse && grp == 0 && kh == 0)
+      p.lse[(int64_t)r * p.H + head] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+  } else {
+    const int64_t prow = ((int64_t)r * p.n_split + split) * p.H + head;
+    float* dst = p.part_o + prow * kVDim + kh * (kDBlocks * 16) + grp * 4;
+#pragma unroll
+    for (int db = 0; db < kDBlocks; ++db) *(f32x4*)(dst + db * 16) = o[db] * inv;
+    if (grp == 0 && kh == 0) {
+      p.part_m[prow] = l_tot > 0.f ? m_run * kLn2 : -INFINITY;
+      p.part_l[prow] = l_tot;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// fp8 rows, wide-tile variant (chunks of at most kChunkX selected rows): 4 waves, one per SIMD,
+// each with up to 512 registers, 64-token tiles.
+//   * Tiles are copied HBM -> LDS directly (36 copies of 1 KiB per tile, 9 per wave, whole rows
+//     per copy, through a buffer resource) into a ring of kRingX slots, kRingX-1 tiles in flight;
+//     layout as in mla_fp8_kernel (row t at t*576, piece p in slot p ^ fp8_swz(t)).
+//   * S^T and the online softmax: wave w owns the 16 heads 16w .. 16w+15 over all 64 tokens and
+//     the full K (q in registers); it publishes P (bf16, in the P.V operand layout) and the
+//     tile's per-head rescale factor through LDS.
+//   * P.V: wave w owns the output values 128w .. 128w+127 for all 64 heads, so each V^T operand
+//     is read from LDS and widened once and feeds the four head groups' MFMAs.
+//   * Two barriers per tile (tile landed; P published).  Loop-body LDS accesses go through
+//     restrict pointers (see the loop), copies through a buffer resource, so the compiler's
+//     waits for LDS reads stay partial and never cover the copies in flight.
+
+constexpr int kTX = 64;                                  // tokens per tile
+constexpr int kTXBytes = kTX * kRowDim;                  // 36864
+constexpr int kTXCopies = kTXBytes / 1024;               // 36
+constexpr int kRingX = 4;
+constexpr int kNTX = 256;                                // 4 waves
+constexpr int kChunkX = 1024;                            // selected rows staged per workgroup
+constexpr int kStepsX = kRowDim / 32;                    // 18 K steps of 32
+constexpr int kDBlocksW = kVDim / 16 / 4;                // 8 output blocks of 16 per wave
+
+// Shared memory of mla_fp8x_kernel.
+struct FXSmem {
+  uint8_t ring[kRingX][kTXBytes + kTX * 4];   // tile, then its 64 per-token scales
+  int32_t sl[kChunkX + kTX];                  // the chunk's slots, -1 padded
+  bf16x8 pex[4][2][64];                       // P^T operands: head group, K half, lane
+  float alpha[64];                            // per-head rescale of the running sums (this tile)
+  float fin_m[64], fin_l[64];                 // per-head running max and sum, after the last tile
+};
+
+__global__ __launch_bounds__(kNTX) void mla_fp8x_kernel(MlaParams p) {
+  __shared__ __attribute__((aligned(16))) FXSmem sm;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = blockIdx.y, split = blockIdx.x;
+  const int j0 = split * p.chunk;
+  const int j1 = min(p.k, j0 + p.chunk);
+  const int ntiles = j1 > j0 ? (j1 - j0 + kTX - 1) / kTX : 0;
+  const int32_t* sl = p.slots + (int64_t)r * p.k;
+  const int ngroups = min(4, p.H / 16);           // live head groups (H is a multiple of 16)
+  const bool s_active = wave < ngroups;           // this wave's S^T head group exists
+  const int m16 = lane & 15, grp = lane >> 4;
+
+  {
+    const int span = ntiles * kTX;
+    for (int e0 = 0; e0 < span; e0 += 4 * kNTX) {
+      int32_t v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = sl[min(j0 + e0 + u * kNTX + (int)threadIdx.x, p.k - 1)];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = e0 + u * kNTX + threadIdx.x;
+        if (e < span) sm.sl[e] = j0 + e < j1 ? v[u] : -1;
+      }
+    }
+  }
+  __syncthreads();
+
+  // Copies of tile v into ring slot `dst`: lane i of copy cc fills tile slot q = 64cc + i (token
+  // q/36, slot q%36); wave 0 also copies the 64 scales behind the tile.
+  const __amdgpu_buffer_rsrc_t kv_rs = rows_rsrc(p.kv, kRowDim, p.num_slots);
+  const __amdgpu_buffer_rsrc_t sc_rs = rows_rsrc(p.kv_scale, 4, p.num_slots);
+  auto issue = [&](const FXSmem* __restrict__ rd, uint8_t* __restrict__ dst, int v) {
+#pragma unroll
+    for (int c = 0; c < kTXCopies / 4; ++c) {
+      const int cc = wave * (kTXCopies / 4) + c;
+      const int q = cc * 64 + lane;
+      const int t = q / kFp8Pieces, sp = q - t * kFp8Pieces;
+      const int32_t sv = rd->sl[v * kTX + t];
+      lds_dma16_row(kv_rs, sv < 0 ? 0 : sv, (sp ^ fp8_swz(t)) << 4, dst + cc * 1024);
+    }
+    if (wave == 0) {
+      const int32_t ss = rd->sl[v * kTX + lane];
+      lds_dma4_row(sc_rs, ss < 0 ? 0 : ss, dst + kTXBytes);
+    }
+  };
+
+  // q fragments of this wave's S^T head group (head 16w + m16).  The K order of the S^T
+  // contraction is permuted so that one 16-byte LDS read serves two MFMA steps: step 2u + h
+  // gives lane group grp the dims 64u + 16grp + 8h .. +8 (the rows' operand follows suit).
+  bf16x8 qf[kStepsX];
+  if (s_active) {
+    const bf16x8* qrow = (const bf16x8*)((const __bf16*)p.q + ((int64_t)r * p.H + wave * 16 + m16) * kRowDim);
+#pragma unroll
+    for (int u = 0; u < kStepsX / 2; ++u)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) qf[2 * u + h] = qrow[8 * u + 2 * grp + h];
+  }
+#pragma unroll
+  for (int v = 0; v < kRingX - 1; ++v)
+    if (v < ntiles) issue(&sm, sm.ring[v], v);
+  if (!s_active) {   // head groups past the head count: P = 0, no rescale, for every tile
+    sm.pex[wave][0][lane] = bf16x8{};
+    sm.pex[wave][1][lane] = bf16x8{};
+    if (grp == 0) sm.alpha[wave * 16 + m16] = 1.f;
+  }
+
+  // P.V accumulators: head group g, output block 8w + db; lane holds O^T[d][head g*16 + m16]
+  f32x4 o[4][kDBlocksW];
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+#pragma unroll
+    for (int db = 0; db < kDBlocksW; ++db) o[g][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY;   // S^T head group: running max of z * log2(e), per head
+  float l_run = 0.f;         // this lane group's share of sum exp2(z - m_run)
+  const float scale2 = p.sm_scale * kLog2e;
+
+  // S^T operand of block beta (tokens 16beta + m16), steps 2u and 2u+1: logical piece
+  // 4u + grp, read whole; pieces 4 apart lie 64 bytes apart
+  int a_base[4];
+#pragma unroll
+  for (int beta = 0; beta < 4; ++beta) a_base[beta] = fp8_pos(16 * beta + m16, grp);
+  // V^T operand of output block 8w + db, K half kq: row e = m16/2 of the group's 8x16 block is
+  // token 32kq + tau(grp, e); pieces 4 apart lie 64 bytes apart
+  const int e_row = m16 >> 1;
+  const int tau = e_row < 4 ? 4 * grp + e_row : 16 + 4 * grp + (e_row - 4);
+  int v_base[2][4];
+#pragma unroll
+  for (int kq = 0; kq < 2; ++kq)
+#pragma unroll
+    for (int d4 = 0; d4 < 4; ++d4) v_base[kq][d4] = fp8_pos(32 * kq + tau, d4) + 8 * (m16 & 1) + 128 * wave;
+
+  // one tile: rd = shared memory as this iteration reads (and, for skipped rows, zeroes) it;
+  // dst = the ring slot that receives tile v + kRingX - 1
+  auto tile = [&](FXSmem* __restrict__ rd, uint8_t* __restrict__ dst, int v) {
+    if (v + kRingX - 1 < ntiles) issue(rd, dst, v + kRingX - 1);
+    uint8_t* T = rd->ring[v % kRingX];
+    const float* sc_t = (const float*)(T + kTXBytes);
+    const int toff = v * kTX;
+    // skipped tokens (past the chunk, or slot -1) read row 0: zero their rows (every wave reads
+    // the same slot list, so the choice is uniform over the workgroup)
+    if (__ballot(rd->sl[toff + lane] < 0)) {
+      for (int e = threadIdx.x; e < kTX * kFp8Pieces; e += kNTX) {
+        const int t = e / kFp8Pieces, pc = e - t * kFp8Pieces;
+        if (rd->sl[toff + t] < 0) *(u32x4*)(T + t * kRowDim + pc * 16) = u32x4{0u, 0u, 0u, 0u};
+      }
+      lds_barrier();
+    }
+
+    if (s_active) {
+      // ---- S^T for the 64 tokens (four blocks) x 16 heads, full K, operands read one step ahead
+      f32x4 sacc[4];
+#pragma unroll
+      for (int beta = 0; beta < 4; ++beta) sacc[beta] = f32x4{0.f, 0.f, 0.f, 0.f};
+      {
+        // operands of double step u+1 are requested before double step u is computed
+        u32x4 a[2][4];
+#pragma unroll
+        for (int beta = 0; beta < 4; ++beta) a[0][beta] = *(const u32x4*)(T + a_base[beta]);
+#pragma unroll
+        for (int u = 0; u < kStepsX / 2; ++u) {
+          if (u + 1 < kStepsX / 2) {
+#pragma unroll
+            for (int beta = 0; beta < 4; ++beta) a[(u + 1) & 1][beta] = *(const u32x4*)(T + a_base[beta] + 64 * (u + 1));
+          }
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int beta = 0; beta < 4; ++beta)
+              sacc[beta] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  fp8x8_to_bf16x8(a[u & 1][beta][2 * h], a[u & 1][beta][2 * h + 1]), qf[2 * u + h], sacc[beta], 0, 0,
+                  0);
+        }
+      }
+      // ---- online softmax; lane holds head 16w + m16, tokens 16beta + 4grp + j
+      float z[16], sc[16];
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int beta = 0; beta < 4; ++beta) {
+        const int t0 = 16 * beta + 4 * grp;
+        const f32x4 sc4 = *(const f32x4*)(sc_t + t0);
+        const int32_t* slt = rd->sl + toff + t0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          sc[4 * beta + j] = sc4[j];
+          const float zz = slt[j] >= 0 ? sacc[beta][j] * sc4[j] * scale2 : -INFINITY;
+          z[4 * beta + j] = zz;
+          tmax = fmaxf(tmax, zz);
+        }
+      }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      const bool first = m_run == -INFINITY && tmax > -INFINITY;
+      const bool need = tmax > m_run + 8.f && !first;
+      float alpha = 1.f;
+      if (need) {
+        alpha = __builtin_amdgcn_exp2f(m_run - tmax);
+        m_run = tmax;
+        l_run *= alpha;
+      }
+      m_run = first ? tmax : m_run;
+      // P^T operand of K half kq: tokens 32kq + tau(grp, e) = blocks 2kq, 2kq+1, rows 4grp + j
+#pragma unroll
+      for (int kq = 0; kq < 2; ++kq) {
+        bf16x8 pb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float ze = z[8 * kq + e];
+          const float pe = ze == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ze - m_run);
+          l_run += pe;
+          pb[e] = (__bf16)(pe * sc[8 * kq + e]);
+        }
+        rd->pex[wave][kq][lane] = pb;
+      }
+      if (grp == 0) rd->alpha[wave * 16 + m16] = alpha;
+    }
+    lds_barrier();   // P and the rescale factors of every head group are published
+
+    // ---- O^T += V^T . P^T over this wave's 128 output values, all four head groups (a group
+    // past the head count has P = 0 and is never written out).  All V^T operands of the tile
+    // are requested first, so their latency overlaps the rescale check and the P reads.
+    u32x2 raw[kDBlocksW][2];
+#pragma unroll
+    for (int db = 0; db < kDBlocksW; ++db)
+#pragma unroll
+      for (int kq = 0; kq < 2; ++kq)
+        raw[db][kq] = __builtin_bit_cast(
+            u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                       (__attribute__((address_space(3))) i32x2*)(T + v_base[kq][db & 3] + 64 * (db >> 2))));
+    bf16x8 pg[4][2];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      pg[g][0] = rd->pex[g][0][lane];
+      pg[g][1] = rd->pex[g][1][lane];
+      const float al = rd->alpha[g * 16 + m16];
+      if (__any(al != 1.f)) {
+#pragma unroll
+        for (int db = 0; db < kDBlocksW; ++db) o[g][db] *= al;
+      }
+    }
+#pragma unroll
+    for (int db = 0; db < kDBlocksW; ++db) {
+#pragma unroll
+      for (int kq = 0; kq < 2; ++kq) {
+        const bf16x8 av = fp8x8_to_bf16x8(raw[db][kq][0], raw[db][kq][1]);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) o[g][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pg[g][kq], o[g][db], 0, 0, 0);
+      }
+    }
+  };
+
+  for (int v = 0; v < ntiles; ++v) {
+    const int later = min(kRingX - 2, ntiles - 1 - v);
+    if (wave == 0) {
+      if (later >= 2) wait_vmcnt<2 * (kTXCopies / 4 + 1)>();
+      else if (later == 1) wait_vmcnt<kTXCopies / 4 + 1>();
+      else wait_vmcnt<0>();
+    } else {
+      if (later >= 2) wait_vmcnt<2 * (kTXCopies / 4)>();
+      else if (later == 1) wait_vmcnt<kTXCopies / 4>();
+      else wait_vmcnt<0>();
+    }
+    lds_barrier();   // tile v landed for every wave; ring slot (v-1) % kRingX and P are no longer read
+    tile(&sm, sm.ring[(v + kRingX - 1) % kRingX], v);
+  }
+
+  // ---- final running max and sum per head, then each wave writes its 128 output values
+  if (s_active) {
+    float l_tot = l_run + __shfl_xor(l_run, 16);
+    l_tot += __shfl_xor(l_tot, 32);
+    if (grp == 0) {
+      sm.fin_m[wave * 16 + m16] = m_run;
+      sm.fin_l[wave * 16 + m16] = l_tot;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    if (g >= ngroups) break;
+    const int head = g * 16 + m16;
+    const float mh = sm.fin_m[head], lh = sm.fin_l[head];
+    const float inv = lh > 0.f ? 1.f / lh : 0.f;
+    // lane holds O^T[d = 128w + db*16 + grp*4 + j][head]
+    float* dst;
+    if (p.n_split == 1) {
+      dst = p.out + ((int64_t)r * p.H + head) * kVDim + wave * 128 + grp * 4;
+      if (p.lse && wave == 0 && grp == 0)
+        p.lse[(int64_t)r * p.H + head] = lh > 0.f ? (mh + log2f(lh)) * kLn2 : -INFINITY;
+    } else {
+      const int64_t prow = ((int64_t)r * p.n_split + split) * p.H + head;
+      dst = p.part_o + prow * kVDim + wave * 128 + grp * 4;
+      if (wave == 0 && grp == 0) {
+        p.part_m[prow] = lh > 0.f ? mh * kLn2 : -INFINITY;
+        p.part_l[prow] = lh;
+      }
+    }
+#pragma unroll
+    for (int db = 0; db < kDBlocksW; ++db) *(f32x4*)(dst + db * 16) = o[g][db] * inv;
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
 // split-k merge.  One 128-thread workgroup per (row, head, 128-value quarter of the output).
 // Thread (g, q) merges chunks j = g, g+4, g+8, ... for output values 4q..4q+3 of the quarter: it
 // issues the loads of m_j, l_j and o_j for up to 8 chunks at once, keeps a running
@@ -465,10 +1010,13 @@ __global__ __launch_bounds__(128) void mla_combine_kernel(CombineParams p) {
 
 int mla_default_split(int rows, int H, int k) {
   (void)H;
-  // about one workgroup per compute unit, at least 64 selected rows per chunk
+  // about one workgroup per compute unit, at least 64 selected rows per chunk, and at most
+  // kChunkX (the wide fp8 kernel's staging limit)
   int ns = 256 / (rows > 0 ? rows : 1);
   const int max_ns = (k + 63) / 64;
   if (ns > max_ns) ns = max_ns;
+  const int min_ns = (k + kChunkX - 1) / kChunkX;
+  if (ns < min_ns) ns = min_ns;
   if (ns < 1) ns = 1;
   return ns;
 }
@@ -488,7 +1036,10 @@ hipError_t launch_mla(const MlaParams& p0, dsa_dtype_t q_dtype, dsa_dtype_t kv_d
   chunk = (chunk + kTT - 1) / kTT * kTT;
   p.chunk = chunk;
   const dim3 grid((unsigned)p.n_split, (unsigned)p.rows);
-  if (kv_dtype == DSA_FP8_E4M3FN) hipLaunchKernelGGL(mla_mfma_kernel<true>, grid, dim3(kNT), 0, s, p);
+  if (kv_dtype == DSA_FP8_E4M3FN) {
+    if (chunk <= kChunkX) hipLaunchKernelGGL(mla_fp8x_kernel, grid, dim3(kNTX), 0, s, p);
+    else hipLaunchKernelGGL(mla_fp8_kernel, grid, dim3(kNT), 0, s, p);
+  }
   else hipLaunchKernelGGL(mla_mfma_kernel<false>, grid, dim3(kNT), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_split == 1) return e;
