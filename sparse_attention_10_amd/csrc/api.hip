@@ -234,6 +234,7 @@ dsa_status_t dsa_indexer_scores(const dsa_batch_t* b, const void* q, dsa_dtype_t
   p.w = w;
   p.k_cache = k_cache;
   p.k_scale = k_dtype == DSA_FP8_E4M3FN ? k_scale : nullptr;
+  p.num_slots = b->num_slots;
   p.scores = scores;
   p.ld = scores_ld;
   p.B = b->batch;
@@ -389,6 +390,7 @@ dsa_status_t dsa_decode_step(const dsa_decode_step_args_t* a, void* workspace, s
   ip.w = a->w;
   ip.k_cache = a->k_cache;
   ip.k_scale = a->k_dtype == DSA_FP8_E4M3FN ? a->k_scale : nullptr;
+  ip.num_slots = b->num_slots;
   ip.scores = scores;
   ip.ld = w.ld;
   ip.B = b->batch;

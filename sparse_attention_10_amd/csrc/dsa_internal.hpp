@@ -106,6 +106,7 @@ struct IndexerParams {
   const float* k_scale;
   float* scores;
   int64_t ld;
+  int64_t num_slots;      // rows of k_cache (and k_scale)
   int32_t B, Q, max_seq_len, P, maxP;
   int32_t Hi, Di;
   int32_t tiles_per_wg;   // matrix-core path: 128-token tiles per workgroup

@@ -74,13 +74,16 @@ __global__ __launch_bounds__(256) void indexer_valu_kernel(IndexerParams p) {
 // matrix-core path: Hi = 64, Di = 128, QB = 1 or 2 query rows per workgroup
 //
 // 8 waves (two per SIMD) stream the keys of one token range through an LDS ring of NB stages.
-// A stage holds ST = 32 * 8 / QB tokens; it is filled by direct-to-LDS loads in which
-// consecutive lanes fetch consecutive 16-byte pieces of key rows, so each load instruction moves
-// 1 KB in few cache lines, and piece p of row r is stored at slot p ^ swz(r) of its LDS row so
-// that the MFMA operand reads are free of bank conflicts.  Every key is read from memory once
-// per workgroup: with QB = 2 the waves 0-3 score row 0 and the waves 4-7 row 1 on the same
-// 32-token sub-tiles.  One barrier per stage: after it the stage has landed for every wave and
-// the stage read before it is free to be refilled.
+// A stage holds ST = 32 * 8 / QB tokens; it is filled by direct-to-LDS copies (through a
+// buffer resource over the key rows) in which consecutive lanes fetch consecutive 16-byte
+// pieces of key rows, so each copy moves 1 KB in few cache lines, and piece p of row r is
+// stored at slot p ^ swz(r) of its LDS row so that the MFMA operand reads are free of bank
+// conflicts.  Every key is read from memory once per workgroup: with QB = 2 the waves 0-3 score
+// row 0 and the waves 4-7 row 1 on the same 32-token sub-tiles.  One barrier per stage (waiting
+// only for LDS operations): after it the stage has landed for every wave and the stage read
+// before it is free to be refilled.  The loop body reads LDS only through a restrict pointer
+// and writes it only through another (the copies), so the compiler's waits for its LDS reads
+// never cover the copies in flight.
 
 constexpr int kHi = 64, kDi = 128;
 constexpr int kSub = 32;                  // tokens per sub-tile (the MFMA N)
@@ -105,22 +108,28 @@ struct Geo {
 template <bool FP8>
 __device__ __forceinline__ int swz(int r) { return FP8 ? ((r >> 1) & 7) : (r & 15); }
 
+// Shared memory of indexer_mfma_kernel: ring stage = keys, then (fp8) their per-token scales.
+template <bool FP8, int QB>
+struct ISmem {
+  uint8_t ring[Geo<FP8, QB>::NB][Geo<FP8, QB>::SB + (FP8 ? Geo<FP8, QB>::ST * 4 : 0)];
+  __bf16 q[QB][kHi][kDi];
+  float w[QB][kHi];
+  int32_t pt[kMaxWgPages];
+};
+
 
 // CONTIG (32 divides P): a sub-tile's 32 tokens are one 32-aligned run inside one page, so its
 // key rows are contiguous in the cache and one page lookup per sub-tile gives every address.
 template <bool FP8, bool CONTIG, int QB>
 __global__ __launch_bounds__(kThreadsI) void indexer_mfma_kernel(IndexerParams p) {
   using G = Geo<FP8, QB>;
+  using Smem = ISmem<FP8, QB>;
   constexpr int NB = G::NB;
   static_assert(NB >= 2 && NB <= 4, "ring depth");
-  __shared__ __attribute__((aligned(16))) uint8_t ring[NB][G::SB];
-  __shared__ __attribute__((aligned(16))) float sring[FP8 ? NB : 1][FP8 ? G::ST : 1];   // fp8 token scales
-  __shared__ __attribute__((aligned(16))) __bf16 q_lds[QB][kHi][kDi];
-  __shared__ __attribute__((aligned(16))) float w_lds[QB][kHi];
-  __shared__ int32_t pt_lds[kMaxWgPages];
+  __shared__ __attribute__((aligned(16))) Smem sm;
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // One workgroup = QB query rows x one range of p.tiles_per_wg tiles.  The grid is ordered so
   // that the Q/QB row groups of one key range get ids 8 apart (ids go to the 8 XCDs round-robin):
   // they run on one XCD, close together, and the groups after the first read the keys from its
@@ -147,47 +156,47 @@ __global__ __launch_bounds__(kThreadsI) void indexer_mfma_kernel(IndexerParams p
   const int page0 = tile_base / p.P;
   const int npg = (t_stop > tile_base) ? (t_stop - 1) / p.P - page0 + 1 : 0;
   const int32_t* ptab_g = p.page_table + (int64_t)b * p.maxP;
-  const uint8_t* kc = (const uint8_t*)p.k_cache;
+  const __amdgpu_buffer_rsrc_t k_rs = rows_rsrc(p.k_cache, G::RB, p.num_slots);
+  const __amdgpu_buffer_rsrc_t s_rs = rows_rsrc(FP8 ? (const void*)p.k_scale : p.k_cache, 4, FP8 ? p.num_slots : 0);
 
   // Stage v covers tokens tile_base + v*ST ..; this thread's load c fills LDS bytes
   // [off, off+16) of the stage, off = ((c*8 + wave)*64 + lane)*16: row r = off / RB and slot
   // off % RB / 16, fetched from piece (slot ^ swz(r)) of that token's key row.
-  int lane_off[G::ND];     // byte offset inside the (contiguous) 32-token sub-tile
-  int lane_row[G::ND];
+  int lane_row[G::ND];     // stage row of this lane's piece in copy c
+  int lane_boff[G::ND];    // byte offset of that piece inside its key row
 #pragma unroll
   for (int c = 0; c < G::ND; ++c) {
     const int off = ((c * kWaves + wave) * 64 + lane) * 16;
     const int r = off / G::RB, q = (off % G::RB) / 16;
     lane_row[c] = r;
-    lane_off[c] = (r & (kSub - 1)) * G::RB + 16 * (q ^ swz<FP8>(r));
+    lane_boff[c] = 16 * (q ^ swz<FP8>(r));
   }
   const bool scale_wave = FP8 && wave < G::NSW;
-  auto issue = [&](int v, auto&& slot_of) {
+  // copies of stage v into ring stage `dst` (keys, then the scales behind them)
+  auto issue = [&](uint8_t* __restrict__ dst, int v, auto&& slot_of) {
     const int t0 = tile_base + v * G::ST;
-    uint8_t* stg = &ring[v % NB][0];
 #pragma unroll
     for (int c = 0; c < G::ND; ++c) {
       const int r = lane_row[c];
-      const int off = ((c * kWaves + wave) * 64) * 16;     // this load's 1-KB block of the stage
+      const int off = ((c * kWaves + wave) * 64) * 16;     // this copy's 1-KB block of the stage
       if constexpr (CONTIG) {
         // the 1-KB block lies in one sub-tile: rows t0 + (r & ~31) .. +31 are contiguous
         // (the run never leaves its page, so rows past the sequence are still allocated cache
         // rows; their scores are never written)
         const int ts = t0 + (r & ~(kSub - 1));
         const int64_t slot0 = ts < t_stop ? slot_of(ts) : 0;
-        lds_dma16(kc + slot0 * G::RB + lane_off[c], stg + off);
+        lds_dma16_row(k_rs, (int)slot0 + (r & (kSub - 1)), lane_boff[c], dst + off);
       } else {
         const int t = t0 + r;
-        const int q = (((c * kWaves + wave) * 64 + lane) * 16 % G::RB) / 16;
         const int64_t slot = t < t_stop ? slot_of(t) : 0;   // row 0 (valid) for unscored tokens
-        lds_dma16(kc + slot * G::RB + 16 * (q ^ swz<FP8>(r)), stg + off);
+        lds_dma16_row(k_rs, (int)slot, lane_boff[c], dst + off);
       }
     }
     if constexpr (FP8) {
       if (scale_wave) {
         const int t = t0 + wave * 64 + lane;
         const int64_t slot = t < t_stop ? slot_of(t) : 0;
-        lds_dma4(p.k_scale + slot, &sring[v % NB][wave * 64]);
+        lds_dma4_row(s_rs, (int)slot, dst + G::SB + wave * 256);
       }
     }
   };
@@ -196,13 +205,13 @@ __global__ __launch_bounds__(kThreadsI) void indexer_mfma_kernel(IndexerParams p
   auto slot_global = [&](int t) { return (int64_t)ptab_g[t / p.P] * p.P + t % p.P; };
 #pragma unroll
   for (int v = 0; v < NB - 1; ++v)
-    if (v < nstage) issue(v, slot_global);
+    if (v < nstage) issue(sm.ring[v], v, slot_global);
 
   // stage q (bf16), w and the page-table entries of this workgroup's tokens
   {
     const int64_t row0 = (int64_t)b * p.Q + qb0;
     const u32x4* qsrc = (const u32x4*)((const __bf16*)p.q + row0 * kHi * kDi);
-    u32x4* qdst = (u32x4*)&q_lds[0][0][0];
+    u32x4* qdst = (u32x4*)&sm.q[0][0][0];
     constexpr int kPer = QB * kHi * kDi / 8 / kThreadsI;
     u32x4 qv[kPer];
 #pragma unroll
@@ -215,10 +224,10 @@ __global__ __launch_bounds__(kThreadsI) void indexer_mfma_kernel(IndexerParams p
       pv[c] = c * kThreadsI < npg ? ptab_g[page0 + min(c * kThreadsI + (int)threadIdx.x, npg - 1)] : 0;
 #pragma unroll
     for (int c = 0; c < kPer; ++c) qdst[c * kThreadsI + threadIdx.x] = qv[c];
-    if (threadIdx.x < QB * kHi) (&w_lds[0][0])[threadIdx.x] = wv;
+    if (threadIdx.x < QB * kHi) (&sm.w[0][0])[threadIdx.x] = wv;
 #pragma unroll
     for (int c = 0; c < kPtPer; ++c)
-      if (c * kThreadsI + (int)threadIdx.x < npg) pt_lds[c * kThreadsI + threadIdx.x] = pv[c];
+      if (c * kThreadsI + (int)threadIdx.x < npg) sm.pt[c * kThreadsI + threadIdx.x] = pv[c];
   }
   __syncthreads();
 
@@ -229,33 +238,37 @@ __global__ __launch_bounds__(kThreadsI) void indexer_mfma_kernel(IndexerParams p
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
     for (int s = 0; s < 8; ++s)
-      afrag[mb][s] = *(const bf16x8*)&q_lds[ri][mb * 32 + n_in_sub][half * 64 + s * 8];
+      afrag[mb][s] = *(const bf16x8*)&sm.q[ri][mb * 32 + n_in_sub][half * 64 + s * 8];
   float wr[2][4][4];   // head weights of the heads this lane holds: m = mb*32 + g*8 + half*4 + j
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const f32x4 wv = *(const f32x4*)&w_lds[ri][mb * 32 + g * 8 + half * 4];
+      const f32x4 wv = *(const f32x4*)&sm.w[ri][mb * 32 + g * 8 + half * 4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) wr[mb][g][j] = wv[j];
     }
 
   const int P = p.P;
-  auto slot_lds = [&](int t) {
-    const int pg = p.p_shift >= 0 ? t >> p.p_shift : t / P;   // (uniform: power-of-two pages shift)
-    return (int64_t)pt_lds[pg - page0] * P + (t - pg * P);
-  };
-  float* dst = p.scores + ((int64_t)b * p.Q + qb0 + ri) * p.ld;
+  float* out = p.scores + ((int64_t)b * p.Q + qb0 + ri) * p.ld;
 
-  // this wave's sub-tile of stage v: B fragments (lane: token n, half h) from LDS, 32x32x16
-  // MFMAs over the two 32-head M-blocks, then ReLU, head weights and the head sum
-  auto compute = [&](int v) {
+  // one stage: request stage v + NB - 1 into ring stage `dst` (page-table entries read through
+  // rd), then this wave's sub-tile of stage v: B fragments (lane: token n, half h) from LDS,
+  // 32x32x16 MFMAs over the two 32-head M-blocks, then ReLU, head weights and the head sum
+  auto stage = [&](const Smem* __restrict__ rd, uint8_t* __restrict__ dst, int v) {
+    if (v + NB - 1 < nstage) {
+      auto slot_lds = [&](int t) {
+        const int pg = p.p_shift >= 0 ? t >> p.p_shift : t / P;   // (uniform: power-of-two pages shift)
+        return (int64_t)rd->pt[pg - page0] * P + (t - pg * P);
+      };
+      issue(dst, v + NB - 1, slot_lds);
+    }
     const int t = tile_base + v * G::ST + si * kSub + n_in_sub;
     if (tile_base + v * G::ST + si * kSub > pos) {   // (uniform) the whole sub-tile is unseen
-      if (half == 0 && t < tile_end) dst[t] = -INFINITY;
+      if (half == 0 && t < tile_end) out[t] = -INFINITY;
       return;
     }
-    const uint8_t* rows = &ring[v % NB][si * kSub * G::RB];
+    const uint8_t* rows = &rd->ring[v % NB][si * kSub * G::RB];
     bf16x8 kf[8];
     if constexpr (FP8) {
 #pragma unroll
@@ -291,8 +304,8 @@ __global__ __launch_bounds__(kThreadsI) void indexer_mfma_kernel(IndexerParams p
           part = fmaf(wr[mb][g][jj], __int_as_float(max(__float_as_int(acc[mb][4 * g + jj]), 0)), part);
     part += __shfl_xor(part, 32);
     if (half == 0 && t < tile_end) {
-      const float kscale = FP8 ? sring[FP8 ? v % NB : 0][FP8 ? si * kSub + n_in_sub : 0] : 1.f;
-      dst[t] = t <= pos ? part * kscale : -INFINITY;
+      const float kscale = FP8 ? ((const float*)(&rd->ring[v % NB][G::SB]))[si * kSub + n_in_sub] : 1.f;
+      out[t] = t <= pos ? part * kscale : -INFINITY;
     }
   };
 
@@ -310,9 +323,8 @@ __global__ __launch_bounds__(kThreadsI) void indexer_mfma_kernel(IndexerParams p
       else if (later == 1) wait_vmcnt<G::ND>();
       else wait_vmcnt<0>();
     }
-    __syncthreads();   // stage v landed for every wave; stage v-1 is no longer read
-    if (v + NB - 1 < nstage) issue(v + NB - 1, slot_lds);
-    compute(v);
+    lds_barrier();   // stage v landed for every wave; stage v-1 is no longer read
+    stage(&sm, sm.ring[(v + NB - 1) % NB], v);
   }
   // tokens of [tile_base, tile_end) past the block's last position: -inf (their stages are not
   // computed)
