@@ -394,7 +394,10 @@ def main():
         v["us"] = round(v["us"], 3)
     # the dominant kernel: the stage with the largest average launch time
     dom = max(stage_info, key=lambda s: stage_info[s]["us"])
-    kern = {"indexer": "indexer_mfma_kernel", "mla": "mla_mfma_kernel", "topk": "topk_kernel",
+    # fp8 rows run on the wide-tile kernel when a split chunk holds at most 1024 rows
+    mla_kern = ("mla_mfma_kernel" if cfg.kv_dtype != "fp8" else
+                "mla_fp8x_kernel" if -(-(-(-k // ns)) // 32) * 32 <= 1024 else "mla_fp8_kernel")
+    kern = {"indexer": "indexer_mfma_kernel", "mla": mla_kern, "topk": "topk_kernel",
             "combine": "mla_combine_kernel"}[dom]
     if cfg.name == "c4" and dom in ("indexer", "mla"):
         ach = stage_info[dom]["flops"] / (stage_info[dom]["us"] * 1e-6) / 1e12
