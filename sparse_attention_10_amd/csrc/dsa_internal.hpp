@@ -84,6 +84,18 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Wait until at most later*PER vector-memory operations are outstanding, later in 0..MAXL
+// (a runtime count, resolved into immediate waits).
+template <int PER, int MAXL>
+__device__ __forceinline__ void wait_vmcnt_later(int later) {
+  if constexpr (MAXL <= 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (later >= MAXL) wait_vmcnt<MAXL * PER>();
+    else wait_vmcnt_later<PER, MAXL - 1>(later);
+  }
+}
+
 // Workgroup barrier for rings filled by direct-to-LDS copies.  It waits only for this wave's
 // LDS operations (lgkmcnt 0), not for vector-memory operations in flight, which the caller
 // bounds with wait_vmcnt beforehand: a __syncthreads also orders global memory, which here
@@ -110,7 +122,7 @@ struct IndexerParams {
   int32_t B, Q, max_seq_len, P, maxP;
   int32_t Hi, Di;
   int32_t tiles_per_wg;   // matrix-core path: 128-token tiles per workgroup
-  int32_t groups_padded;  // matrix-core path: tile groups per sequence, rounded up to 8
+  int32_t groups;         // matrix-core path: key ranges (workgroups per row group) per sequence
   int32_t p_shift;        // log2(P) when the page size is a power of two, else -1
 };
 

@@ -91,18 +91,21 @@ constexpr int kWaves = 8;
 constexpr int kThreadsI = 64 * kWaves;
 constexpr int kTile = 256;                // grid granularity: tokens per tile
 constexpr int kMaxTpwAny = 8;             // tiles per workgroup, any page size
-constexpr int kMaxTpwContig = 64;         // tiles per workgroup when 32 | P (pages of >= 32 tokens)
+constexpr int kMaxTpwContig = 128;        // tiles per workgroup when 32 | P (pages of >= 32 tokens)
 constexpr int kMaxWgPages = kMaxTpwAny * kTile + 1;   // page-table entries a workgroup can span
 static_assert(kMaxTpwContig * kTile / 32 + 1 <= kMaxWgPages, "page-table staging covers both layouts");
 
 template <bool FP8, int QB>
 struct Geo {
   static constexpr int RB = FP8 ? kDi : 2 * kDi;       // key row bytes
-  static constexpr int SPS = kWaves / QB;              // sub-tiles per stage
-  static constexpr int ST = kSub * SPS;                // tokens per stage
+  static constexpr int WPR = kWaves / QB;              // waves per query row
+  // sub-tiles per wave and stage: two for fp8 keys and two rows, so that a stage (and the
+  // barrier that closes it) covers 256 tokens as in the other layouts
+  static constexpr int SPW = (FP8 && QB == 2) ? 2 : 1;
+  static constexpr int ST = kSub * WPR * SPW;          // tokens per stage
   static constexpr int SB = ST * RB;                   // stage bytes
   static constexpr int ND = SB / (kThreadsI * 16);     // 16-byte loads per thread per stage
-  static constexpr int NB = FP8 ? (QB == 2 ? 4 : 3) : (QB == 2 ? 3 : 2);   // ring depth (<= 128 KB)
+  static constexpr int NB = FP8 ? 3 : (QB == 2 ? 3 : 2);   // ring depth (stages of 32 / 64 KB)
   static constexpr int NSW = FP8 ? ST / 64 : 0;        // waves that also load the stage's scales
 };
 template <bool FP8>
@@ -125,21 +128,24 @@ __global__ __launch_bounds__(kThreadsI) void indexer_mfma_kernel(IndexerParams p
   using G = Geo<FP8, QB>;
   using Smem = ISmem<FP8, QB>;
   constexpr int NB = G::NB;
-  static_assert(NB >= 2 && NB <= 4, "ring depth");
+  static_assert(NB >= 2 && (NB - 2) * (G::ND + 1) < 64, "ring depth");
   __shared__ __attribute__((aligned(16))) Smem sm;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // One workgroup = QB query rows x one range of p.tiles_per_wg tiles.  The grid is ordered so
-  // that the Q/QB row groups of one key range get ids 8 apart (ids go to the 8 XCDs round-robin):
+  // One workgroup = QB query rows x one key range (p.tiles_per_wg tiles of one sequence).  Key
+  // ranges are numbered over all sequences, kr = b * groups + g, and the grid is ordered so that
+  // the Q/QB row groups of one key range get ids 8 apart (ids go to the 8 XCDs round-robin):
   // they run on one XCD, close together, and the groups after the first read the keys from its
-  // L2.   id = b*(Gp*NQ) + 8NQ*m + 8*i + j  ->  row group i, key range g = 8m + j
+  // L2.   id = 8NQ*m + 8*i + j  ->  row group i, key range kr = 8m + j
   const int nq = p.Q / QB;
-  const int per_b = p.groups_padded * nq;
-  const int b = (int)blockIdx.x / per_b;
-  const int local = (int)blockIdx.x - b * per_b;
-  const int qb0 = ((local >> 3) % nq) * QB;           // first query row of the block
-  const int grp_id = 8 * (local / (8 * nq)) + (local & 7);
+  const int blk = (int)blockIdx.x / (8 * nq);
+  const int rem = (int)blockIdx.x - blk * 8 * nq;
+  const int kr = 8 * blk + (rem & 7);
+  if (kr >= p.B * p.groups) return;           // grid padding (uniform)
+  const int b = kr / p.groups;
+  const int grp_id = kr - b * p.groups;
+  const int qb0 = (rem >> 3) * QB;            // first query row of the block
   const int L = min(p.seq_lens[b], p.max_seq_len);
   const int tile_base = grp_id * p.tiles_per_wg * kTile;
   if (tile_base >= L) return;                 // uniform early exit
@@ -148,8 +154,8 @@ __global__ __launch_bounds__(kThreadsI) void indexer_mfma_kernel(IndexerParams p
   const int t_stop = min(tile_end, pos_last + 1);  // tokens at or past this are never scored
   const int nstage = t_stop > tile_base ? (t_stop - tile_base + G::ST - 1) / G::ST : 0;
 
-  const int ri = wave / G::SPS;               // the row this wave scores
-  const int si = wave - ri * G::SPS;          // its sub-tile within a stage
+  const int ri = wave / G::WPR;               // the row this wave scores
+  const int si = wave - ri * G::WPR;          // its first sub-tile within a stage is si * SPW
   const int pos = L - p.Q + qb0 + ri;         // that row sees tokens t <= pos
   const int n_in_sub = lane & 31;
   const int half = lane >> 5;
@@ -172,32 +178,40 @@ __global__ __launch_bounds__(kThreadsI) void indexer_mfma_kernel(IndexerParams p
     lane_boff[c] = 16 * (q ^ swz<FP8>(r));
   }
   const bool scale_wave = FP8 && wave < G::NSW;
-  // copies of stage v into ring stage `dst` (keys, then the scales behind them)
-  auto issue = [&](uint8_t* __restrict__ dst, int v, auto&& slot_of) {
+  // Cache rows of this lane's copies of one stage: copy c fetches row slot[c] (CONTIG: the first
+  // row of the copy's 32-token run, which the lane offsets by r % 32), the scale copy row sslot.
+  struct Rows {
+    int32_t slot[G::ND];
+    int32_t sslot;
+  };
+  auto rows_of = [&](int v, auto&& slot_of) {
+    Rows rw;
     const int t0 = tile_base + v * G::ST;
 #pragma unroll
     for (int c = 0; c < G::ND; ++c) {
-      const int r = lane_row[c];
+      // CONTIG: the run t0 + (r & ~31) .. +31 lies in one page; rows past the sequence are
+      // still allocated cache rows (their scores are never written).  Tokens at or past t_stop
+      // read row 0 (valid) and are never scored.
+      const int t = CONTIG ? t0 + (lane_row[c] & ~(kSub - 1)) : t0 + lane_row[c];
+      rw.slot[c] = t < t_stop ? (int32_t)slot_of(t) : 0;
+    }
+    rw.sslot = 0;
+    if constexpr (FP8) {
+      const int t = t0 + wave * 64 + lane;
+      rw.sslot = scale_wave && t < t_stop ? (int32_t)slot_of(t) : 0;
+    }
+    return rw;
+  };
+  // copies of one stage into ring stage `dst` (keys, then the scales behind them)
+  auto issue = [&](uint8_t* __restrict__ dst, const Rows& rw) {
+#pragma unroll
+    for (int c = 0; c < G::ND; ++c) {
       const int off = ((c * kWaves + wave) * 64) * 16;     // this copy's 1-KB block of the stage
-      if constexpr (CONTIG) {
-        // the 1-KB block lies in one sub-tile: rows t0 + (r & ~31) .. +31 are contiguous
-        // (the run never leaves its page, so rows past the sequence are still allocated cache
-        // rows; their scores are never written)
-        const int ts = t0 + (r & ~(kSub - 1));
-        const int64_t slot0 = ts < t_stop ? slot_of(ts) : 0;
-        lds_dma16_row(k_rs, (int)slot0 + (r & (kSub - 1)), lane_boff[c], dst + off);
-      } else {
-        const int t = t0 + r;
-        const int64_t slot = t < t_stop ? slot_of(t) : 0;   // row 0 (valid) for unscored tokens
-        lds_dma16_row(k_rs, (int)slot, lane_boff[c], dst + off);
-      }
+      const int row = CONTIG ? (int)rw.slot[c] + (lane_row[c] & (kSub - 1)) : (int)rw.slot[c];
+      lds_dma16_row(k_rs, row, lane_boff[c], dst + off);
     }
     if constexpr (FP8) {
-      if (scale_wave) {
-        const int t = t0 + wave * 64 + lane;
-        const int64_t slot = t < t_stop ? slot_of(t) : 0;
-        lds_dma4_row(s_rs, (int)slot, dst + G::SB + wave * 256);
-      }
+      if (scale_wave) lds_dma4_row(s_rs, (int)rw.sslot, dst + G::SB + wave * 256);
     }
   };
   // the first NB-1 stages are requested before q is staged, from page-table entries read
@@ -205,7 +219,7 @@ __global__ __launch_bounds__(kThreadsI) void indexer_mfma_kernel(IndexerParams p
   auto slot_global = [&](int t) { return (int64_t)ptab_g[t / p.P] * p.P + t % p.P; };
 #pragma unroll
   for (int v = 0; v < NB - 1; ++v)
-    if (v < nstage) issue(sm.ring[v], v, slot_global);
+    if (v < nstage) issue(sm.ring[v], rows_of(v, slot_global));
 
   // stage q (bf16), w and the page-table entries of this workgroup's tokens
   {
@@ -251,49 +265,54 @@ __global__ __launch_bounds__(kThreadsI) void indexer_mfma_kernel(IndexerParams p
 
   const int P = p.P;
   float* out = p.scores + ((int64_t)b * p.Q + qb0 + ri) * p.ld;
-
-  // one stage: request stage v + NB - 1 into ring stage `dst` (page-table entries read through
-  // rd), then this wave's sub-tile of stage v: B fragments (lane: token n, half h) from LDS,
-  // 32x32x16 MFMAs over the two 32-head M-blocks, then ReLU, head weights and the head sum
-  auto stage = [&](const Smem* __restrict__ rd, uint8_t* __restrict__ dst, int v) {
-    if (v + NB - 1 < nstage) {
-      auto slot_lds = [&](int t) {
-        const int pg = p.p_shift >= 0 ? t >> p.p_shift : t / P;   // (uniform: power-of-two pages shift)
-        return (int64_t)rd->pt[pg - page0] * P + (t - pg * P);
-      };
-      issue(dst, v + NB - 1, slot_lds);
-    }
-    const int t = tile_base + v * G::ST + si * kSub + n_in_sub;
-    if (tile_base + v * G::ST + si * kSub > pos) {   // (uniform) the whole sub-tile is unseen
-      if (half == 0 && t < tile_end) out[t] = -INFINITY;
-      return;
-    }
-    const uint8_t* rows = &rd->ring[v % NB][si * kSub * G::RB];
-    bf16x8 kf[8];
-    if constexpr (FP8) {
+  // Rows of the next stage to request are looked up one stage ahead, so the page-table reads
+  // from LDS are long done when the copies are issued.  Copy c (c < ND: keys, c = ND: scales)
+  // of stage v starts at token tok(v, c); (lk_pg, lk_of) = its page and offset in that page for
+  // the stage to look up next, stepped by ST tokens per stage (no division in the loop).
+  auto tok = [&](int v, int c) {
+    const int t0 = tile_base + v * G::ST;
+    if (c == G::ND) return t0 + wave * 64 + lane;
+    return CONTIG ? t0 + (lane_row[c] & ~(kSub - 1)) : t0 + lane_row[c];
+  };
+  constexpr int NL = G::ND + (FP8 ? 1 : 0);
+  int lk_pg[NL], lk_of[NL];
 #pragma unroll
-      for (int s2 = 0; s2 < 4; ++s2) {          // dims h*64 + 16*s2 .. +16 = piece 4h + s2
-        const u32x4 raw = *(const u32x4*)(rows + n_in_sub * G::RB + 16 * ((4 * half + s2) ^ swz<FP8>(n_in_sub)));
-        __bf16 tmp[16];
+  for (int c = 0; c < NL; ++c) {
+    const int t = tok(NB - 1, c);
+    lk_pg[c] = t / P;
+    lk_of[c] = t - lk_pg[c] * P;
+  }
+  const int st_pg = G::ST / P, st_of = G::ST - st_pg * P;
+  auto lookup = [&](const Smem* __restrict__ rd, int v) {
+    Rows rw;
+    rw.sslot = 0;
 #pragma unroll
-        for (int d = 0; d < 4; ++d) fp8x4_to_bf16x4(raw[d], tmp + 4 * d);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          kf[2 * s2][e] = tmp[e];
-          kf[2 * s2 + 1][e] = tmp[8 + e];
-        }
+    for (int c = 0; c < NL; ++c) {
+      // (tokens at or past t_stop read an entry inside the staged table, or zeros past it,
+      // and take row 0)
+      const int32_t sl = rd->pt[lk_pg[c] - page0] * P + lk_of[c];
+      const int32_t val = tok(v, c) < t_stop ? sl : 0;
+      // (CONTIG: the copy's run start is the same for the whole wave)
+      if (c < G::ND) rw.slot[c] = CONTIG ? __builtin_amdgcn_readfirstlane(val) : val;
+      else rw.sslot = scale_wave ? val : 0;
+      lk_pg[c] += st_pg;
+      lk_of[c] += st_of;
+      if (lk_of[c] >= P) {
+        lk_of[c] -= P;
+        ++lk_pg[c];
       }
-    } else {
-#pragma unroll
-      for (int s = 0; s < 8; ++s)               // dims h*64 + 8s .. +8 = piece 8h + s
-        kf[s] = *(const bf16x8*)(rows + n_in_sub * G::RB + 16 * ((8 * half + s) ^ swz<FP8>(n_in_sub)));
     }
-    f32x16 acc[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-    for (int s = 0; s < 8; ++s)
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag[mb][s], kf[s], acc[mb], 0, 0, 0);
+    return rw;
+  };
+  Rows next = lookup(&sm, NB - 1);
+
+  // The head reduction of a sub-tile runs one stage late: the MFMAs of stage v are issued next
+  // to the ReLU / weight / head-sum work of stage v-1, so the matrix core and the vector ALU
+  // overlap.  (acc_prev, t_prev, ks_prev) = stage v-1's accumulators, lane token and scale.
+  f32x16 acc_prev[2] = {f32x16{}, f32x16{}};
+  int t_prev = -1;
+  float ks_prev = 0.f;
+  auto finish = [&](const f32x16 (&acc)[2], int t, float ks) {
     float part = 0.f;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
@@ -302,30 +321,72 @@ __global__ __launch_bounds__(kThreadsI) void indexer_mfma_kernel(IndexerParams p
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj)   // ReLU as one integer max on the bits (negatives -> +0)
           part = fmaf(wr[mb][g][jj], __int_as_float(max(__float_as_int(acc[mb][4 * g + jj]), 0)), part);
-    part += __shfl_xor(part, 32);
-    if (half == 0 && t < tile_end) {
-      const float kscale = FP8 ? ((const float*)(&rd->ring[v % NB][G::SB]))[si * kSub + n_in_sub] : 1.f;
-      out[t] = t <= pos ? part * kscale : -INFINITY;
+    // add the other lane half's partial sum (lanes l and l ^ 32 hold the same token)
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
+    part = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    if (half == 0 && t >= 0 && t < tile_end) out[t] = t <= pos ? part * ks : -INFINITY;
+  };
+
+  // one stage: request stage v + NB - 1 into ring stage `dst` and look up the rows of stage
+  // v + NB; per sub-tile of this wave in stage v: B fragments (lane: token n, half h) from LDS,
+  // 32x32x16 MFMAs over the two 32-head M-blocks, then the head reduction of the sub-tile
+  // before it
+  auto compute = [&](const Smem* __restrict__ rd, int v) {
+#pragma unroll
+    for (int j = 0; j < G::SPW; ++j) {
+      const int sub = si * G::SPW + j;
+      const int t = tile_base + v * G::ST + sub * kSub + n_in_sub;
+      const uint8_t* rows = &rd->ring[v % NB][sub * kSub * G::RB];
+      bf16x8 kf[8];
+      if constexpr (FP8) {
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) {          // dims h*64 + 16*s2 .. +16 = piece 4h + s2
+          const u32x4 raw = *(const u32x4*)(rows + n_in_sub * G::RB + 16 * ((4 * half + s2) ^ swz<FP8>(n_in_sub)));
+          __bf16 tmp[16];
+#pragma unroll
+          for (int d = 0; d < 4; ++d) fp8x4_to_bf16x4(raw[d], tmp + 4 * d);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            kf[2 * s2][e] = tmp[e];
+            kf[2 * s2 + 1][e] = tmp[8 + e];
+          }
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < 8; ++s)               // dims h*64 + 8s .. +8 = piece 8h + s
+          kf[s] = *(const bf16x8*)(rows + n_in_sub * G::RB + 16 * ((8 * half + s) ^ swz<FP8>(n_in_sub)));
+      }
+      const float ks = FP8 ? ((const float*)(&rd->ring[v % NB][G::SB]))[sub * kSub + n_in_sub] : 1.f;
+      // (sub-tiles wholly past the row's position are computed too, on valid rows, and written
+      // as -inf by the reduction)
+      f32x16 acc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+          acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag[mb][s], kf[s], acc[mb], 0, 0, 0);
+      finish(acc_prev, t_prev, ks_prev);
+      acc_prev[0] = acc[0];
+      acc_prev[1] = acc[1];
+      t_prev = t;
+      ks_prev = ks;
     }
   };
 
-  // loads of this wave per stage (its 16-byte pieces, plus the scales for some waves)
   for (int v = 0; v < nstage; ++v) {
     // stage v must have landed: at most the loads of the later stages requested so far
     // (v+1 .. v+NB-2) may still be outstanding (vector-memory loads complete in order)
     const int later = min(NB - 2, nstage - 1 - v);
-    if (scale_wave) {
-      if (later >= 2) wait_vmcnt<2 * (G::ND + 1)>();
-      else if (later == 1) wait_vmcnt<G::ND + 1>();
-      else wait_vmcnt<0>();
-    } else {
-      if (later >= 2) wait_vmcnt<2 * G::ND>();
-      else if (later == 1) wait_vmcnt<G::ND>();
-      else wait_vmcnt<0>();
-    }
+    if (scale_wave) wait_vmcnt_later<G::ND + 1, NB - 2>(later);
+    else wait_vmcnt_later<G::ND, NB - 2>(later);
     lds_barrier();   // stage v landed for every wave; stage v-1 is no longer read
-    stage(&sm, sm.ring[(v + NB - 1) % NB], v);
+    if (v + NB - 1 < nstage) {
+      issue(sm.ring[(v + NB - 1) % NB], next);
+      if (v + NB < nstage) next = lookup(&sm, v + NB);
+    }
+    compute(&sm, v);
   }
+  finish(acc_prev, t_prev, ks_prev);
   // tokens of [tile_base, tile_end) past the block's last position: -inf (their stages are not
   // computed)
   for (int t = max(t_stop, tile_base) + (int)threadIdx.x; t < tile_end; t += kThreadsI)
@@ -343,19 +404,20 @@ hipError_t launch_indexer(const IndexerParams& p0, dsa_dtype_t q_dtype, dsa_dtyp
   IndexerParams p = p0;
   if (indexer_uses_mfma(p.Hi, p.Di, q_dtype, k_dtype)) {
     const int64_t tiles = ((int64_t)p.max_seq_len + kTile - 1) / kTile;
-    // about two rounds of the 256 workgroups the GPU holds at once (one per CU), each with as
-    // many steps as that allows: longer workgroups pay their q / page-table staging less often
+    // about one round of the 256 workgroups the GPU holds at once (one per CU): a workgroup's
+    // q / page-table staging and first copies take several microseconds, paid once per CU
     const bool contig = p.P % kSub == 0;
     const int QB = (p.Q % 2 == 0) ? 2 : 1;
     const int64_t work = tiles * p.B * (p.Q / QB);
     const int max_tpw = contig ? kMaxTpwContig : kMaxTpwAny;
-    int tpw = (int)(work / 512);
+    int tpw = (int)(work / 256);
     tpw = tpw < 1 ? 1 : (tpw > max_tpw ? max_tpw : tpw);
     p.tiles_per_wg = tpw;
     p.p_shift = (p.P & (p.P - 1)) == 0 ? __builtin_ctz((unsigned)p.P) : -1;
     const int64_t groups = (tiles + tpw - 1) / tpw;
-    p.groups_padded = (int32_t)((groups + 7) / 8 * 8);
-    const dim3 grid((unsigned)((int64_t)p.groups_padded * (p.Q / QB) * p.B));
+    p.groups = (int32_t)groups;
+    const int64_t ranges = (groups * p.B + 7) / 8 * 8;
+    const dim3 grid((unsigned)(ranges * (p.Q / QB)));
     const bool f8 = k_dtype == DSA_FP8_E4M3FN;
 #define DSA_IDX_MFMA(F8, CT, QBV) hipLaunchKernelGGL((indexer_mfma_kernel<F8, CT, QBV>), grid, dim3(kThreadsI), 0, s, p)
     if (QB == 2) {
