@@ -155,11 +155,11 @@ def topk_workspace_bytes(batch: DsaBatch, k: int) -> int:
 def dsa_topk(batch: DsaBatch, scores: torch.Tensor, k: int, topk_idx: torch.Tensor,
              topk_slots: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
              stream=None) -> torch.Tensor:
-    """Top-k with the fused page map (see dsa.h).  A workspace passed in must be zero-filled
-    before its first use; the call leaves it zero-filled.  Without one a zeroed buffer is made."""
+    """Top-k with the fused page map (see dsa.h).  Long rows use a workspace of
+    topk_workspace_bytes(batch, k) bytes (no initial contents); without one a buffer is made."""
     need = topk_workspace_bytes(batch, k)
     if workspace is None and need:
-        workspace = torch.zeros(need, dtype=torch.uint8, device=scores.device)
+        workspace = torch.empty(need, dtype=torch.uint8, device=scores.device)
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().dsa_topk(ctypes.byref(batch), _ptr(scores), scores.shape[-1], k, _ptr(topk_idx),
                           _ptr(topk_slots), _ptr(workspace), nbytes, _stream(stream)))

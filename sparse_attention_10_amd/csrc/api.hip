@@ -248,22 +248,21 @@ dsa_status_t dsa_indexer_scores(const dsa_batch_t* b, const void* q, dsa_dtype_t
 }
 
 size_t dsa_topk_workspace_size(const dsa_batch_t* b, int32_t k) {
-  (void)k;
-  if (!b || b->batch < 1 || b->q_per_seq < 1 || b->max_seq_len < 1) return 0;
-  return topk_workspace_bytes((int64_t)b->batch * b->q_per_seq, b->max_seq_len);
+  if (!b || b->batch < 1 || b->q_per_seq < 1 || b->max_seq_len < 1 || k < 1) return 0;
+  return topk_workspace_bytes((int64_t)b->batch * b->q_per_seq, b->max_seq_len, k);
 }
 
 dsa_status_t dsa_topk(const dsa_batch_t* b, const float* scores, int64_t scores_ld, int32_t k, int32_t* topk_idx,
                       int32_t* topk_slots, void* workspace, size_t workspace_bytes, void* stream) {
   DSA_TRY(check_topk(b, scores, scores_ld, k, topk_idx));
   DSA_REQUIRE(!topk_slots || aligned(topk_slots, 4), "topk: topk_slots must be 4-byte aligned");
-  const size_t need = topk_workspace_bytes((int64_t)b->batch * b->q_per_seq, b->max_seq_len);
+  const size_t need = topk_workspace_bytes((int64_t)b->batch * b->q_per_seq, b->max_seq_len, k);
   if (workspace_bytes < need || (need > 0 && workspace == nullptr))
     return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "topk: workspace needs %zu bytes (got %zu)", need, workspace_bytes);
   DSA_REQUIRE(need == 0 || aligned(workspace, 256), "topk: workspace must be 256-byte aligned");
   DSA_TRY(check_device());
   TopkParams p{scores, scores_ld, b->seq_lens, b->page_table, topk_idx, topk_slots,
-               b->q_per_seq, k, b->page_size, b->max_pages_per_seq};
+               b->q_per_seq, k, b->page_size, b->max_pages_per_seq, 0, 0, nullptr, nullptr, 0};
   return launched(launch_topk(p, b->batch * b->q_per_seq, b->max_seq_len, workspace, (hipStream_t)stream),
                   "top-k");
 }
@@ -336,8 +335,8 @@ StepWs step_ws(const dsa_decode_step_args_t* a) {
   const int64_t rows = (int64_t)b.batch * b.q_per_seq;
   w.ld = b.max_seq_len;
   size_t off = 0;
-  w.topk_off = off;   // first, so that its zero-filled state sits at a fixed place
-  off += align_up(topk_workspace_bytes(rows, b.max_seq_len), 256);
+  w.topk_off = off;   // top-k candidates of long rows
+  off += align_up(topk_workspace_bytes(rows, b.max_seq_len, a->top_k), 256);
   w.scores_off = off;
   if (!a->debug_scores) off += align_up((size_t)rows * w.ld * sizeof(float), 256);
   w.idx_off = off;
@@ -403,7 +402,7 @@ dsa_status_t dsa_decode_step(const dsa_decode_step_args_t* a, void* workspace, s
   DSA_TRY(launched(launch_indexer(ip, a->q_idx_dtype, a->k_dtype, s), "indexer"));
 
   TopkParams tp{scores, w.ld, b->seq_lens, b->page_table, idx, slots,
-                b->q_per_seq, a->top_k, b->page_size, b->max_pages_per_seq};
+                b->q_per_seq, a->top_k, b->page_size, b->max_pages_per_seq, 0, 0, nullptr, nullptr, 0};
   DSA_TRY(launched(launch_topk(tp, b->batch * b->q_per_seq, b->max_seq_len, ws + w.topk_off, s), "top-k"));
 
   const int64_t rows = (int64_t)b->batch * b->q_per_seq;

@@ -134,6 +134,13 @@ struct TopkParams {
   int32_t* idx;
   int32_t* slots;   // may be null
   int32_t Q, k, P, maxP;
+  // long rows in two passes: chunks of chunk_len columns (nchunks per row) each keep their
+  // own top min(k, chunk_len) as candidates (score, column) in ascending column order, then one
+  // pass per row selects among the candidates
+  int32_t chunk_len, nchunks;
+  float* cand_score;      // [rows, cand_ld]
+  int32_t* cand_col;      // [rows, cand_ld]
+  int64_t cand_ld;
 };
 
 struct MlaParams {
@@ -164,9 +171,10 @@ struct CombineParams {
 hipError_t launch_indexer(const IndexerParams& p, dsa_dtype_t q_dtype, dsa_dtype_t k_dtype,
                           hipStream_t s);
 bool indexer_uses_mfma(int Hi, int Di, dsa_dtype_t q_dtype, dsa_dtype_t k_dtype);
-// Top-k: `ws` is topk_workspace_bytes(rows, max_seq_len) bytes of zero-filled device memory
-// (left zero-filled by the launch), or unused when that size is 0.
-size_t topk_workspace_bytes(int64_t rows, int max_seq_len);
+// Top-k: `ws` is topk_workspace_bytes(rows, max_seq_len, k) bytes of device memory (the
+// candidates of the two-pass plan for long rows; no initial contents), or unused when that
+// size is 0.
+size_t topk_workspace_bytes(int64_t rows, int max_seq_len, int k);
 hipError_t launch_topk(const TopkParams& p, int rows, int max_seq_len, void* ws, hipStream_t s);
 hipError_t launch_page_map(const int32_t* idx, int64_t total, int k, int Q, const int32_t* pt,
                            int maxP, int P, int32_t* slots, hipStream_t s);

@@ -202,7 +202,11 @@ __device__ __forceinline__ uint32_t radix_round(KeysFn&& keys_fn, uint32_t pmask
   return select_bin(hist, nb, kr, red, sel, above, cnt);
 }
 
-template <int RV>
+// MODE 0: one workgroup per row.  MODE 1 (first pass over long rows): one workgroup per chunk
+// of p.chunk_len columns, whose winners go to the candidate list.  MODE 2 (second pass): one
+// workgroup per row, over the row's candidates (position j of the list holds the column
+// p.cand_col[j]; positions ascend with columns, so ties still go to the lower column).
+template <int RV, int MODE>
 __global__ __launch_bounds__(kThreads) void topk_kernel(TopkParams p) {
   __shared__ __attribute__((aligned(16))) uint32_t big[kHistWords];   // histogram, then the regions above
   __shared__ uint32_t tsum[kThreads + kThreads / 8];   // padded layout of wave_select<8>
@@ -214,31 +218,60 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkParams p) {
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform (kept in a scalar register)
-  const int row = blockIdx.x;
+  const int row = MODE == 1 ? (int)blockIdx.x / p.nchunks : (int)blockIdx.x;
+  const int chunk = MODE == 1 ? (int)blockIdx.x - row * p.nchunks : 0;
   const int b = row / p.Q, i = row - b * p.Q;
-  int n = p.seq_lens[b] - p.Q + i + 1;             // visible tokens of this row
-  n = n < 0 ? 0 : n;
-  n = (int64_t)n > p.ld ? (int)p.ld : n;           // guards against lengths past the scores row
-  n = n > kMaxTopkSeq ? kMaxTopkSeq : n;
+  int n_row = p.seq_lens[b] - p.Q + i + 1;         // visible tokens of this row
+  n_row = n_row < 0 ? 0 : n_row;
+  n_row = (int64_t)n_row > p.ld ? (int)p.ld : n_row;   // guards against lengths past the scores row
+  n_row = n_row > kMaxTopkSeq ? kMaxTopkSeq : n_row;
+  if constexpr (MODE != 0) n_row = min(n_row, p.nchunks * p.chunk_len);   // the candidate rows' reach
   const int k = p.k;
-  int32_t* idx_out = p.idx + (int64_t)row * k;
-  int32_t* slot_out = p.slots ? p.slots + (int64_t)row * k : nullptr;
   const int32_t* ptab = p.page_table + (int64_t)b * p.maxP;
+  const int kc = min(k, p.chunk_len);              // candidates kept per full chunk
+  // n: keys this workgroup ranks; srow: their scores; c0: column of the first (MODE 1)
+  int n = n_row, c0 = 0;
+  const float* srow = p.scores + (int64_t)row * p.ld;
+  if constexpr (MODE == 1) {
+    c0 = chunk * p.chunk_len;
+    n = min(max(n_row - c0, 0), p.chunk_len);
+    srow += c0;
+  } else if constexpr (MODE == 2) {
+    const int nch = (n_row + p.chunk_len - 1) / p.chunk_len;
+    n = nch > 0 ? (nch - 1) * kc + min(k, n_row - (nch - 1) * p.chunk_len) : 0;
+    srow = p.cand_score + (int64_t)row * p.cand_ld;
+  }
+  const int32_t* ccol = MODE == 2 ? p.cand_col + (int64_t)row * p.cand_ld : nullptr;
+  // MODE 1 writes its winners after those of the chunks before it (each keeps kc)
+  float* cs_out = MODE == 1 ? p.cand_score + (int64_t)row * p.cand_ld + (int64_t)chunk * kc : nullptr;
+  int32_t* cc_out = MODE == 1 ? p.cand_col + (int64_t)row * p.cand_ld + (int64_t)chunk * kc : nullptr;
+  int32_t* idx_out = MODE == 1 ? nullptr : p.idx + (int64_t)row * k;
+  int32_t* slot_out = MODE != 1 && p.slots ? p.slots + (int64_t)row * k : nullptr;
 
-  if (n <= k) {   // everything visible is selected
-    for (int j = tid; j < k; j += kThreads) {
-      idx_out[j] = j < n ? j : -1;
-      if (slot_out) slot_out[j] = j < n ? ptab[j / p.P] * p.P + j % p.P : -1;
+  if constexpr (MODE == 1) {
+    if (n <= k) {   // the whole chunk is kept
+      for (int j = tid; j < n; j += kThreads) {
+        cs_out[j] = srow[j];
+        cc_out[j] = c0 + j;
+      }
+      return;
     }
-    return;
+  } else {
+    if (n_row <= k || n <= k) {   // everything visible (every candidate) is selected
+      for (int j = tid; j < k; j += kThreads) {
+        const int t = j < n ? (MODE == 2 ? ccol[j] : j) : -1;
+        idx_out[j] = t;
+        if (slot_out) slot_out[j] = t >= 0 ? ptab[t / p.P] * p.P + t % p.P : -1;
+      }
+      return;
+    }
   }
 
   // ---- pass 1: keys (registers), page-table row (registers), first-digit histogram
   constexpr int kRegRows = RV * kWaves;              // key rows held in registers
-  const float* srow = p.scores + (int64_t)row * p.ld;
   const int nrows = (n + 63) >> 6;
   const int nseg = nrows > kRegRows ? (nrows - kRegRows + kTailRows * kWaves - 1) / (kTailRows * kWaves) : 0;
-  const int npages = (n + p.P - 1) / p.P;
+  const int npages = (n_row + p.P - 1) / p.P;       // pages of the row's visible columns
   const bool cache_pages = slot_out != nullptr && npages <= kPtabCache;
   // key row r (uniform) holds columns 64r .. 64r+63; register row j of wave w is row w*RV + j
   auto key_of = [&](float x, int r) -> uint32_t {
@@ -643,16 +676,23 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkParams p) {
   if (ties) emit_all(Flag<true>());
   else emit_all(Flag<false>());
   __syncthreads();
-  // the k winners, in column order, with their cache slots (fused page map)
+  // the k winners, in column order, with their cache slots (fused page map); MODE 1: their
+  // scores and columns as candidates
   const int P = p.P;
   const bool p_pow2 = (P & (P - 1)) == 0;
   const int p_shift = __ffs(P) - 1;
   for (int j = tid; j < k; j += kThreads) {
-    const int t = out_s[j];
+    const int pos = out_s[j];
+    if constexpr (MODE == 1) {
+      cs_out[j] = srow[pos];
+      cc_out[j] = c0 + pos;
+      continue;
+    }
+    const int t = MODE == 2 ? ccol[pos] : pos;
     idx_out[j] = t;
     if (slot_out) {
       int pg = p_pow2 ? t >> p_shift : t / P;
-      pg = min(max(pg, 0), npages - 1);            // (t is always in [0, n); the clamp only guards the lookup)
+      pg = min(max(pg, 0), npages - 1);            // (t is always in [0, n_row); the clamp only guards the lookup)
       const int pe = cache_pages ? big[kOffPtab + pg] : ptab[pg];
       slot_out[j] = pe * P + (t - pg * P);
     }
@@ -671,22 +711,66 @@ __global__ __launch_bounds__(256) void page_map_kernel(const int32_t* idx, int64
 
 }  // namespace
 
-size_t topk_workspace_bytes(int64_t rows, int max_seq_len) {
-  (void)rows;
-  (void)max_seq_len;
-  return 0;
+namespace {
+
+// Two-pass plan for long rows: the chunk length L (0 = one pass) and chunks per row.  Rows of
+// 64K+ columns are split when they are few (at most 64, a quarter of the compute units), the
+// chunks still fit about one workgroup per compute unit, and a chunk keeps at most a quarter of
+// its columns as candidates.  (Measured on MI355X: a 128K row takes 57 us in one pass and 31 us
+// in chunks of 16K; 128 rows of 64K are faster in one pass.)
+struct TopkPlan {
+  int L, C;
+};
+TopkPlan topk_plan(int64_t rows, int max_seq_len, int k) {
+  if (max_seq_len < 65536 || rows > 64) return {0, 0};
+  for (int L = 16384; L <= 32768; L *= 2) {
+    const int C = (max_seq_len + L - 1) / L;
+    if (L >= 4 * k && C >= 2 && rows * C <= 256) return {L, C};
+  }
+  return {0, 0};
 }
 
-hipError_t launch_topk(const TopkParams& p, int rows, int max_seq_len, void* ws, hipStream_t s) {
-  (void)ws;
-  // 8, 16, 32 or 64 key rows per wave stay in registers (up to 32K columns); rows past that
-  // are re-read from L2 in each pass.
-  const dim3 grid((unsigned)rows), block(kThreads);
-  const int need = (max_seq_len + 64 * kWaves - 1) / (64 * kWaves);   // key rows per wave
-  if (need <= 8) hipLaunchKernelGGL(topk_kernel<8>, grid, block, 0, s, p);
-  else if (need <= 16) hipLaunchKernelGGL(topk_kernel<16>, grid, block, 0, s, p);
-  else if (need <= 32) hipLaunchKernelGGL(topk_kernel<32>, grid, block, 0, s, p);
-  else hipLaunchKernelGGL(topk_kernel<64>, grid, block, 0, s, p);
+template <int MODE>
+void launch_topk_mode(const TopkParams& p, unsigned blocks, int keys, hipStream_t s) {
+  // 8, 16, 32 or 64 key rows per wave stay in registers (up to 32K keys); keys past that are
+  // re-read from L2 in each pass
+  const int need = (keys + 64 * kWaves - 1) / (64 * kWaves);
+  const dim3 grid(blocks), block(kThreads);
+  if (need <= 8) hipLaunchKernelGGL((topk_kernel<8, MODE>), grid, block, 0, s, p);
+  else if (need <= 16) hipLaunchKernelGGL((topk_kernel<16, MODE>), grid, block, 0, s, p);
+  else if (need <= 32) hipLaunchKernelGGL((topk_kernel<32, MODE>), grid, block, 0, s, p);
+  else hipLaunchKernelGGL((topk_kernel<64, MODE>), grid, block, 0, s, p);
+}
+
+}  // namespace
+
+size_t topk_workspace_bytes(int64_t rows, int max_seq_len, int k) {
+  const TopkPlan pl = topk_plan(rows, max_seq_len, k);
+  if (pl.L == 0) return 0;
+  const int64_t ld = (int64_t)pl.C * (k < pl.L ? k : pl.L);
+  return (size_t)(rows * ld) * (sizeof(float) + sizeof(int32_t)) + 256;
+}
+
+hipError_t launch_topk(const TopkParams& p0, int rows, int max_seq_len, void* ws, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  const TopkPlan pl = topk_plan(rows, max_seq_len, p0.k);
+  if (pl.L == 0) {
+    TopkParams p = p0;
+    p.chunk_len = 1 << 30;
+    launch_topk_mode<0>(p, (unsigned)rows, max_seq_len, s);
+    return hipGetLastError();
+  }
+  TopkParams p = p0;
+  p.chunk_len = pl.L;
+  p.nchunks = pl.C;
+  p.cand_ld = (int64_t)pl.C * (p.k < pl.L ? p.k : pl.L);
+  p.cand_score = (float*)ws;
+  const size_t score_bytes = ((size_t)rows * p.cand_ld * sizeof(float) + 255) / 256 * 256;
+  p.cand_col = (int32_t*)((char*)ws + score_bytes);
+  launch_topk_mode<1>(p, (unsigned)(rows * pl.C), pl.L, s);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  launch_topk_mode<2>(p, (unsigned)rows, (int)p.cand_ld, s);
   return hipGetLastError();
 }
 

@@ -90,6 +90,20 @@ def test_topk_rejects(L):
     assert L.dsa_topk_workspace_size(ctypes.byref(b), 2048) == 0
 
 
+def test_topk_workspace_long_rows(L):
+    # a few rows of 64K+ columns are ranked in two passes whose candidates need a workspace:
+    # 32 rows x 8 chunks of 16K keep 8 x 2048 (score, column) pairs each
+    long = _batch(batch=32, q_per_seq=1, max_seq_len=131072, max_pages_per_seq=2048, num_slots=32 * 131072)
+    need = L.dsa_topk_workspace_size(ctypes.byref(long), 2048)
+    assert need >= 32 * 8 * 2048 * 8
+    assert L.dsa_topk(ctypes.byref(long), FAKE, 131072, 2048, FAKE, None, None, 0, None) == 3
+    assert L.dsa_topk(ctypes.byref(long), FAKE, 131072, 2048, FAKE, None, FAKE, need - 1, None) == 3
+    # below 64K columns, or many rows (one workgroup per row fills the GPU): one pass
+    assert L.dsa_topk_workspace_size(ctypes.byref(_batch(max_seq_len=65535, max_pages_per_seq=1024)), 2048) == 0
+    many = _batch(batch=64, q_per_seq=2, max_seq_len=65536, max_pages_per_seq=1024, num_slots=64 * 65536)
+    assert L.dsa_topk_workspace_size(ctypes.byref(many), 2048) == 0
+
+
 def _mla(L, **kw):
     a = dict(B=1, Q=1, q=FAKE, qd=dsa.DSA_BF16, kv=FAKE, kvd=dsa.DSA_BF16, ks=None, ns_=4096, sl=FAKE, k=2048,
              H=64, scale=0.04, out=FAKE, lse=None, split=0, ws=None, wsb=0)

@@ -104,6 +104,10 @@ TOPK_CASES = [
     # many long ragged rows at once: register part plus the streamed tail
     ("narrow", [131072, 100000, 70001, 65537, 40000, 32769, 5000, 2049], 1, 2048),
     ("dupes", [131072, 98304], 2, 2048),
+    # two passes (rows of 64K+ columns in chunks of 16K): a last chunk of exactly k columns, one
+    # of k + 1, a row inside the first chunk, rows that need no selection
+    ("narrow", [65636, 18432, 18433, 3000, 2048, 50], 1, 2048),
+    ("levels", [65536 + 17, 40000], 2, 2048),
 ]
 
 
