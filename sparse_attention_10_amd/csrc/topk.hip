@@ -9,8 +9,9 @@
 // columns, one per lane.  Wave w holds RV consecutive key rows of the row's first 512*RV
 // columns in registers; later columns are streamed from L2 in segments.
 //   pass 1  Scores become order-preserving uint32 keys (larger score <-> larger key; key 0
-//           marks a column outside the row) and are counted into an LDS histogram of their top
-//           15 bits.  A scan of per-thread bin sums, then of the chosen thread's bins, finds the
+//           marks a column outside the row) and are counted into an LDS histogram of 15 bits:
+//           those just below the leading bits that all keys of the row share (found from the
+//           keys' min and max).  A scan of per-thread bin sums, then of the chosen thread's bins, finds the
 //           bin b holding the k-th largest key.  A bin holding more than kCandCap keys is
 //           narrowed by 11-bit radix rounds over the keys of that bin.
 //   pass 2  Per unit (one wave's key rows of the register block, or of one streamed segment)
@@ -65,18 +66,18 @@ static_assert(kBinsPerThread % 4 == 0 && kBinsPerThread <= 64, "histogram layout
 
 // Order-preserving key of a float score: larger float <-> larger unsigned key.  Adding +0.0
 // turns -0.0 into +0.0 (so the two compare equal) and leaves every other value unchanged.
-// Finite scores and -inf map to keys >= 0x007FFFFF (15-bit bin >= 63), so key 0 is free to
-// mark "no score" and bins 0..62 of the first-digit histogram hold no score.
+// Finite scores and -inf map to keys >= 0x007FFFFF, so key 0 is free to mark "no score".
 __device__ __forceinline__ uint32_t order_key(float f) {
   const uint32_t u = __float_as_uint(f + 0.0f);
   return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 
-// Word of bin (key >> 17) in the first-digit histogram.  Thread t's B = kBinsPerThread bins
+// Word of first-digit bin `bin` (15 bits) in the histogram.  Thread t's B = kBinsPerThread bins
 // [Bt, Bt+B) sit at words kHistStride*t.., 16-byte aligned, so that the per-thread sums are
-// read as b128 and the 16 lanes of one LDS pass start on distinct banks.
-__device__ __forceinline__ uint32_t hist_word(uint32_t key) {
-  return (key >> 17) + (kHistStride - kBinsPerThread) * (key >> (17 + kBinShift));
+// read as b128 and the 16 lanes of one LDS pass start on distinct banks.  The 4 words after
+// each thread's bins are never summed.
+__device__ __forceinline__ uint32_t hist_word(uint32_t bin) {
+  return bin + (kHistStride - kBinsPerThread) * (bin >> kBinShift);
 }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
@@ -213,6 +214,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkParams p) {
   __shared__ uint32_t red[kWaves];
   __shared__ uint32_t sel[4];
   __shared__ uint32_t wave_cnt[kWaves];
+  __shared__ uint32_t wave_min[kWaves], wave_max[kWaves];
   __shared__ uint32_t cand_n;
 
   const int tid = threadIdx.x;
@@ -357,26 +359,55 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkParams p) {
     tail_pass([&](uint32_t kk, int) { visit(kk); }, nop, nop);
   };
 
-  __syncthreads();
+  // ---- the first digit: the 15 key bits below the leading bits that every key of the row
+  // shares (the keys' min and max agree on them), so that a row of close scores still spreads
+  // over the histogram.  Rows with a streamed part (which would need a pass of its own for
+  // the min and max) take the top 15 bits.
   {
-    // a column outside the row counts into one of the bins 1..32, which no score uses (spread
-    // so that a short row does not pile onto one LDS address)
-    const uint32_t dummy = (uint32_t)(lane & 31) + 1u;
+    uint32_t mn = ~0u, mx = 0u;                      // key 0 (outside the row) is left out of the min
+#pragma unroll
+    for (int j = 0; j < RV; ++j) {
+      mn = min(mn, key[j] ? key[j] : ~0u);
+      mx = max(mx, key[j]);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      mn = min(mn, (uint32_t)__shfl_xor((int)mn, o));
+      mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
+    }
+    if (lane == 0) {
+      wave_min[wave] = mn;
+      wave_max[wave] = mx;
+    }
+  }
+  __syncthreads();
+  uint32_t kmin = wave_min[0], kmax = wave_max[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) {
+    kmin = min(kmin, wave_min[w]);
+    kmax = max(kmax, wave_max[w]);
+  }
+  // (n > k >= 1, so some key is in the row and kmin <= kmax)
+  const int common = nseg > 0 ? 0 : (kmin ^ kmax) ? __builtin_clz(kmin ^ kmax) : 32;
+  const int sh1 = common >= 17 ? 0 : 17 - common;   // the digit is key bits [sh1, sh1 + 15)
+  auto bin1 = [sh1](uint32_t kk) { return (kk >> sh1) & 0x7FFFu; };
+  {
+    // a column outside the row counts into one of 32 words that are never summed (spread so
+    // that a short row does not pile onto one LDS address)
+    const uint32_t dummy = (uint32_t)(kHistStride * (lane & 31) + kBinsPerThread);
     auto count = [&](uint32_t kk, int r) {
-      if (((r + 1) << 6) <= n) atomicAdd(&big[hist_word(kk)], 1u);
-      else if ((r << 6) < n) atomicAdd(&big[kk ? hist_word(kk) : dummy], 1u);
+      if (((r + 1) << 6) <= n) atomicAdd(&big[hist_word(bin1(kk))], 1u);
+      else if ((r << 6) < n) atomicAdd(&big[kk ? hist_word(bin1(kk)) : dummy], 1u);
     };
     if (reg_full) {
 #pragma unroll
-      for (int j = 0; j < RV; ++j) atomicAdd(&big[hist_word(key[j])], 1u);
+      for (int j = 0; j < RV; ++j) atomicAdd(&big[hist_word(bin1(key[j]))], 1u);
     } else {
 #pragma unroll
       for (int j = 0; j < RV; ++j) count(key[j], wave * RV + j);
     }
     tail_pass(count, nop, nop);
   }
-  __syncthreads();
-  if (tid < 63) big[tid] = 0u;                       // bins 0..62 (words 0..62) hold no score
   __syncthreads();
 
   // ---- the first-digit bin: sums of kBinsPerThread bins per thread, then the bins of the chosen sum
@@ -407,9 +438,10 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkParams p) {
   const uint32_t b1 = r1 * kBinsPerThread + fb;
   kr -= above1;
   __syncthreads();                                   // every wave has read the histogram
-  int plen = 15;
-  uint32_t pmask = 0xFFFE0000u;
-  uint32_t pval = b1 << 17;
+  // the bin's keys: the shared leading bits, then b1
+  int plen = 32 - sh1;
+  uint32_t pmask = ~0u << sh1;
+  uint32_t pval = (sh1 + 15 >= 32 ? 0u : kmin & (~0u << (sh1 + 15))) | (b1 << sh1);
   bool take_all = cnt == kr;                         // the whole bin is selected
 
   // ---- narrowing rounds while the bin is too large to gather (many equal or near-equal keys)
