@@ -27,6 +27,17 @@ namespace dsa {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+
+// Four f32 values as e4m3 pairs (round to nearest even): hw = e4m3(f), lw = e4m3(f - hw), byte
+// j of each word for value j.
+__device__ __forceinline__ void split_e4m3_x4(float f0, float f1, float f2, float f3, int& hw, int& lw) {
+  hw = __builtin_amdgcn_cvt_pk_fp8_f32(f0, f1, 0, false);
+  hw = __builtin_amdgcn_cvt_pk_fp8_f32(f2, f3, hw, true);
+  const float h0 = __builtin_amdgcn_cvt_f32_fp8(hw, 0), h1 = __builtin_amdgcn_cvt_f32_fp8(hw, 1);
+  const float h2 = __builtin_amdgcn_cvt_f32_fp8(hw, 2), h3 = __builtin_amdgcn_cvt_f32_fp8(hw, 3);
+  lw = __builtin_amdgcn_cvt_pk_fp8_f32(f0 - h0, f1 - h1, 0, false);
+  lw = __builtin_amdgcn_cvt_pk_fp8_f32(f2 - h2, f3 - h3, lw, true);
+}
 constexpr float kLn2 = 0.6931471805599453f;
 
 // ---------------------------------------------------------------------------------------------
@@ -660,7 +671,8 @@ constexpr int kTXCopies = kTXBytes / 1024;               // 36
 constexpr int kRingX = 4;
 constexpr int kNTX = 256;                                // 4 waves
 constexpr int kChunkX = 1024;                            // selected rows staged per workgroup
-constexpr int kStepsX = kRowDim / 32;                    // 18 K steps of 32
+constexpr int kStepsX = kRowDim / 32;                    // 18 K steps of 32 (bf16 q loads)
+constexpr int kKBlocksX = (kRowDim + 127) / 128;         // 5 e4m3 K blocks of 128 (the last half empty)
 constexpr int kDBlocksW = kVDim / 16 / 4;                // 8 output blocks of 16 per wave
 
 // Shared memory of mla_fp8x_kernel.
@@ -720,16 +732,50 @@ __global__ __launch_bounds__(kNTX) void mla_fp8x_kernel(MlaParams p) {
     }
   };
 
-  // q fragments of this wave's S^T head group (head 16w + m16).  The K order of the S^T
-  // contraction is permuted so that one 16-byte LDS read serves two MFMA steps: step 2u + h
-  // gives lane group grp the dims 64u + 16grp + 8h .. +8 (the rows' operand follows suit).
-  bf16x8 qf[kStepsX];
+  // q of this wave's S^T head group (head 16w + m16) as two e4m3 parts: scaled by 2^qs so that
+  // its largest magnitude lies in [128, 256), hi = e4m3(q 2^qs) and lo = e4m3(q 2^qs - hi), so
+  // hi + lo = q 2^qs exactly for every element down to 2^-18 of the largest (e4m3 holds 4
+  // significant bits, bf16 8).  S^T then runs on the e4m3 matrix core with no widening of the
+  // rows.  K block b (of 5) gives lane group grp, in bytes 0-15 / 16-31, the dims
+  // 64u + 16grp .. +16 of u = 2b / 2b + 1 (u = 9: zeros), the rows' operand following suit.
+  i32x8 qh[kKBlocksX], ql[kKBlocksX];
+  float q_unscale = 1.f;                          // 2^-qs
   if (s_active) {
     const bf16x8* qrow = (const bf16x8*)((const __bf16*)p.q + ((int64_t)r * p.H + wave * 16 + m16) * kRowDim);
+    bf16x8 raw[kStepsX];
 #pragma unroll
     for (int u = 0; u < kStepsX / 2; ++u)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) qf[2 * u + h] = qrow[8 * u + 2 * grp + h];
+      for (int h = 0; h < 2; ++h) raw[2 * u + h] = qrow[8 * u + 2 * grp + h];
+    float mx = 0.f;
+#pragma unroll
+    for (int i = 0; i < kStepsX; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf((float)raw[i][e]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    // exponent of mx (mx = f * 2^ex, f in [1, 2)): qs = 7 - ex puts mx in [128, 256)
+    const int ex = mx > 0.f ? (int)((__float_as_uint(mx) >> 23) & 255u) - 127 : 7;
+    const int qs = 7 - ex;
+    q_unscale = __uint_as_float((uint32_t)(127 - qs) << 23);
+#pragma unroll
+    for (int b = 0; b < kKBlocksX; ++b) {
+      qh[b] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+      ql[b] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int i = 0; i < kStepsX; ++i)   // raw[i] = dims 64(i/2) + 16grp + 8(i%2) .. +8
+#pragma unroll
+      for (int w2 = 0; w2 < 2; ++w2) {   // 4 values per register
+        int hw, lw;
+        split_e4m3_x4(ldexpf((float)raw[i][4 * w2], qs), ldexpf((float)raw[i][4 * w2 + 1], qs),
+                      ldexpf((float)raw[i][4 * w2 + 2], qs), ldexpf((float)raw[i][4 * w2 + 3], qs), hw, lw);
+        // step i = 2u + h: block b = u / 2, bytes 16(u % 2) + 8h + 4w2
+        const int u = i >> 1, hh = i & 1, b = u >> 1;
+        const int word = 4 * (u & 1) + 2 * hh + w2;
+        qh[b][word] = hw;
+        ql[b][word] = lw;
+      }
   }
 #pragma unroll
   for (int v = 0; v < kRingX - 1; ++v)
@@ -748,7 +794,7 @@ __global__ __launch_bounds__(kNTX) void mla_fp8x_kernel(MlaParams p) {
     for (int db = 0; db < kDBlocksW; ++db) o[g][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY;   // S^T head group: running max of z * log2(e), per head
   float l_run = 0.f;         // this lane group's share of sum exp2(z - m_run)
-  const float scale2 = p.sm_scale * kLog2e;
+  const float scale2 = p.sm_scale * kLog2e * q_unscale;   // (q_unscale: exact power of two)
 
   // S^T operand of block beta (tokens 16beta + m16), steps 2u and 2u+1: logical piece
   // 4u + grp, read whole; pieces 4 apart lie 64 bytes apart
@@ -788,23 +834,33 @@ __global__ __launch_bounds__(kNTX) void mla_fp8x_kernel(MlaParams p) {
 #pragma unroll
       for (int beta = 0; beta < 4; ++beta) sacc[beta] = f32x4{0.f, 0.f, 0.f, 0.f};
       {
-        // operands of double step u+1 are requested before double step u is computed
-        u32x4 a[2][4];
+        // e4m3 x e4m3 on v_mfma_scale_f32_16x16x128_f8f6f4 (unit scales), q hi then lo into the
+        // same accumulator; operands of K block b+1 are requested before block b is computed
+        constexpr int kU = kStepsX / 2;             // 9 double steps of 64 dims
+        u32x4 a[2][2][4];
 #pragma unroll
-        for (int beta = 0; beta < 4; ++beta) a[0][beta] = *(const u32x4*)(T + a_base[beta]);
+        for (int beta = 0; beta < 4; ++beta) {
+          a[0][0][beta] = *(const u32x4*)(T + a_base[beta]);
+          a[0][1][beta] = *(const u32x4*)(T + a_base[beta] + 64);
+        }
 #pragma unroll
-        for (int u = 0; u < kStepsX / 2; ++u) {
-          if (u + 1 < kStepsX / 2) {
+        for (int b = 0; b < kKBlocksX; ++b) {
+          if (b + 1 < kKBlocksX) {
 #pragma unroll
-            for (int beta = 0; beta < 4; ++beta) a[(u + 1) & 1][beta] = *(const u32x4*)(T + a_base[beta] + 64 * (u + 1));
+            for (int beta = 0; beta < 4; ++beta) {
+              a[(b + 1) & 1][0][beta] = *(const u32x4*)(T + a_base[beta] + 64 * (2 * b + 2));
+              if (2 * b + 3 < kU) a[(b + 1) & 1][1][beta] = *(const u32x4*)(T + a_base[beta] + 64 * (2 * b + 3));
+            }
           }
 #pragma unroll
-          for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int beta = 0; beta < 4; ++beta)
-              sacc[beta] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                  fp8x8_to_bf16x8(a[u & 1][beta][2 * h], a[u & 1][beta][2 * h + 1]), qf[2 * u + h], sacc[beta], 0, 0,
-                  0);
+          for (int beta = 0; beta < 4; ++beta) {
+            const u32x4 lo4 = a[b & 1][0][beta];
+            const u32x4 hi4 = 2 * b + 1 < kU ? a[b & 1][1][beta] : u32x4{0u, 0u, 0u, 0u};
+            const i32x8 av = {(int)lo4[0], (int)lo4[1], (int)lo4[2], (int)lo4[3],
+                              (int)hi4[0], (int)hi4[1], (int)hi4[2], (int)hi4[3]};
+            sacc[beta] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, qh[b], sacc[beta], 0, 0, 0, 127, 0, 127);
+            sacc[beta] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, ql[b], sacc[beta], 0, 0, 0, 127, 0, 127);
+          }
         }
       }
       // ---- online softmax; lane holds head 16w + m16, tokens 16beta + 4grp + j
