@@ -329,8 +329,7 @@ __global__ __launch_bounds__(kNT) void mla_mfma_kernel(MlaParams p) {
           z[4 * beta + j] = zz;
           tmax = fmaxf(tmax, zz);
         }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      tmax = lanes4_max(tmax);
       // the running maximum moves when this tile exceeds it by more than 2^8 (or on the first
       // live tile, where the accumulator is still zero and needs no rescale)
       const bool first = m_run == -INFINITY && tmax > -INFINITY;
@@ -378,8 +377,7 @@ __global__ __launch_bounds__(kNT) void mla_mfma_kernel(MlaParams p) {
   }
 
   if (!active) return;
-  float l_tot = l_run + __shfl_xor(l_run, 16);
-  l_tot += __shfl_xor(l_tot, 32);
+  const float l_tot = lanes4_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   // lane holds O^T[d = 256kh + db*16 + grp*4 + j][head]
   if (p.n_split == 1) {
@@ -597,8 +595,7 @@ __global__ __launch_bounds__(kNT) void mla_fp8_kernel(MlaParams p) {
           z[4 * beta + j] = zz;
           tmax = fmaxf(tmax, zz);
         }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      tmax = lanes4_max(tmax);
       const bool first = m_run == -INFINITY && tmax > -INFINITY;
       const bool need = tmax > m_run + 8.f && !first;
       if (__any(need)) {
@@ -628,8 +625,7 @@ __global__ __launch_bounds__(kNT) void mla_fp8_kernel(MlaParams p) {
   }
 
   if (!active) return;
-  float l_tot = l_run + __shfl_xor(l_run, 16);
-  l_tot += __shfl_xor(l_tot, 32);
+  const float l_tot = lanes4_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   // lane holds O^T[d = 256kh + db*16 + grp*4 + j][head]
   if (p.n_split == 1) {
@@ -752,8 +748,7 @@ __global__ __launch_bounds__(kNTX) void mla_fp8x_kernel(MlaParams p) {
     for (int i = 0; i < kStepsX; ++i)
 #pragma unroll
       for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf((float)raw[i][e]));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = lanes4_max(mx);
     // exponent of mx (mx = f * 2^ex, f in [1, 2)): qs = 7 - ex puts mx in [128, 256)
     const int ex = mx > 0.f ? (int)((__float_as_uint(mx) >> 23) & 255u) - 127 : 7;
     const int qs = 7 - ex;
@@ -879,8 +874,7 @@ __global__ __launch_bounds__(kNTX) void mla_fp8x_kernel(MlaParams p) {
           tmax = fmaxf(tmax, zz);
         }
       }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      tmax = lanes4_max(tmax);
       const bool first = m_run == -INFINITY && tmax > -INFINITY;
       const bool need = tmax > m_run + 8.f && !first;
       float alpha = 1.f;
@@ -957,8 +951,7 @@ __global__ __launch_bounds__(kNTX) void mla_fp8x_kernel(MlaParams p) {
 
   // ---- final running max and sum per head, then each wave writes its 128 output values
   if (s_active) {
-    float l_tot = l_run + __shfl_xor(l_run, 16);
-    l_tot += __shfl_xor(l_tot, 32);
+    const float l_tot = lanes4_sum(l_run);
     if (grp == 0) {
       sm.fin_m[wave * 16 + m16] = m_run;
       sm.fin_l[wave * 16 + m16] = l_tot;
