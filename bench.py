@@ -342,8 +342,9 @@ def main():
                                scores, stream=stream)
         dsa.dsa_topk(batches[0], scores, k, idx_t, slots_t, workspace=topk_ws, stream=stream)
     torch.cuda.synchronize()
-    ns = args.n_split or dsa.lib().dsa_sparse_mla_default_split(B, Q, H, k)
-    mla_ws_bytes = dsa.mla_workspace_bytes(B, Q, H, k, ns, dsa.dtype_code(reps[0]["q_mla"]))
+    kvd = dsa.dtype_code(reps[0]["kv_cache"])
+    ns = args.n_split or dsa.lib().dsa_sparse_mla_default_split(B, Q, H, k, kvd)
+    mla_ws_bytes = dsa.mla_workspace_bytes(B, Q, H, k, ns, dsa.dtype_code(reps[0]["q_mla"]), kvd)
     mla_ws = torch.empty(max(1, mla_ws_bytes), dtype=torch.uint8, device=dev)
     KS = max(20, min(K, 1000))
     # slots per replica (so the MLA stage alone gathers rows of the replica's own pages)

@@ -73,8 +73,8 @@ def lib() -> ctypes.CDLL:
             "dsa_topk_workspace_size": (sz, [bp, i32]),
             "dsa_page_map": (e, [bp, vp, i32, vp, vp]),
             "dsa_sparse_mla_decode": (e, [i32, i32, vp, e, vp, e, vp, i64, vp, i32, i32, f32, vp, vp, i32, vp, sz, vp]),
-            "dsa_sparse_mla_workspace_size": (sz, [i32, i32, i32, i32, i32, e]),
-            "dsa_sparse_mla_default_split": (i32, [i32, i32, i32, i32]),
+            "dsa_sparse_mla_workspace_size": (sz, [i32, i32, i32, i32, i32, e, e]),
+            "dsa_sparse_mla_default_split": (i32, [i32, i32, i32, i32, e]),
             "dsa_mla_combine": (e, [i32, i32, i32, vp, vp, vp, vp, vp, vp]),
             "dsa_decode_step": (e, [ctypes.POINTER(DsaDecodeStepArgs), vp, sz, vp]),
             "dsa_decode_step_workspace_size": (sz, [ctypes.POINTER(DsaDecodeStepArgs)]),
@@ -172,8 +172,9 @@ def dsa_page_map(batch: DsaBatch, topk_idx: torch.Tensor, slots: torch.Tensor, s
     return slots
 
 
-def mla_workspace_bytes(batch: int, q_per_seq: int, n_heads: int, k: int, n_split: int, q_dtype: int) -> int:
-    return lib().dsa_sparse_mla_workspace_size(batch, q_per_seq, n_heads, k, n_split, q_dtype)
+def mla_workspace_bytes(batch: int, q_per_seq: int, n_heads: int, k: int, n_split: int, q_dtype: int,
+                        kv_dtype: int) -> int:
+    return lib().dsa_sparse_mla_workspace_size(batch, q_per_seq, n_heads, k, n_split, q_dtype, kv_dtype)
 
 
 def dsa_sparse_mla_decode(q: torch.Tensor, kv_cache: torch.Tensor, kv_scale: Optional[torch.Tensor],
@@ -183,7 +184,7 @@ def dsa_sparse_mla_decode(q: torch.Tensor, kv_cache: torch.Tensor, kv_scale: Opt
     """q [B,Q,H,576], kv_cache [slots,576], slots [B,Q,k] -> out [B,Q,H,512] (+ lse [B,Q,H])."""
     B, Q, H = q.shape[0], q.shape[1], q.shape[2]
     k = slots.shape[-1]
-    need = mla_workspace_bytes(B, Q, H, k, n_split, dtype_code(q))
+    need = mla_workspace_bytes(B, Q, H, k, n_split, dtype_code(q), dtype_code(kv_cache))
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     _check(lib().dsa_sparse_mla_decode(B, Q, _ptr(q), dtype_code(q), _ptr(kv_cache), dtype_code(kv_cache),

@@ -166,9 +166,10 @@ MlaWs mla_ws(int64_t rows, int32_t H, int32_t ns) {
   return w;
 }
 
-int32_t effective_split(int64_t rows, int32_t H, int32_t k, int32_t n_split, dsa_dtype_t q_dtype) {
+int32_t effective_split(int64_t rows, int32_t H, int32_t k, int32_t n_split, dsa_dtype_t q_dtype,
+                        dsa_dtype_t kv_dtype) {
   if (!mla_uses_mfma(q_dtype)) return 1;
-  int32_t ns = n_split > 0 ? n_split : mla_default_split((int)rows, H, k);
+  int32_t ns = n_split > 0 ? n_split : mla_default_split((int)rows, H, k, kv_dtype);
   // never more chunks than 32-row tiles
   const int32_t max_ns = (k + 31) / 32;
   return ns > max_ns ? max_ns : ns;
@@ -279,16 +280,17 @@ dsa_status_t dsa_page_map(const dsa_batch_t* b, const int32_t* topk_idx, int32_t
                   "page map");
 }
 
-int32_t dsa_sparse_mla_default_split(int32_t batch, int32_t q_per_seq, int32_t n_heads, int32_t k) {
+int32_t dsa_sparse_mla_default_split(int32_t batch, int32_t q_per_seq, int32_t n_heads, int32_t k,
+                                     dsa_dtype_t kv_dtype) {
   if (batch < 1 || q_per_seq < 1 || k < 1) return 1;
-  return effective_split((int64_t)batch * q_per_seq, n_heads, k, 0, DSA_BF16);
+  return effective_split((int64_t)batch * q_per_seq, n_heads, k, 0, DSA_BF16, kv_dtype);
 }
 
 size_t dsa_sparse_mla_workspace_size(int32_t batch, int32_t q_per_seq, int32_t n_heads, int32_t k, int32_t n_split,
-                                     dsa_dtype_t q_dtype) {
+                                     dsa_dtype_t q_dtype, dsa_dtype_t kv_dtype) {
   if (batch < 1 || q_per_seq < 1 || n_heads < 1 || k < 1) return 0;
   const int64_t rows = (int64_t)batch * q_per_seq;
-  return mla_ws(rows, n_heads, effective_split(rows, n_heads, k, n_split, q_dtype)).total;
+  return mla_ws(rows, n_heads, effective_split(rows, n_heads, k, n_split, q_dtype, kv_dtype)).total;
 }
 
 dsa_status_t dsa_sparse_mla_decode(int32_t batch, int32_t q_per_seq, const void* q, dsa_dtype_t q_dtype,
@@ -299,7 +301,7 @@ dsa_status_t dsa_sparse_mla_decode(int32_t batch, int32_t q_per_seq, const void*
   DSA_TRY(check_mla(batch, q_per_seq, q, q_dtype, kv_cache, kv_dtype, kv_scale, num_slots, slots, k, n_heads,
                     sm_scale, out, lse, n_split));
   const int64_t rows = (int64_t)batch * q_per_seq;
-  const int32_t ns = effective_split(rows, n_heads, k, n_split, q_dtype);
+  const int32_t ns = effective_split(rows, n_heads, k, n_split, q_dtype, kv_dtype);
   const MlaWs w = mla_ws(rows, n_heads, ns);
   if (workspace_bytes < w.total || (w.total > 0 && workspace == nullptr))
     return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "mla: workspace needs %zu bytes (got %zu)", w.total, workspace_bytes);
@@ -344,7 +346,7 @@ StepWs step_ws(const dsa_decode_step_args_t* a) {
   w.slots_off = off;
   if (!a->debug_slots) off += align_up((size_t)rows * a->top_k * sizeof(int32_t), 256);
   w.mla_off = off;
-  w.ns = effective_split(rows, a->mla_heads, a->top_k, a->n_split, a->q_mla_dtype);
+  w.ns = effective_split(rows, a->mla_heads, a->top_k, a->n_split, a->q_mla_dtype, a->kv_dtype);
   off += mla_ws(rows, a->mla_heads, w.ns).total;
   w.total = off;
   return w;

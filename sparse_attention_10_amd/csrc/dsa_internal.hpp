@@ -196,6 +196,6 @@ hipError_t launch_page_map(const int32_t* idx, int64_t total, int k, int Q, cons
                            int maxP, int P, int32_t* slots, hipStream_t s);
 hipError_t launch_mla(const MlaParams& p, dsa_dtype_t q_dtype, dsa_dtype_t kv_dtype, hipStream_t s);
 hipError_t launch_combine(const CombineParams& p, hipStream_t s);
-int mla_default_split(int rows, int H, int k);
+int mla_default_split(int rows, int H, int k, dsa_dtype_t kv_dtype);
 
 }  // namespace dsa

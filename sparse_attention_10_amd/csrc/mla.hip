@@ -1057,14 +1057,14 @@ __global__ __launch_bounds__(128) void mla_combine_kernel(CombineParams p) {
 
 }  // namespace
 
-int mla_default_split(int rows, int H, int k) {
+int mla_default_split(int rows, int H, int k, dsa_dtype_t kv_dtype) {
   (void)H;
-  // about one workgroup per compute unit, at least 64 selected rows per chunk, and at most
-  // kChunkX (the wide fp8 kernel's staging limit)
+  // about one workgroup per compute unit, at least 64 selected rows per chunk, and for fp8 rows
+  // at most kChunkX (the wide fp8 kernel's staging limit)
   int ns = 256 / (rows > 0 ? rows : 1);
   const int max_ns = (k + 63) / 64;
   if (ns > max_ns) ns = max_ns;
-  const int min_ns = (k + kChunkX - 1) / kChunkX;
+  const int min_ns = kv_dtype == DSA_FP8_E4M3FN ? (k + kChunkX - 1) / kChunkX : 1;
   if (ns < min_ns) ns = min_ns;
   if (ns < 1) ns = 1;
   return ns;
