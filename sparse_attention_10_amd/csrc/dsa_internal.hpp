@@ -137,8 +137,8 @@ struct IndexerParams {
   int64_t num_slots;      // rows of k_cache (and k_scale)
   int32_t B, Q, max_seq_len, P, maxP;
   int32_t Hi, Di;
-  int32_t tiles_per_wg;   // matrix-core path: 128-token tiles per workgroup
-  int32_t groups;         // matrix-core path: key ranges (workgroups per row group) per sequence
+  int32_t tiles_per_wg;   // matrix-core paths: key tiles (stages) per workgroup
+  int32_t groups;         // matrix-core paths: key ranges (workgroups per row group) per sequence
   int32_t p_shift;        // log2(P) when the page size is a power of two, else -1
 };
 

@@ -394,6 +394,186 @@ __global__ __launch_bounds__(kThreadsI) void indexer_mfma_kernel(IndexerParams p
     for (int qq = 0; qq < QB; ++qq) p.scores[((int64_t)b * p.Q + qb0 + qq) * p.ld + t] = -INFINITY;
 }
 
+
+// ---------------------------------------------------------------------------------------------
+// matrix-core path for many query rows per sequence (a chunked prefill): Hi = 64, Di = 128, bf16
+// q and keys, pages of a multiple of 32 tokens
+//
+// One workgroup = 16 query rows x one key range, 8 waves (two per SIMD): wave w scores the rows
+// 2w and 2w+1 (q of 2 rows x 64 heads in registers, 4 M-blocks of 32 heads) against every key
+// of the range.  Keys go HBM -> LDS by direct copies into a ring of 32-token stages (the decode
+// kernel's swizzled row layout) and each is read once per workgroup for all 16 rows: a key byte
+// feeds 16 x 64 flops, so the matrix cores bound the kernel, not the key stream (the keys of a
+// chunk are shared by all its workgroups and come from L2 or the Infinity Cache).  Per 32-token
+// sub-tile a wave reads its B fragments once and runs the 16 MFMAs of each of its rows; the two
+// waves of a SIMD cover each other's head reductions, copies and barrier waits.
+
+constexpr int kPfQB = 16;                        // query rows per workgroup
+constexpr int kPfWaves = 8;
+constexpr int kPfThreads = 64 * kPfWaves;
+constexpr int kPfQW = kPfQB / kPfWaves;          // rows per wave
+constexpr int kPfST = 32;                        // tokens per stage (one sub-tile: the registers of
+                                                 // two would not fit beside two rows of q)
+constexpr int kPfNB = 8;                         // ring stages
+constexpr int kPfSB = kPfST * 2 * kDi;           // stage bytes (8 KB)
+constexpr int kPfND = kPfSB / (kPfThreads * 16); // 16-byte copies per thread per stage
+constexpr int kPfMaxPages = 2048;                // page-table entries of one key range
+
+struct PfSmem {
+  uint8_t ring[kPfNB][kPfSB];
+  float w[kPfQB][kHi];
+  int32_t pt[kPfMaxPages];
+};
+
+__global__ __launch_bounds__(kPfThreads) void indexer_prefill_kernel(IndexerParams p) {
+  __shared__ __attribute__((aligned(16))) PfSmem sm;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // id = (b * ranges + range) * query blocks + query block
+  const int nqb = (p.Q + kPfQB - 1) / kPfQB;
+  const int qb = (int)blockIdx.x % nqb;
+  const int rest = (int)blockIdx.x / nqb;
+  const int kr = rest % p.groups, b = rest / p.groups;
+  const int L = min(p.seq_lens[b], p.max_seq_len);
+  const int q0 = qb * kPfQB;
+  const int nq = min(kPfQB, p.Q - q0);             // rows of this block
+  const int t_begin = kr * p.tiles_per_wg * kPfST;
+  const int t_end = min(L, t_begin + p.tiles_per_wg * kPfST);
+  if (t_begin >= t_end) return;                    // uniform
+  const int pos_last = L - p.Q + q0 + nq - 1;      // the block's largest position
+  const int t_stop = min(t_end, pos_last + 1);     // tokens at or past this are never scored
+  const int nstage = t_stop > t_begin ? (t_stop - t_begin + kPfST - 1) / kPfST : 0;
+  const int P = p.P;
+  const int page0 = t_begin / P;
+  const int npg = t_stop > t_begin ? (t_stop - 1) / P - page0 + 1 : 0;
+  const int32_t* ptab_g = p.page_table + (int64_t)b * p.maxP;
+  const __amdgpu_buffer_rsrc_t k_rs = rows_rsrc(p.k_cache, 2 * kDi, p.num_slots);
+  const int n_in_sub = lane & 31, half = lane >> 5;
+
+  // copy c of this thread fills LDS bytes ((c*8 + wave)*64 + lane)*16 of the stage: row r, slot
+  // q, from piece q ^ swz(r) of the row; a copy's 4 rows lie in one 32-token run of one page
+  int lane_row[kPfND], lane_boff[kPfND];
+#pragma unroll
+  for (int c = 0; c < kPfND; ++c) {
+    const int off = ((c * kPfWaves + wave) * 64 + lane) * 16;
+    const int r = off / (2 * kDi), q = (off % (2 * kDi)) / 16;
+    lane_row[c] = r;
+    lane_boff[c] = 16 * (q ^ swz<false>(r));
+  }
+  // page and in-page offset of copy c's run in the next stage to request, stepped by kPfST
+  // tokens per stage (P is a multiple of 32: at most two page steps)
+  int lk_pg[kPfND], lk_of[kPfND];
+#pragma unroll
+  for (int c = 0; c < kPfND; ++c) {
+    const int ts = t_begin + (lane_row[c] & ~(kSub - 1));
+    lk_pg[c] = ts / P;
+    lk_of[c] = ts - lk_pg[c] * P;
+  }
+  int lk_t0 = t_begin;                             // first token of the next stage to request
+  // copies of the next stage into `dst` (cache rows through pt_of), in stage order
+  auto issue = [&](uint8_t* __restrict__ dst, auto&& pt_of) {
+#pragma unroll
+    for (int c = 0; c < kPfND; ++c) {
+      const int ts = lk_t0 + (lane_row[c] & ~(kSub - 1));
+      // (runs past the scored tokens read row 0: valid, never scored)
+      const int s0 = ts < t_stop ? __builtin_amdgcn_readfirstlane(pt_of(lk_pg[c]) * P + lk_of[c]) : 0;
+      lds_dma16_row(k_rs, s0 + (lane_row[c] & (kSub - 1)), lane_boff[c],
+                    dst + ((c * kPfWaves + wave) * 64) * 16);
+      lk_of[c] += kPfST;
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        if (lk_of[c] >= P) {
+          lk_of[c] -= P;
+          ++lk_pg[c];
+        }
+    }
+    lk_t0 += kPfST;
+  };
+  auto pt_global = [&](int pg) { return ptab_g[pg]; };
+#pragma unroll
+  for (int v = 0; v < kPfNB - 1; ++v)
+    if (v < nstage) issue(sm.ring[v], pt_global);
+
+  // q of this wave's rows (clamped into the chunk; rows past it are computed, never stored):
+  // lane (head m of M-block mb, half h) holds dims h*64 + s*8 .. +8 for step s
+  bf16x8 afrag[kPfQW][2][8];
+#pragma unroll
+  for (int qi = 0; qi < kPfQW; ++qi) {
+    const int row = min(q0 + wave * kPfQW + qi, p.Q - 1);
+    const __bf16* qrow = (const __bf16*)p.q + ((int64_t)b * p.Q + row) * kHi * kDi;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        afrag[qi][mb][s] = *(const bf16x8*)(qrow + (mb * 32 + n_in_sub) * kDi + half * 64 + s * 8);
+  }
+  for (int e = threadIdx.x; e < kPfQB * kHi; e += kPfThreads) {
+    const int row = min(q0 + e / kHi, p.Q - 1);
+    (&sm.w[0][0])[e] = p.w[((int64_t)b * p.Q + row) * kHi + e % kHi];
+  }
+  for (int e = threadIdx.x; e < npg; e += kPfThreads) sm.pt[e] = ptab_g[page0 + e];
+  __syncthreads();
+
+  float* out_b = p.scores + ((int64_t)b * p.Q + q0) * p.ld;
+  // head reduction of row qi's 32 tokens (acc) at token t; weights from LDS
+  auto finish = [&](const PfSmem* __restrict__ rd, const f32x16 (&acc)[2], int qi, int t) {
+    const float* wrow = rd->w[wave * kPfQW + qi];
+    float part = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 wv = *(const f32x4*)&wrow[mb * 32 + g * 8 + half * 4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)   // ReLU as one integer max on the bits (negatives -> +0)
+          part = fmaf(wv[jj], __int_as_float(max(__float_as_int(acc[mb][4 * g + jj]), 0)), part);
+      }
+    // add the other lane half's partial sum (lanes l and l ^ 32 hold the same token)
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
+    part = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    const int ri = wave * kPfQW + qi;
+    const int pos = L - p.Q + q0 + ri;
+    if (half == 0 && ri < nq && t < t_end) out_b[(int64_t)ri * p.ld + t] = t <= pos ? part : -INFINITY;
+  };
+  // stage v: B fragments once, then each row's 16 MFMAs and reduction
+  auto compute = [&](const PfSmem* __restrict__ rd, int v) {
+    const uint8_t* stg = rd->ring[v % kPfNB];
+#pragma unroll
+    for (int j = 0; j < kPfST / kSub; ++j) {
+      const uint8_t* rows = stg + j * kSub * 2 * kDi;
+      bf16x8 kf[8];
+#pragma unroll
+      for (int s = 0; s < 8; ++s)               // dims h*64 + 8s .. +8 = piece 8h + s
+        kf[s] = *(const bf16x8*)(rows + n_in_sub * 2 * kDi + 16 * ((8 * half + s) ^ swz<false>(n_in_sub)));
+      const int t = t_begin + v * kPfST + j * kSub + n_in_sub;
+#pragma unroll
+      for (int qi = 0; qi < kPfQW; ++qi) {
+        f32x16 acc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+            acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag[qi][mb][s], kf[s], acc[mb], 0, 0, 0);
+        finish(rd, acc, qi, t);
+      }
+    }
+  };
+  auto pt_lds = [&](const PfSmem* __restrict__ rd) { return [rd, page0](int pg) { return rd->pt[pg - page0]; }; };
+  for (int v = 0; v < nstage; ++v) {
+    // stage v must have landed: at most the copies of the later stages requested so far
+    // (v+1 .. v+NB-2) may still be outstanding (vector-memory operations complete in order)
+    wait_vmcnt_later<kPfND, kPfNB - 2>(min(kPfNB - 2, nstage - 1 - v));
+    lds_barrier();   // stage v landed for every wave; stage v-1 is no longer read
+    if (v + kPfNB - 1 < nstage) issue(sm.ring[(v + kPfNB - 1) % kPfNB], pt_lds(&sm));
+    compute(&sm, v);
+  }
+  // tokens of [t_begin, t_end) past the block's last position: -inf (their stages are not
+  // computed)
+  const int t_tail = max(t_stop, t_begin), n_tail = t_end - t_tail;
+  for (int e = threadIdx.x; e < nq * n_tail; e += kPfThreads)
+    out_b[(int64_t)(e / n_tail) * p.ld + t_tail + e % n_tail] = -INFINITY;
+}
+
 }  // namespace
 
 bool indexer_uses_mfma(int Hi, int Di, dsa_dtype_t q_dtype, dsa_dtype_t k_dtype) {
@@ -402,6 +582,21 @@ bool indexer_uses_mfma(int Hi, int Di, dsa_dtype_t q_dtype, dsa_dtype_t k_dtype)
 
 hipError_t launch_indexer(const IndexerParams& p0, dsa_dtype_t q_dtype, dsa_dtype_t k_dtype, hipStream_t s) {
   IndexerParams p = p0;
+  if (indexer_uses_mfma(p.Hi, p.Di, q_dtype, k_dtype) && k_dtype == DSA_BF16 && p.Q >= kPfQB && p.P % kSub == 0) {
+    // many rows per sequence: blocks of 16 rows, key ranges so that about 256 workgroups run
+    // (and one range's page-table entries fit the LDS copy)
+    const int64_t nqb = (p.Q + kPfQB - 1) / kPfQB;
+    const int64_t stages = ((int64_t)p.max_seq_len + kPfST - 1) / kPfST;
+    int64_t ranges = (256 + nqb * p.B - 1) / (nqb * p.B);
+    const int64_t max_stages = (int64_t)(kPfMaxPages - 2) * p.P / kPfST;
+    if ((stages + ranges - 1) / ranges > max_stages) ranges = (stages + max_stages - 1) / max_stages;
+    if (ranges > stages) ranges = stages;
+    p.groups = (int32_t)ranges;
+    p.tiles_per_wg = (int32_t)((stages + ranges - 1) / ranges);
+    p.p_shift = (p.P & (p.P - 1)) == 0 ? __builtin_ctz((unsigned)p.P) : -1;
+    hipLaunchKernelGGL(indexer_prefill_kernel, dim3((unsigned)(nqb * ranges * p.B)), dim3(kPfThreads), 0, s, p);
+    return hipGetLastError();
+  }
   if (indexer_uses_mfma(p.Hi, p.Di, q_dtype, k_dtype)) {
     const int64_t tiles = ((int64_t)p.max_seq_len + kTile - 1) / kTile;
     // about one round of the 256 workgroups the GPU holds at once (one per CU): a workgroup's

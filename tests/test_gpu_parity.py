@@ -30,6 +30,11 @@ INDEXER_CASES = [
     ("c3", [4133, 300, 1, 8191, 2050], dict()),                       # ragged batch
     ("c5", [3000, 4097, 130], dict()),                                # fp8 keys, Q = 2
     ("c4", [64 + 1000], dict(q_per_seq=64)),                          # prefill-style causal block
+    # the prefill path (16 rows per workgroup): a partial last block over two sequences, one
+    # block over many key ranges, a page size that is not a power of two
+    ("c4", [37 + 2000, 37 + 500], dict(q_per_seq=37)),
+    ("c4", [16 + 70000], dict(q_per_seq=16)),
+    ("c4", [48 + 3000], dict(q_per_seq=48, page_size=96)),
     ("c2", [777, 65], dict(q_per_seq=3)),                             # odd Q (one row per block)
     ("c2", [900], dict(idx_heads=8, idx_dim=32)),                     # vector path, bf16
     ("c5", [700], dict(idx_heads=8, idx_dim=32, q_per_seq=1)),        # vector path, fp8
