@@ -491,7 +491,7 @@ __global__ __launch_bounds__(kPfThreads) void indexer_prefill_kernel(IndexerPara
   };
   auto pt_global = [&](int pg) { return ptab_g[pg]; };
 #pragma unroll
-  for (int v = 0; v < kPfNB - 1; ++v)
+  for (int v = 0; v < kPfNB - 2; ++v)
     if (v < nstage) issue(sm.ring[v], pt_global);
 
   // q of this wave's rows (clamped into the chunk; rows past it are computed, never stored):
@@ -559,13 +559,18 @@ __global__ __launch_bounds__(kPfThreads) void indexer_prefill_kernel(IndexerPara
     }
   };
   auto pt_lds = [&](const PfSmem* __restrict__ rd) { return [rd, page0](int pg) { return rd->pt[pg - page0]; }; };
-  for (int v = 0; v < nstage; ++v) {
-    // stage v must have landed: at most the copies of the later stages requested so far
-    // (v+1 .. v+NB-2) may still be outstanding (vector-memory operations complete in order)
-    wait_vmcnt_later<kPfND, kPfNB - 2>(min(kPfNB - 2, nstage - 1 - v));
-    lds_barrier();   // stage v landed for every wave; stage v-1 is no longer read
-    if (v + kPfNB - 1 < nstage) issue(sm.ring[(v + kPfNB - 1) % kPfNB], pt_lds(&sm));
+  // two stages per barrier: stages v and v+1 are computed while v+2 .. v+7 are in flight
+  for (int v = 0; v < nstage; v += 2) {
+    // stages v and v+1 must have landed: the copies of the later stages requested so far may
+    // still be outstanding (vector-memory operations complete in order)
+    wait_vmcnt_later<kPfND, kPfNB - 4>(min(v + kPfNB - 2, nstage) - min(v + 2, nstage));
+    lds_barrier();   // stages v, v+1 landed for every wave; stages v-2, v-1 are no longer read
+#pragma unroll
+    for (int u = kPfNB - 2; u < kPfNB; ++u)
+      if (v + u < nstage) issue(sm.ring[(v + u) % kPfNB], pt_lds(&sm));
     compute(&sm, v);
+    __builtin_amdgcn_sched_barrier(0);   // (keeps the two stages' registers apart)
+    if (v + 1 < nstage) compute(&sm, v + 1);
   }
   // tokens of [t_begin, t_end) past the block's last position: -inf (their stages are not
   // computed)
