@@ -414,7 +414,8 @@ constexpr int kPfThreads = 64 * kPfWaves;
 constexpr int kPfQW = kPfQB / kPfWaves;          // rows per wave
 constexpr int kPfST = 32;                        // tokens per stage (one sub-tile: the registers of
                                                  // two would not fit beside two rows of q)
-constexpr int kPfNB = 8;                         // ring stages
+constexpr int kPfSPB = 4;                        // stages computed per barrier
+constexpr int kPfNB = 3 * kPfSPB;                // ring stages
 constexpr int kPfSB = kPfST * 2 * kDi;           // stage bytes (8 KB)
 constexpr int kPfND = kPfSB / (kPfThreads * 16); // 16-byte copies per thread per stage
 constexpr int kPfMaxPages = 2048;                // page-table entries of one key range
@@ -491,7 +492,7 @@ __global__ __launch_bounds__(kPfThreads) void indexer_prefill_kernel(IndexerPara
   };
   auto pt_global = [&](int pg) { return ptab_g[pg]; };
 #pragma unroll
-  for (int v = 0; v < kPfNB - 2; ++v)
+  for (int v = 0; v < kPfNB - kPfSPB; ++v)
     if (v < nstage) issue(sm.ring[v], pt_global);
 
   // q of this wave's rows (clamped into the chunk; rows past it are computed, never stored):
@@ -559,18 +560,20 @@ __global__ __launch_bounds__(kPfThreads) void indexer_prefill_kernel(IndexerPara
     }
   };
   auto pt_lds = [&](const PfSmem* __restrict__ rd) { return [rd, page0](int pg) { return rd->pt[pg - page0]; }; };
-  // two stages per barrier: stages v and v+1 are computed while v+2 .. v+7 are in flight
-  for (int v = 0; v < nstage; v += 2) {
-    // stages v and v+1 must have landed: the copies of the later stages requested so far may
-    // still be outstanding (vector-memory operations complete in order)
-    wait_vmcnt_later<kPfND, kPfNB - 4>(min(v + kPfNB - 2, nstage) - min(v + 2, nstage));
-    lds_barrier();   // stages v, v+1 landed for every wave; stages v-2, v-1 are no longer read
+  // kPfSPB stages per barrier, computed while the next 2 kPfSPB are in flight
+  for (int v = 0; v < nstage; v += kPfSPB) {
+    // stages v .. v+SPB-1 must have landed: the copies of the later stages requested so far
+    // may still be outstanding (vector-memory operations complete in order)
+    wait_vmcnt_later<kPfND, kPfNB - 2 * kPfSPB>(min(v + kPfNB - kPfSPB, nstage) - min(v + kPfSPB, nstage));
+    lds_barrier();   // those stages landed for every wave; the previous ones are no longer read
 #pragma unroll
-    for (int u = kPfNB - 2; u < kPfNB; ++u)
+    for (int u = kPfNB - kPfSPB; u < kPfNB; ++u)
       if (v + u < nstage) issue(sm.ring[(v + u) % kPfNB], pt_lds(&sm));
-    compute(&sm, v);
-    __builtin_amdgcn_sched_barrier(0);   // (keeps the two stages' registers apart)
-    if (v + 1 < nstage) compute(&sm, v + 1);
+#pragma unroll
+    for (int u = 0; u < kPfSPB; ++u) {
+      if (v + u < nstage) compute(&sm, v + u);
+      __builtin_amdgcn_sched_barrier(0);   // (keeps the stages' registers apart)
+    }
   }
   // tokens of [t_begin, t_end) past the block's last position: -inf (their stages are not
   // computed)
