@@ -398,7 +398,10 @@ def main():
     # fp8 rows run on the wide-tile kernel when a split chunk holds at most 1024 rows
     mla_kern = ("mla_mfma_kernel" if cfg.kv_dtype != "fp8" else
                 "mla_fp8x_kernel" if -(-(-(-k // ns)) // 32) * 32 <= 1024 else "mla_fp8_kernel")
-    kern = {"indexer": "indexer_mfma_kernel", "mla": mla_kern, "topk": "topk_kernel",
+    # many rows per sequence with bf16 keys run on the prefill indexer (16 rows per workgroup)
+    idx_kern = ("indexer_prefill_kernel" if Q >= 16 and cfg.key_dtype == "bf16" and cfg.page_size % 32 == 0
+                else "indexer_mfma_kernel")
+    kern = {"indexer": idx_kern, "mla": mla_kern, "topk": "topk_kernel",
             "combine": "mla_combine_kernel"}[dom]
     if cfg.name == "c4" and dom in ("indexer", "mla"):
         ach = stage_info[dom]["flops"] / (stage_info[dom]["us"] * 1e-6) / 1e12
