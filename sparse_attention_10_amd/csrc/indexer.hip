@@ -146,24 +146,8 @@ __global__ __launch_bounds__(kThreadsI) void indexer_mfma_kernel(IndexerParams p
   const int b = kr / p.groups;
   const int grp_id = kr - b * p.groups;
   const int qb0 = (rem >> 3) * QB;            // first query row of the block
-  const int L = min(p.seq_lens[b], p.max_seq_len);
   const int tile_base = grp_id * p.tiles_per_wg * kTile;
-  if (tile_base >= L) return;                 // uniform early exit
-  const int tile_end = min(L, tile_base + p.tiles_per_wg * kTile);
-  const int pos_last = L - p.Q + qb0 + QB - 1;  // the block's largest position
-  const int t_stop = min(tile_end, pos_last + 1);  // tokens at or past this are never scored
-  const int nstage = t_stop > tile_base ? (t_stop - tile_base + G::ST - 1) / G::ST : 0;
-
-  const int ri = wave / G::WPR;               // the row this wave scores
-  const int si = wave - ri * G::WPR;          // its first sub-tile within a stage is si * SPW
-  const int pos = L - p.Q + qb0 + ri;         // that row sees tokens t <= pos
-  const int n_in_sub = lane & 31;
-  const int half = lane >> 5;
-  const int page0 = tile_base / p.P;
-  const int npg = (t_stop > tile_base) ? (t_stop - 1) / p.P - page0 + 1 : 0;
   const int32_t* ptab_g = p.page_table + (int64_t)b * p.maxP;
-  const __amdgpu_buffer_rsrc_t k_rs = rows_rsrc(p.k_cache, G::RB, p.num_slots);
-  const __amdgpu_buffer_rsrc_t s_rs = rows_rsrc(FP8 ? (const void*)p.k_scale : p.k_cache, 4, FP8 ? p.num_slots : 0);
 
   // Stage v covers tokens tile_base + v*ST ..; this thread's load c fills LDS bytes
   // [off, off+16) of the stage, off = ((c*8 + wave)*64 + lane)*16: row r = off / RB and slot
@@ -178,29 +162,48 @@ __global__ __launch_bounds__(kThreadsI) void indexer_mfma_kernel(IndexerParams p
     lane_boff[c] = 16 * (q ^ swz<FP8>(r));
   }
   const bool scale_wave = FP8 && wave < G::NSW;
+  // token whose cache row copy c (c = ND: the scale copy) of stage v starts at
+  auto tok = [&](int v, int c) {
+    const int t0 = tile_base + v * G::ST;
+    if (c == G::ND) return t0 + wave * 64 + lane;
+    return CONTIG ? t0 + (lane_row[c] & ~(kSub - 1)) : t0 + lane_row[c];
+  };
+  constexpr int NL = G::ND + (FP8 ? 1 : 0);
+  // the page-table entries of the first NB-1 stages are requested before the sequence length
+  // arrives (bounded by max_seq_len alone), so the first copies wait one round trip less
+  int32_t pre_pe[NB - 1][NL];
+  {
+    const int t_cap = min(tile_base + p.tiles_per_wg * kTile, p.max_seq_len);
+#pragma unroll
+    for (int v = 0; v < NB - 1; ++v)
+#pragma unroll
+      for (int c = 0; c < NL; ++c) {
+        const int t = tok(v, c);
+        pre_pe[v][c] = t < t_cap && (c < G::ND || scale_wave) ? ptab_g[t / p.P] : 0;
+      }
+  }
+  const int L = min(p.seq_lens[b], p.max_seq_len);
+  if (tile_base >= L) return;                 // uniform early exit
+  const int tile_end = min(L, tile_base + p.tiles_per_wg * kTile);
+  const int pos_last = L - p.Q + qb0 + QB - 1;  // the block's largest position
+  const int t_stop = min(tile_end, pos_last + 1);  // tokens at or past this are never scored
+  const int nstage = t_stop > tile_base ? (t_stop - tile_base + G::ST - 1) / G::ST : 0;
+
+  const int ri = wave / G::WPR;               // the row this wave scores
+  const int si = wave - ri * G::WPR;          // its first sub-tile within a stage is si * SPW
+  const int pos = L - p.Q + qb0 + ri;         // that row sees tokens t <= pos
+  const int n_in_sub = lane & 31;
+  const int half = lane >> 5;
+  const int page0 = tile_base / p.P;
+  const int npg = (t_stop > tile_base) ? (t_stop - 1) / p.P - page0 + 1 : 0;
+  const __amdgpu_buffer_rsrc_t k_rs = rows_rsrc(p.k_cache, G::RB, p.num_slots);
+  const __amdgpu_buffer_rsrc_t s_rs = rows_rsrc(FP8 ? (const void*)p.k_scale : p.k_cache, 4, FP8 ? p.num_slots : 0);
+
   // Cache rows of this lane's copies of one stage: copy c fetches row slot[c] (CONTIG: the first
   // row of the copy's 32-token run, which the lane offsets by r % 32), the scale copy row sslot.
   struct Rows {
     int32_t slot[G::ND];
     int32_t sslot;
-  };
-  auto rows_of = [&](int v, auto&& slot_of) {
-    Rows rw;
-    const int t0 = tile_base + v * G::ST;
-#pragma unroll
-    for (int c = 0; c < G::ND; ++c) {
-      // CONTIG: the run t0 + (r & ~31) .. +31 lies in one page; rows past the sequence are
-      // still allocated cache rows (their scores are never written).  Tokens at or past t_stop
-      // read row 0 (valid) and are never scored.
-      const int t = CONTIG ? t0 + (lane_row[c] & ~(kSub - 1)) : t0 + lane_row[c];
-      rw.slot[c] = t < t_stop ? (int32_t)slot_of(t) : 0;
-    }
-    rw.sslot = 0;
-    if constexpr (FP8) {
-      const int t = t0 + wave * 64 + lane;
-      rw.sslot = scale_wave && t < t_stop ? (int32_t)slot_of(t) : 0;
-    }
-    return rw;
   };
   // copies of one stage into ring stage `dst` (keys, then the scales behind them)
   auto issue = [&](uint8_t* __restrict__ dst, const Rows& rw) {
@@ -214,12 +217,24 @@ __global__ __launch_bounds__(kThreadsI) void indexer_mfma_kernel(IndexerParams p
       if (scale_wave) lds_dma4_row(s_rs, (int)rw.sslot, dst + G::SB + wave * 256);
     }
   };
-  // the first NB-1 stages are requested before q is staged, from page-table entries read
-  // straight from global memory
-  auto slot_global = [&](int t) { return (int64_t)ptab_g[t / p.P] * p.P + t % p.P; };
+  // the first NB-1 stages are requested before q is staged, from the prefetched page-table
+  // entries
 #pragma unroll
   for (int v = 0; v < NB - 1; ++v)
-    if (v < nstage) issue(sm.ring[v], rows_of(v, slot_global));
+    if (v < nstage) {
+      Rows rw;
+#pragma unroll
+      for (int c = 0; c < G::ND; ++c) {
+        const int t = tok(v, c);
+        rw.slot[c] = t < t_stop ? pre_pe[v][c] * p.P + t % p.P : 0;
+      }
+      rw.sslot = 0;
+      if constexpr (FP8) {
+        const int t = tok(v, G::ND);
+        rw.sslot = scale_wave && t < t_stop ? pre_pe[v][G::ND] * p.P + t % p.P : 0;
+      }
+      issue(sm.ring[v], rw);
+    }
 
   // stage q (bf16), w and the page-table entries of this workgroup's tokens
   {
@@ -269,12 +284,6 @@ __global__ __launch_bounds__(kThreadsI) void indexer_mfma_kernel(IndexerParams p
   // from LDS are long done when the copies are issued.  Copy c (c < ND: keys, c = ND: scales)
   // of stage v starts at token tok(v, c); (lk_pg, lk_of) = its page and offset in that page for
   // the stage to look up next, stepped by ST tokens per stage (no division in the loop).
-  auto tok = [&](int v, int c) {
-    const int t0 = tile_base + v * G::ST;
-    if (c == G::ND) return t0 + wave * 64 + lane;
-    return CONTIG ? t0 + (lane_row[c] & ~(kSub - 1)) : t0 + lane_row[c];
-  };
-  constexpr int NL = G::ND + (FP8 ? 1 : 0);
   int lk_pg[NL], lk_of[NL];
 #pragma unroll
   for (int c = 0; c < NL; ++c) {

@@ -250,6 +250,20 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkParams p) {
   int32_t* idx_out = MODE == 1 ? nullptr : p.idx + (int64_t)row * k;
   int32_t* slot_out = MODE != 1 && p.slots ? p.slots + (int64_t)row * k : nullptr;
 
+  // The register block is requested before the row's length arrives: the loads need only the
+  // row's extent in memory, and columns past the row are masked when the keys are formed.
+  constexpr int kRegRows = RV * kWaves;              // key rows held in registers
+  const int64_t ext = MODE == 2 ? p.cand_ld : MODE == 1 ? min((int64_t)p.chunk_len, p.ld - c0) : p.ld;
+  float x[RV];
+  if (((int64_t)kRegRows << 6) <= ext) {
+    const float* wrow = srow + ((wave * RV) << 6);   // uniform base, lane offset, constant row offsets
+#pragma unroll
+    for (int j = 0; j < RV; ++j) x[j] = wrow[(j << 6) + lane];
+  } else {
+#pragma unroll
+    for (int j = 0; j < RV; ++j) x[j] = srow[min(((wave * RV + j) << 6) + lane, (int)ext - 1)];
+  }
+
   if constexpr (MODE == 1) {
     if (n <= k) {   // the whole chunk is kept
       for (int j = tid; j < n; j += kThreads) {
@@ -270,7 +284,6 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkParams p) {
   }
 
   // ---- pass 1: keys (registers), page-table row (registers), first-digit histogram
-  constexpr int kRegRows = RV * kWaves;              // key rows held in registers
   const int nrows = (n + 63) >> 6;
   const int nseg = nrows > kRegRows ? (nrows - kRegRows + kTailRows * kWaves - 1) / (kTailRows * kWaves) : 0;
   const int npages = (n_row + p.P - 1) / p.P;       // pages of the row's visible columns
@@ -283,15 +296,6 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkParams p) {
   const bool reg_full = (kRegRows << 6) <= n;
   uint32_t key[RV];
   {
-    float x[RV];
-    if (reg_full) {
-      const float* wrow = srow + ((wave * RV) << 6);   // uniform base, lane offset, constant row offsets
-#pragma unroll
-      for (int j = 0; j < RV; ++j) x[j] = wrow[(j << 6) + lane];
-    } else {
-#pragma unroll
-      for (int j = 0; j < RV; ++j) x[j] = srow[min(((wave * RV + j) << 6) + lane, n - 1)];
-    }
     // the histogram is cleared while the loads are in flight
     u32x4* l4 = (u32x4*)big;
     const u32x4 z = {0u, 0u, 0u, 0u};
