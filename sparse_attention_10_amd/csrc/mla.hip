@@ -728,6 +728,11 @@ __global__ __launch_bounds__(kNTX) void mla_fp8x_kernel(MlaParams p) {
     }
   };
 
+  // the first kRingX-1 tiles are requested before q is loaded and split, so their copies are
+  // in flight meanwhile
+#pragma unroll
+  for (int v = 0; v < kRingX - 1; ++v)
+    if (v < ntiles) issue(&sm, sm.ring[v], v);
   // q of this wave's S^T head group (head 16w + m16) as two e4m3 parts: scaled by 2^qs so that
   // its largest magnitude lies in [128, 256), hi = e4m3(q 2^qs) and lo = e4m3(q 2^qs - hi), so
   // hi + lo = q 2^qs exactly for every element down to 2^-18 of the largest (e4m3 holds 4
@@ -772,9 +777,6 @@ __global__ __launch_bounds__(kNTX) void mla_fp8x_kernel(MlaParams p) {
         ql[b][word] = lw;
       }
   }
-#pragma unroll
-  for (int v = 0; v < kRingX - 1; ++v)
-    if (v < ntiles) issue(&sm, sm.ring[v], v);
   if (!s_active) {   // head groups past the head count: P = 0, no rescale, for every tile
     sm.pex[wave][0][lane] = bf16x8{};
     sm.pex[wave][1][lane] = bf16x8{};
