@@ -99,14 +99,21 @@ template <bool FP8, int QB>
 struct Geo {
   static constexpr int RB = FP8 ? kDi : 2 * kDi;       // key row bytes
   static constexpr int WPR = kWaves / QB;              // waves per query row
+  // one row: the two waves of a sub-tile take 32 heads each (HS = 2) and add their head sums
+  // through LDS, so a stage is 128 tokens and the ring holds four; two rows: a wave takes all
+  // 64 heads of its sub-tiles
+  static constexpr int HS = QB == 1 ? 2 : 1;           // waves per sub-tile (head halves)
+  static constexpr int MBW = 2 / HS;                   // 32-head M-blocks per wave
+  static constexpr int SPS = WPR / HS;                 // sub-tile slots per stage
   // sub-tiles per wave and stage: two for fp8 keys and two rows, so that a stage (and the
-  // barrier that closes it) covers 256 tokens as in the other layouts
+  // barrier that closes it) covers 256 tokens
   static constexpr int SPW = (FP8 && QB == 2) ? 2 : 1;
-  static constexpr int ST = kSub * WPR * SPW;          // tokens per stage
+  static constexpr int ST = kSub * SPS * SPW;          // tokens per stage
   static constexpr int SB = ST * RB;                   // stage bytes
   static constexpr int ND = SB / (kThreadsI * 16);     // 16-byte loads per thread per stage
-  static constexpr int NB = FP8 ? 3 : (QB == 2 ? 3 : 2);   // ring depth (stages of 32 / 64 KB)
+  static constexpr int NB = QB == 1 ? 4 : 3;           // ring depth (stages of 16 / 32 KB)
   static constexpr int NSW = FP8 ? ST / 64 : 0;        // waves that also load the stage's scales
+  static_assert(HS == 1 || SPW == 1, "a head-split wave keeps one pending head sum per stage");
 };
 template <bool FP8>
 __device__ __forceinline__ int swz(int r) { return FP8 ? ((r >> 1) & 7) : (r & 15); }
@@ -118,6 +125,7 @@ struct ISmem {
   __bf16 q[QB][kHi][kDi];
   float w[QB][kHi];
   int32_t pt[kMaxWgPages];
+  float xs[2][4][kSub];    // one row: head sums of heads 32..63, by stage parity and sub-tile
 };
 
 
@@ -190,7 +198,9 @@ __global__ __launch_bounds__(kThreadsI) void indexer_mfma_kernel(IndexerParams p
   const int nstage = t_stop > tile_base ? (t_stop - tile_base + G::ST - 1) / G::ST : 0;
 
   const int ri = wave / G::WPR;               // the row this wave scores
-  const int si = wave - ri * G::WPR;          // its first sub-tile within a stage is si * SPW
+  const int wl = wave - ri * G::WPR;
+  const int si = wl % G::SPS;                 // its first sub-tile within a stage is si * SPW
+  const int mh = wl / G::SPS;                 // its head half (one row), else 0
   const int pos = L - p.Q + qb0 + ri;         // that row sees tokens t <= pos
   const int n_in_sub = lane & 31;
   const int half = lane >> 5;
@@ -262,18 +272,20 @@ __global__ __launch_bounds__(kThreadsI) void indexer_mfma_kernel(IndexerParams p
 
   // A fragments of this wave's row: lane (head m = lane%32 of M-block mb, half h) holds, for
   // k-step s, q dims [h*64 + s*8, +8) (the contraction index is permuted the same way for keys)
-  bf16x8 afrag[2][8];
+  // (this wave's M-blocks: mh*MBW .. +MBW)
+  bf16x8 afrag[G::MBW][8];
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
+  for (int mb = 0; mb < G::MBW; ++mb)
 #pragma unroll
     for (int s = 0; s < 8; ++s)
-      afrag[mb][s] = *(const bf16x8*)&sm.q[ri][mb * 32 + n_in_sub][half * 64 + s * 8];
-  float wr[2][4][4];   // head weights of the heads this lane holds: m = mb*32 + g*8 + half*4 + j
+      afrag[mb][s] = *(const bf16x8*)&sm.q[ri][(mh * G::MBW + mb) * 32 + n_in_sub][half * 64 + s * 8];
+  // head weights of the heads this lane holds: m = (mh*MBW + mb)*32 + g*8 + half*4 + j
+  float wr[G::MBW][4][4];
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
+  for (int mb = 0; mb < G::MBW; ++mb)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const f32x4 wv = *(const f32x4*)&sm.w[ri][mb * 32 + g * 8 + half * 4];
+      const f32x4 wv = *(const f32x4*)&sm.w[ri][(mh * G::MBW + mb) * 32 + g * 8 + half * 4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) wr[mb][g][j] = wv[j];
     }
@@ -318,13 +330,26 @@ __global__ __launch_bounds__(kThreadsI) void indexer_mfma_kernel(IndexerParams p
   // The head reduction of a sub-tile runs one stage late: the MFMAs of stage v are issued next
   // to the ReLU / weight / head-sum work of stage v-1, so the matrix core and the vector ALU
   // overlap.  (acc_prev, t_prev, ks_prev) = stage v-1's accumulators, lane token and scale.
-  f32x16 acc_prev[2] = {f32x16{}, f32x16{}};
-  int t_prev = -1;
+  f32x16 acc_prev[G::MBW];
+#pragma unroll
+  for (int mb = 0; mb < G::MBW; ++mb) acc_prev[mb] = f32x16{};
+  int t_prev = -1, par_prev = 0;
   float ks_prev = 0.f;
-  auto finish = [&](const f32x16 (&acc)[2], int t, float ks) {
+  // one row (HS = 2): the head half 0 waves keep the head sum of heads 0..31 of stage u (pend_*)
+  // until, after the next barrier, the half 1 waves' sum of heads 32..63 is in xs[u & 1]
+  float pend_part = 0.f, pend_ks = 0.f;
+  int pend_t = -1, pend_par = 0;
+  auto store = [&](int t, float part, float ks) {
+    if (half == 0 && t >= 0 && t < tile_end) out[t] = t <= pos ? part * ks : -INFINITY;
+  };
+  auto complete = [&](const Smem* __restrict__ rd) {   // (HS = 2, head half 0)
+    if (pend_t >= 0) store(pend_t, pend_part + rd->xs[pend_par][si][n_in_sub], pend_ks);
+    pend_t = -1;
+  };
+  auto finish = [&](Smem* __restrict__ rd, const f32x16 (&acc)[G::MBW], int t, float ks, int par) {
     float part = 0.f;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < G::MBW; ++mb)
 #pragma unroll
       for (int g = 0; g < 4; ++g)
 #pragma unroll
@@ -333,14 +358,28 @@ __global__ __launch_bounds__(kThreadsI) void indexer_mfma_kernel(IndexerParams p
     // add the other lane half's partial sum (lanes l and l ^ 32 hold the same token)
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
     part = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-    if (half == 0 && t >= 0 && t < tile_end) out[t] = t <= pos ? part * ks : -INFINITY;
+    if constexpr (G::HS == 1) {
+      store(t, part, ks);
+    } else if (t >= 0) {
+      if (mh == 1) {
+        if (half == 0) rd->xs[par][si][n_in_sub] = part;
+      } else {
+        pend_part = part;
+        pend_ks = ks;
+        pend_t = t;
+        pend_par = par;
+      }
+    }
   };
 
   // one stage: request stage v + NB - 1 into ring stage `dst` and look up the rows of stage
   // v + NB; per sub-tile of this wave in stage v: B fragments (lane: token n, half h) from LDS,
   // 32x32x16 MFMAs over the two 32-head M-blocks, then the head reduction of the sub-tile
   // before it
-  auto compute = [&](const Smem* __restrict__ rd, int v) {
+  auto compute = [&](Smem* __restrict__ rd, int v) {
+    if constexpr (G::HS == 2) {
+      if (mh == 0) complete(rd);   // stage v-2's sum: its other half was written before the barrier
+    }
 #pragma unroll
     for (int j = 0; j < G::SPW; ++j) {
       const int sub = si * G::SPW + j;
@@ -368,17 +407,20 @@ __global__ __launch_bounds__(kThreadsI) void indexer_mfma_kernel(IndexerParams p
       const float ks = FP8 ? ((const float*)(&rd->ring[v % NB][G::SB]))[sub * kSub + n_in_sub] : 1.f;
       // (sub-tiles wholly past the row's position are computed too, on valid rows, and written
       // as -inf by the reduction)
-      f32x16 acc[2] = {f32x16{}, f32x16{}};
+      f32x16 acc[G::MBW];
+#pragma unroll
+      for (int mb = 0; mb < G::MBW; ++mb) acc[mb] = f32x16{};
 #pragma unroll
       for (int s = 0; s < 8; ++s)
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+        for (int mb = 0; mb < G::MBW; ++mb)
           acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag[mb][s], kf[s], acc[mb], 0, 0, 0);
-      finish(acc_prev, t_prev, ks_prev);
-      acc_prev[0] = acc[0];
-      acc_prev[1] = acc[1];
+      finish(rd, acc_prev, t_prev, ks_prev, par_prev);
+#pragma unroll
+      for (int mb = 0; mb < G::MBW; ++mb) acc_prev[mb] = acc[mb];
       t_prev = t;
       ks_prev = ks;
+      par_prev = v & 1;
     }
   };
 
@@ -395,7 +437,16 @@ __global__ __launch_bounds__(kThreadsI) void indexer_mfma_kernel(IndexerParams p
     }
     compute(&sm, v);
   }
-  finish(acc_prev, t_prev, ks_prev);
+  if constexpr (G::HS == 2) {
+    // stage nstage-2's other half was written in the last iteration; stage nstage-1's now
+    lds_barrier();
+    if (mh == 0) complete(&sm);
+    finish(&sm, acc_prev, t_prev, ks_prev, par_prev);
+    lds_barrier();
+    if (mh == 0) complete(&sm);
+  } else {
+    finish(&sm, acc_prev, t_prev, ks_prev, par_prev);
+  }
   // tokens of [tile_base, tile_end) past the block's last position: -inf (their stages are not
   // computed)
   for (int t = max(t_stop, tile_base) + (int)threadIdx.x; t < tile_end; t += kThreadsI)
