@@ -3,23 +3,32 @@
 // 512 values, weight-absorbed and without GQA (Show HN "Chay GLM 5.2 tren may tinh cham",
 // main-features section).
 //
-// mla_mfma_kernel: one workgroup = 8 waves = one query row x one chunk of its selected slots
-// (split-k).  A pair of waves owns 16 heads, one wave per half of the K dims (S^T) and of the
-// output dims (P.V).  Per 32-token tile:
+// Kernels (bf16 q; the launcher picks one by row type and chunk length):
+//   mla_bf16d_kernel  bf16 rows, chunks <= 2048: 8 waves, 32-token tiles copied HBM -> LDS into
+//                     a 4-deep ring, S^T per (head group, 16-token block), P.V per 64 output
+//                     values over all heads, softmax against a fixed per-head reference.
+//   mla_fp8x_kernel   fp8 rows, chunks <= 1024: 4 waves, 64-token tiles, S^T on the e4m3 matrix
+//                     core with q split into two e4m3 parts, the same fixed-reference softmax.
+//   mla_fp8_kernel    fp8 rows, longer chunks: 8 waves, online softmax with lazy rescaling.
+//   mla_mfma_kernel   bf16 rows, longer chunks: 8 waves, rows staged through registers.
+// Common to all: S^T = rows . q^T and O^T += V^T . P^T on the bf16 (or e4m3) MFMAs in fp32,
+// exp2 with log2 e folded into the scale, V^T operands read with the transposing LDS reads,
+// the fp8 per-token scale folded into the logits and into P.  With n_split > 1 each chunk
+// writes (m, l, o/l) partials and mla_combine_kernel merges them in a fixed order.
+// mla_valu_kernel is the f32 path (any head count), one workgroup per (row, head).
+//
+// mla_mfma_kernel in detail: one workgroup = 8 waves = one query row x one chunk of its selected
+// slots (split-k).  A pair of waves owns 16 heads, one wave per half of the K dims (S^T) and of
+// the output dims (P.V).  Per 32-token tile:
 //   * the tile's rows are gathered from HBM (16-byte loads, one row = 72 of them; fp8 rows are
 //     widened to bf16 in registers) into LDS, double-buffered, with the next two tiles' loads
 //     in flight while this one is computed;
-//   * S^T = rows . q^T on v_mfma_f32_16x16x32_bf16 (M = 16 tokens, N = 16 heads, K = 576 in 18
-//     steps, q held in registers).  The two 16-token blocks are chosen so that each lane ends
-//     up with 8 consecutive tokens of one head, exactly the K slice the P.V product needs;
-//   * online softmax in fp32 with exp2 (log2 e folded into the scale) and lazy rescaling: the
-//     running maximum moves only when a tile exceeds it by more than 2^8, so the 512-value
-//     accumulator is rarely touched;
-//   * O^T += V^T . P^T on the same MFMA with M = 16 latent dims, N = 16 heads, K = 32 tokens;
-//     the V^T operand comes from LDS with ds_read_b64_tr_b16 (a transposing LDS read), P from
-//     registers as bf16 (the fp8 per-token scale is folded into P and into the logits).
-// With n_split > 1 each chunk writes (m, l, o/l) partials and mla_combine_kernel merges them in
-// a fixed order.  mla_valu_kernel is the f32 path (any head count), one workgroup per (row, head).
+//   * S^T on v_mfma_f32_16x16x32_bf16 (M = 16 tokens, N = 16 heads, K = 576 in 18 steps, q held
+//     in registers).  The two 16-token blocks are chosen so that each lane ends up with 8
+//     consecutive tokens of one head, exactly the K slice the P.V product needs;
+//   * online softmax with lazy rescaling: the running maximum moves only when a tile exceeds it
+//     by more than 2^8, so the 512-value accumulator is rarely touched;
+//   * O^T += V^T . P^T with M = 16 latent dims, N = 16 heads, K = 32 tokens, P from registers.
 #include "dsa_internal.hpp"
 
 namespace dsa {
@@ -27,6 +36,7 @@ namespace dsa {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kRefMargin = 64.f;   // log2 of the largest P relative to the softmax reference R
 
 // Four f32 values as e4m3 pairs (round to nearest even): hw = e4m3(f), lw = e4m3(f - hw), byte
 // j of each word for value j.
@@ -652,9 +662,13 @@ __global__ __launch_bounds__(kNT) void mla_fp8_kernel(MlaParams p) {
 //   * Tiles are copied HBM -> LDS directly (36 copies of 1 KiB per tile, 9 per wave, whole rows
 //     per copy, through a buffer resource) into a ring of kRingX slots, kRingX-1 tiles in flight;
 //     layout as in mla_fp8_kernel (row t at t*576, piece p in slot p ^ fp8_swz(t)).
-//   * S^T and the online softmax: wave w owns the 16 heads 16w .. 16w+15 over all 64 tokens and
-//     the full K (q in registers); it publishes P (bf16, in the P.V operand layout) and the
-//     tile's per-head rescale factor through LDS.
+//   * S^T and the softmax: wave w owns the 16 heads 16w .. 16w+15 over all 64 tokens and the
+//     full K (q in registers); it publishes P (bf16, in the P.V operand layout) through LDS.
+//     P = exp2(z - R) with a fixed reference per head, the largest logit of the head's first
+//     tile with a live token, so that the accumulators are only ever touched by the matrix core
+//     (no rescaling, no copies out of the accumulator registers).  P and the sums stay finite
+//     while every logit is below R + 64 (log2 units); if some head's logit exceeds that, the
+//     chunk is computed again with R = that head's largest logit over the chunk.
 //   * P.V: wave w owns the output values 128w .. 128w+127 for all 64 heads, so each V^T operand
 //     is read from LDS and widened once and feeds the four head groups' MFMAs.
 //   * Two barriers per tile (tile landed; P published).  Loop-body LDS accesses go through
@@ -676,8 +690,8 @@ struct FXSmem {
   uint8_t ring[kRingX][kTXBytes + kTX * 4];   // tile, then its 64 per-token scales
   int32_t sl[kChunkX + kTX];                  // the chunk's slots, -1 padded
   bf16x8 pex[4][2][64];                       // P^T operands: head group, K half, lane
-  float alpha[64];                            // per-head rescale of the running sums (this tile)
-  float fin_m[64], fin_l[64];                 // per-head running max and sum, after the last tile
+  float fin_m[64], fin_l[64];                 // per-head reference and sum, after the last tile
+  int32_t redo;                               // some head exceeded its reference by the margin
 };
 
 __global__ __launch_bounds__(kNTX) void mla_fp8x_kernel(MlaParams p) {
@@ -777,11 +791,11 @@ __global__ __launch_bounds__(kNTX) void mla_fp8x_kernel(MlaParams p) {
         ql[b][word] = lw;
       }
   }
-  if (!s_active) {   // head groups past the head count: P = 0, no rescale, for every tile
+  if (!s_active) {   // head groups past the head count: P = 0 for every tile
     sm.pex[wave][0][lane] = bf16x8{};
     sm.pex[wave][1][lane] = bf16x8{};
-    if (grp == 0) sm.alpha[wave * 16 + m16] = 1.f;
   }
+  if (threadIdx.x == 0) sm.redo = 0;
 
   // P.V accumulators: head group g, output block 8w + db; lane holds O^T[d][head g*16 + m16]
   f32x4 o[4][kDBlocksW];
@@ -789,8 +803,10 @@ __global__ __launch_bounds__(kNTX) void mla_fp8x_kernel(MlaParams p) {
   for (int g = 0; g < 4; ++g)
 #pragma unroll
     for (int db = 0; db < kDBlocksW; ++db) o[g][db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;   // S^T head group: running max of z * log2(e), per head
-  float l_run = 0.f;         // this lane group's share of sum exp2(z - m_run)
+  float m_ref = -INFINITY;   // S^T head group: the head's reference R (z * log2(e) units)
+  float m_seen = -INFINITY;  // the head's largest logit so far
+  float l_run = 0.f;         // this lane group's share of sum exp2(z - R)
+  bool over = false;         // a logit of this lane's head exceeded R + kRefMargin
   const float scale2 = p.sm_scale * kLog2e * q_unscale;   // (q_unscale: exact power of two)
 
   // S^T operand of block beta (tokens 16beta + m16), steps 2u and 2u+1: logical piece
@@ -877,15 +893,9 @@ __global__ __launch_bounds__(kNTX) void mla_fp8x_kernel(MlaParams p) {
         }
       }
       tmax = lanes4_max(tmax);
-      const bool first = m_run == -INFINITY && tmax > -INFINITY;
-      const bool need = tmax > m_run + 8.f && !first;
-      float alpha = 1.f;
-      if (need) {
-        alpha = __builtin_amdgcn_exp2f(m_run - tmax);
-        m_run = tmax;
-        l_run *= alpha;
-      }
-      m_run = first ? tmax : m_run;
+      m_ref = m_ref == -INFINITY ? tmax : m_ref;   // the first tile with a live token sets R
+      m_seen = fmaxf(m_seen, tmax);
+      over |= tmax > m_ref + kRefMargin;
       // P^T operand of K half kq: tokens 32kq + tau(grp, e) = blocks 2kq, 2kq+1, rows 4grp + j
 #pragma unroll
       for (int kq = 0; kq < 2; ++kq) {
@@ -893,13 +903,12 @@ __global__ __launch_bounds__(kNTX) void mla_fp8x_kernel(MlaParams p) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float ze = z[8 * kq + e];
-          const float pe = ze == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ze - m_run);
+          const float pe = ze == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ze - m_ref);
           l_run += pe;
           pb[e] = (__bf16)(pe * sc[8 * kq + e]);
         }
         rd->pex[wave][kq][lane] = pb;
       }
-      if (grp == 0) rd->alpha[wave * 16 + m16] = alpha;
     }
     lds_barrier();   // P and the rescale factors of every head group are published
 
@@ -919,11 +928,6 @@ __global__ __launch_bounds__(kNTX) void mla_fp8x_kernel(MlaParams p) {
     for (int g = 0; g < 4; ++g) {
       pg[g][0] = rd->pex[g][0][lane];
       pg[g][1] = rd->pex[g][1][lane];
-      const float al = rd->alpha[g * 16 + m16];
-      if (__any(al != 1.f)) {
-#pragma unroll
-        for (int db = 0; db < kDBlocksW; ++db) o[g][db] *= al;
-      }
     }
 #pragma unroll
     for (int db = 0; db < kDBlocksW; ++db) {
@@ -936,26 +940,44 @@ __global__ __launch_bounds__(kNTX) void mla_fp8x_kernel(MlaParams p) {
     }
   };
 
-  for (int v = 0; v < ntiles; ++v) {
-    const int later = min(kRingX - 2, ntiles - 1 - v);
-    if (wave == 0) {
-      if (later >= 2) wait_vmcnt<2 * (kTXCopies / 4 + 1)>();
-      else if (later == 1) wait_vmcnt<kTXCopies / 4 + 1>();
-      else wait_vmcnt<0>();
-    } else {
-      if (later >= 2) wait_vmcnt<2 * (kTXCopies / 4)>();
-      else if (later == 1) wait_vmcnt<kTXCopies / 4>();
-      else wait_vmcnt<0>();
+  // pass 0 with R from the first live tile; pass 1 (rare) with R = the chunk's largest logit
+  for (int pass = 0; pass < 2; ++pass) {
+    if (pass == 1) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int db = 0; db < kDBlocksW; ++db) o[g][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+      l_run = 0.f;
+      m_ref = m_seen;
+      over = false;
+#pragma unroll
+      for (int v = 0; v < kRingX - 1; ++v)
+        if (v < ntiles) issue(&sm, sm.ring[v], v);
     }
-    lds_barrier();   // tile v landed for every wave; ring slot (v-1) % kRingX and P are no longer read
-    tile(&sm, sm.ring[(v + kRingX - 1) % kRingX], v);
+    for (int v = 0; v < ntiles; ++v) {
+      const int later = min(kRingX - 2, ntiles - 1 - v);
+      if (wave == 0) {
+        if (later >= 2) wait_vmcnt<2 * (kTXCopies / 4 + 1)>();
+        else if (later == 1) wait_vmcnt<kTXCopies / 4 + 1>();
+        else wait_vmcnt<0>();
+      } else {
+        if (later >= 2) wait_vmcnt<2 * (kTXCopies / 4)>();
+        else if (later == 1) wait_vmcnt<kTXCopies / 4>();
+        else wait_vmcnt<0>();
+      }
+      lds_barrier();   // tile v landed for every wave; ring slot (v-1) % kRingX and P are no longer read
+      tile(&sm, sm.ring[(v + kRingX - 1) % kRingX], v);
+    }
+    if (s_active && __any(over)) sm.redo = 1;
+    __syncthreads();   // (also: the last tile is no longer read before pass 1 refills the ring)
+    if (pass == 1 || sm.redo == 0) break;
   }
 
-  // ---- final running max and sum per head, then each wave writes its 128 output values
+  // ---- final reference and sum per head, then each wave writes its 128 output values
   if (s_active) {
     const float l_tot = lanes4_sum(l_run);
     if (grp == 0) {
-      sm.fin_m[wave * 16 + m16] = m_run;
+      sm.fin_m[wave * 16 + m16] = m_ref;
       sm.fin_l[wave * 16 + m16] = l_tot;
     }
   }
@@ -982,6 +1004,286 @@ __global__ __launch_bounds__(kNTX) void mla_fp8x_kernel(MlaParams p) {
     }
 #pragma unroll
     for (int db = 0; db < kDBlocksW; ++db) *(f32x4*)(dst + db * 16) = o[g][db] * inv;
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// bf16 rows, chunks of at most kChunkD selected rows: 8 waves (two per SIMD), 32-token tiles
+// copied HBM -> LDS directly into a ring of kRingD tile buffers (three tiles in flight).
+//   * Layout of a tile buffer: token t's row at t*1152, its 16-byte piece p in slot
+//     p ^ swzd(t), swzd(t) = (bit 4 of t) | (bit 1 of t) << 1 | (bit 3 of t) << 2 (a permutation
+//     inside each aligned group of 8 pieces), so that the S^T operand reads (16 tokens of a
+//     block, one piece) and the transposing V^T reads (tokens 8g..8g+3 of two lane groups, two
+//     pieces) touch every LDS bank once.  Copy c, lane i fills slot q = 64c + i; a skipped slot
+//     (-1) reads past the buffer resource's last record, which lands as zeros.
+//   * S^T: wave w owns head group hg = w % 4 (heads 16hg .. 16hg+15) and token block
+//     tb = w / 4 over the full K (q in registers).  Block tb row m holds token
+//     8(m/4) + 4tb + m%4, so lane group g of the result holds tokens 8g + 4tb .. +3 of its head,
+//     one half of the P^T operand's 8 tokens 8g .. 8g+7; the two waves of a head group write
+//     their halves of it to LDS.
+//   * P.V: wave w owns the output values 64w .. 64w+63 for all 64 heads (each V^T operand is
+//     read once per workgroup and feeds four head groups' MFMAs).
+//   * Softmax without rescaling: P = exp2(z - R) with a fixed reference per head, the largest
+//     logit of the chunk's first tile (0 if that tile has no live token).  The accumulators are
+//     then only touched by the matrix core.  P, the sums and the accumulators stay finite and
+//     accurate while the head's largest logit is within R +- 64 (a factor of 2^64); otherwise
+//     the chunk is computed again with R = that largest logit.
+
+constexpr int kRingD = 4;                                 // tile buffers (3 tiles in flight)
+constexpr int kChunkD = 2048;                             // selected rows staged per workgroup
+constexpr int kTDBytes = kTT * kRowDim * 2;               // 36864
+constexpr int kTDCopies = kTDBytes / 1024;                // 36 copies of 1 KiB per tile
+constexpr int kStepsD = kRowDim / 32;                     // 18 K steps of 32
+constexpr int kDBlocksD = kVDim / 16 / 8;                 // 4 output blocks of 16 per wave
+
+__device__ __forceinline__ int bf16_swz(int t) { return ((t >> 4) & 1) | (((t >> 1) & 1) << 1) | (((t >> 3) & 1) << 2); }
+// LDS byte offset of logical piece p of token t inside a tile buffer
+__device__ __forceinline__ int bf16_pos(int t, int p) { return t * (kRowDim * 2) + ((p ^ bf16_swz(t)) << 4); }
+
+struct BDSmem {
+  uint8_t ring[kRingD][kTDBytes];
+  bf16x8 pex[4][64];                          // P^T operands: head group, lane
+  int32_t sl[kChunkD + 3 * kTT];              // the chunk's slots, -1 padded past the chunk
+  float m0[2][64];                            // largest logit of the first tile, by token block
+  float fin_m[2][64], fin_l[2][64];           // per head and token block, after the last tile
+  int32_t redo;
+};
+
+__global__ __launch_bounds__(kNT) void mla_bf16d_kernel(MlaParams p) {
+  __shared__ __attribute__((aligned(16))) BDSmem sm;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hg = wave & 3, tb = wave >> 2;
+  // Blocks go to the 8 XCDs round-robin.  With 8 rows or more the chunks of row r run on XCD
+  // r % 8, so the row's q is read from HBM into one L2 (the grid covers the rows rounded up to
+  // a multiple of 8); with fewer rows the chunks spread over all XCDs.
+  int r, split;
+  if (p.rows >= 8) {
+    const int xcd = blockIdx.x & 7, jx = blockIdx.x >> 3;
+    r = 8 * (jx / p.n_split) + xcd;
+    split = jx - (jx / p.n_split) * p.n_split;
+    if (r >= p.rows) return;
+  } else {
+    r = blockIdx.x / p.n_split;
+    split = blockIdx.x - r * p.n_split;
+  }
+  const int j0 = split * p.chunk;
+  const int j1 = min(p.k, j0 + p.chunk);
+  const int ntiles = j1 > j0 ? (j1 - j0 + kTT - 1) / kTT : 0;
+  const int32_t* sl = p.slots + (int64_t)r * p.k;
+  const int ngroups = min(4, p.H / 16);           // live head groups (H is a multiple of 16)
+  const bool s_active = hg < ngroups;             // this wave's S^T head group exists
+  const int m16 = lane & 15, grp = lane >> 4;
+
+  {
+    const int span = ntiles * kTT;
+    for (int e0 = 0; e0 < span; e0 += 4 * kNT) {
+      int32_t v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = sl[min(j0 + e0 + u * kNT + (int)threadIdx.x, p.k - 1)];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = e0 + u * kNT + threadIdx.x;
+        if (e < span) sm.sl[e] = j0 + e < j1 ? v[u] : -1;
+      }
+    }
+  }
+  if (threadIdx.x == 0) sm.redo = 0;
+  if (!s_active) sm.pex[hg][lane] = bf16x8{};   // head groups past the head count: P = 0
+  __syncthreads();
+  // q of this wave's head group (B operand of S^T): head 16hg + m16, dims 32s + 8grp .. +8 (a
+  // group past the head count loads the last head and never uses it).  Requested after the
+  // slot list and before the first tiles, so that the wait for tile 0 covers it and no wait
+  // for it covers the tiles after.
+  bf16x8 qf[kStepsD];
+  {
+    const int qhead = min(hg * 16 + m16, p.H - 1);
+    const bf16x8* qrow = (const bf16x8*)((const __bf16*)p.q + ((int64_t)r * p.H + qhead) * kRowDim);
+#pragma unroll
+    for (int s = 0; s < kStepsD; ++s) qf[s] = qrow[4 * s + grp];
+  }
+
+  // copies of tile v: wave w issues copies w, w+8, .. (< 36): 5 for waves 0-3, 4 for waves 4-7
+  const int nld = wave < kTDCopies - 4 * 8 ? 5 : 4;
+  const __amdgpu_buffer_rsrc_t kv_rs = rows_rsrc(p.kv, kRowDim * 2, p.num_slots);
+  auto issue_one = [&](const BDSmem* __restrict__ rd, uint8_t* __restrict__ dst, int v, int c) {
+    const int cc = wave + 8 * c;
+    if (c < 4 || cc < kTDCopies) {
+      const int q = cc * 64 + lane;
+      const int t = q / 72, sp = q - t * 72;
+      const int32_t sv = rd->sl[v * kTT + t];
+      // a skipped slot reads past the last record: zeros
+      lds_dma16_row(kv_rs, sv < 0 ? 0x7fffffff : sv, (sp ^ bf16_swz(t)) << 4, dst + cc * 1024);
+    }
+  };
+  auto issue = [&](const BDSmem* __restrict__ rd, uint8_t* __restrict__ dst, int v) {
+#pragma unroll
+    for (int c = 0; c < 5; ++c) issue_one(rd, dst, v, c);
+  };
+  auto wait_tile = [&](int later) {   // at most `later` later tiles' copies outstanding
+    if (nld == 5) wait_vmcnt_later<5, kRingD - 2>(later);
+    else wait_vmcnt_later<4, kRingD - 2>(later);
+  };
+
+  // P.V accumulators: head group g, output block db; lane holds O^T[64w + 16db + 4grp + j][16g + m16]
+  f32x4 o[4][kDBlocksD];
+  const float scale2 = p.sm_scale * kLog2e;
+  float ref = 0.f;           // R of this lane's head
+  float m_seen = -INFINITY;  // the head's largest logit in this wave's token blocks
+  float l_run = 0.f;         // this lane group's share of sum exp2(z - R)
+
+  // S^T operand of block tb: row m = token 8(m/4) + 4tb + m%4, logical piece 4s + grp
+  const int a_tok = 8 * (m16 >> 2) + 4 * tb + (m16 & 3);
+  // V^T operand: lane jl of group grp reads token 8grp + jl/4 (+4), bytes 8(jl%4) of the 32-byte
+  // block of dims 64w + 16db
+  const int v_tok = 8 * grp + (m16 >> 2);
+
+  // S^T of the tile at T; with nv >= 0 the copies of tile nv into dst are issued between the
+  // MFMAs (copy c before step 3c + 1), where a wait for room in the memory pipeline overlaps
+  // the matrix core's work
+  auto s_tile = [&](const BDSmem* __restrict__ rd, const uint8_t* __restrict__ T, uint8_t* __restrict__ dst, int nv) -> f32x4 {
+    f32x4 acc0 = f32x4{0.f, 0.f, 0.f, 0.f}, acc1 = f32x4{0.f, 0.f, 0.f, 0.f};
+    constexpr int kAhead = 4;
+    bf16x8 a[kAhead];
+#pragma unroll
+    for (int s = 0; s < kAhead; ++s) a[s] = *(const bf16x8*)(T + bf16_pos(a_tok, 4 * s + grp));
+#pragma unroll
+    for (int s = 0; s < kStepsD; ++s) {
+      if (s % 3 == 1 && s / 3 < 5 && nv >= 0) issue_one(rd, dst, nv, s / 3);
+      const bf16x8 x = a[s % kAhead];
+      if (s + kAhead < kStepsD) a[s % kAhead] = *(const bf16x8*)(T + bf16_pos(a_tok, 4 * (s + kAhead) + grp));
+      // two accumulators (even / odd steps) so that consecutive MFMAs do not wait on each other
+      if (s & 1) acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, qf[s], acc1, 0, 0, 0);
+      else acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, qf[s], acc0, 0, 0, 0);
+    }
+    return acc0 + acc1;
+  };
+  // lane holds head 16hg + m16, tokens 8grp + 4tb + j: logits, -inf for a skipped slot
+  auto logits = [&](const BDSmem* __restrict__ rd, int v, const f32x4& sacc, float (&z)[4]) {
+    const int32_t* slt = rd->sl + v * kTT + 8 * grp + 4 * tb;
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      z[j] = slt[j] >= 0 ? sacc[j] * scale2 : -INFINITY;
+      tmax = fmaxf(tmax, z[j]);
+    }
+    return lanes4_max(tmax);   // over the block's 16 tokens
+  };
+  auto publish = [&](BDSmem* __restrict__ rd, const float (&z)[4]) {
+    bf16x4 pb;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float pe = z[j] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(z[j] - ref);
+      l_run += pe;
+      pb[j] = (__bf16)pe;
+    }
+    *(bf16x4*)((uint8_t*)&rd->pex[hg][lane] + 8 * tb) = pb;
+  };
+  auto pv_tile = [&](const BDSmem* __restrict__ rd, const uint8_t* __restrict__ T) {
+    bf16x8 av[kDBlocksD];
+#pragma unroll
+    for (int db = 0; db < kDBlocksD; ++db) {
+      const int pc = 8 * wave + 2 * db + ((m16 & 3) >> 1);   // logical piece of this lane's 8 bytes
+      const int off = 8 * (m16 & 1);
+      const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+          (__attribute__((address_space(3))) bf16x4*)(T + bf16_pos(v_tok, pc) + off));
+      const bf16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+          (__attribute__((address_space(3))) bf16x4*)(T + bf16_pos(v_tok + 4, pc) + off));
+      av[db] = __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+    bf16x8 pg[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) pg[g] = rd->pex[g][lane];
+#pragma unroll
+    for (int db = 0; db < kDBlocksD; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) o[g][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[db], pg[g], o[g][db], 0, 0, 0);
+  };
+
+  // pass 0 with R from the first tile; pass 1 (rare) with R = the chunk's largest logit
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int db = 0; db < kDBlocksD; ++db) o[g][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    l_run = 0.f;
+#pragma unroll
+    for (int v = 0; v < kRingD - 1; ++v)
+      if (v < ntiles) issue(&sm, sm.ring[v], v);
+
+    for (int v = 0; v < ntiles; ++v) {
+      wait_tile(min(kRingD - 2, ntiles - 1 - v));
+      lds_barrier();   // tile v landed; P and ring slot (v-1) % kRingD are no longer read
+      const int nv = v + kRingD - 1 < ntiles ? v + kRingD - 1 : -1;
+      uint8_t* dst = sm.ring[(v + kRingD - 1) % kRingD];
+      const uint8_t* T = sm.ring[v % kRingD];
+      float z[4];
+      float tmax = -INFINITY;
+      if (s_active) tmax = logits(&sm, v, s_tile(&sm, T, dst, nv), z);
+      else if (nv >= 0) issue(&sm, dst, nv);
+      if (pass == 0 && v == 0) {
+        // the reference: the first tile's largest logit over both token blocks (0 without one)
+        if (s_active && grp == 0) sm.m0[tb][hg * 16 + m16] = tmax;
+        __syncthreads();
+        if (s_active) {
+          const float m0 = fmaxf(sm.m0[0][hg * 16 + m16], sm.m0[1][hg * 16 + m16]);
+          ref = m0 == -INFINITY ? 0.f : m0;
+        }
+      }
+      if (s_active) {
+        m_seen = fmaxf(m_seen, tmax);
+        publish(&sm, z);
+      }
+      lds_barrier();   // P of the tile is published
+      pv_tile(&sm, T);
+    }
+    // does some head's largest logit lie outside R +- 64?
+    if (s_active) {
+      const float l_blk = lanes4_sum(l_run);   // (all lanes of the wave take part)
+      if (grp == 0) {
+        sm.fin_m[tb][hg * 16 + m16] = m_seen;
+        sm.fin_l[tb][hg * 16 + m16] = l_blk;
+      }
+    }
+    __syncthreads();
+    float mx = -INFINITY;
+    if (s_active) {
+      mx = fmaxf(sm.fin_m[0][hg * 16 + m16], sm.fin_m[1][hg * 16 + m16]);
+      if (mx > -INFINITY && (mx > ref + kRefMargin || mx < ref - kRefMargin)) sm.redo = 1;
+    }
+    __syncthreads();
+    if (pass == 1 || sm.redo == 0) break;
+    ref = mx > -INFINITY ? mx : 0.f;
+    __syncthreads();
+  }
+
+  // ---- each wave writes its 64 output values of every head
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    if (g >= ngroups) break;
+    const int head = g * 16 + m16;
+    const float mh = fmaxf(sm.fin_m[0][head], sm.fin_m[1][head]);
+    const float lh = sm.fin_l[0][head] + sm.fin_l[1][head];
+    // R of this head as its S^T waves used it (recomputed from what they published)
+    const float m0 = fmaxf(sm.m0[0][head], sm.m0[1][head]);
+    const float rh = sm.redo ? (mh > -INFINITY ? mh : 0.f) : (m0 == -INFINITY ? 0.f : m0);
+    const float inv = lh > 0.f ? 1.f / lh : 0.f;
+    float* dst;
+    if (p.n_split == 1) {
+      dst = p.out + ((int64_t)r * p.H + head) * kVDim + wave * 64 + grp * 4;
+      if (p.lse && wave == 0 && grp == 0)
+        p.lse[(int64_t)r * p.H + head] = lh > 0.f ? (rh + log2f(lh)) * kLn2 : -INFINITY;
+    } else {
+      const int64_t prow = ((int64_t)r * p.n_split + split) * p.H + head;
+      dst = p.part_o + prow * kVDim + wave * 64 + grp * 4;
+      if (wave == 0 && grp == 0) {
+        p.part_m[prow] = lh > 0.f ? rh * kLn2 : -INFINITY;
+        p.part_l[prow] = lh;
+      }
+    }
+#pragma unroll
+    for (int db = 0; db < kDBlocksD; ++db) *(f32x4*)(dst + db * 16) = o[g][db] * inv;
   }
 }
 
@@ -1091,6 +1393,9 @@ hipError_t launch_mla(const MlaParams& p0, dsa_dtype_t q_dtype, dsa_dtype_t kv_d
     if (chunk <= kChunkX) hipLaunchKernelGGL(mla_fp8x_kernel, grid, dim3(kNTX), 0, s, p);
     else hipLaunchKernelGGL(mla_fp8_kernel, grid, dim3(kNT), 0, s, p);
   }
+  else if (chunk <= kChunkD)
+    hipLaunchKernelGGL(mla_bf16d_kernel, dim3((unsigned)((p.rows >= 8 ? (p.rows + 7) / 8 * 8 : p.rows) * p.n_split)),
+                       dim3(kNT), 0, s, p);
   else hipLaunchKernelGGL(mla_mfma_kernel<false>, grid, dim3(kNT), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_split == 1) return e;

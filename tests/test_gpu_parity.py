@@ -211,6 +211,55 @@ def test_sparse_mla_empty_selection_and_single_row():
     assert np.abs(out.cpu().numpy()[0, 0] - v[None, :]).max() < 1e-6
 
 
+@pytest.mark.parametrize("name,ns", [("c2", 1), ("c2", 2), ("c5", 1), ("c5", 2)])
+def test_sparse_mla_wide_logit_range(name, ns):
+    """Heads whose largest logit lies far above or far below the kernels' first-tile reference.
+
+    Head 3 meets one selected row, late in the chunk, whose logit lies more than 64 (log2
+    units) above the rest; head 7 sees every logit near -200 and, in the second chunk, a first
+    tile with no live slot.  Both need the second pass of the kernels; the expected values are
+    the oracle's.  fp8 rows: the e4m3 matrix core accumulates S^T with an error of about
+    1e-4 * sum |q_d k_d|, which the boosted row's large norm makes visible in every head, so the
+    bound there is relative to each head's output scale and looser."""
+    cfg, inp, _ = _case(name, [3000], seed=106, top_k=512, q_per_seq=1)
+    rng = np.random.default_rng(12)
+    slots = _random_slots(cfg, rng, 512)
+    slots[0, 0, 256:288] = -1                                    # chunk 1 (ns=2) starts with a dead tile
+    q = O.dequantize(inp["q_mla"], "bf16").copy()
+    kv = O.dequantize(inp["kv_cache"], cfg.kv_dtype, inp["kv_scale"]).copy()
+    boost = int(slots[0, 0, 200])
+    fp8 = cfg.kv_dtype == "fp8"
+    kv[boost] = q[0, 0, 3] * (1300.0 if fp8 else 3000.0)        # head 3: one dominant logit
+    kv[:, 575] = 30.0                                            # a shared RoPE component ...
+    q[0, 0, 7, 575] = -110.0                                     # ... that pushes head 7's logits to about -200
+    inp["q_mla"] = dsa_inputs.encode_bf16(q)
+    if fp8:
+        inp["kv_cache"], inp["kv_scale"] = dsa_inputs.encode_fp8_rows(kv)
+    else:
+        inp["kv_cache"] = dsa_inputs.encode_bf16(kv)
+    t = dsa_inputs.to_torch(inp, cfg, DEV)
+    out, lse = gpu_mla(cfg, t, torch.from_numpy(slots).to(DEV), n_split=ns)
+    ro, rl = oracle_mla(cfg, inp, slots)
+    og, lg = out.cpu().numpy().astype(np.float64), lse.cpu().numpy()
+    assert np.isfinite(og).all() and np.isfinite(lg).all()
+    keep = [h for h in range(cfg.mla_heads) if h != 3]
+    if fp8:
+        scale = np.maximum(1.0, np.abs(ro).max(axis=-1, keepdims=True))
+        err = (np.abs(og - ro) / scale).max()
+        # (logit error of 1e-4 * sum |q_d k_d| ~ 0.005 log2 units for the boosted row, plus
+        # the bf16 rounding of P * scale, 2^-9: about 0.5% of a head's output scale)
+        assert err <= 1e-2, f"scaled max-abs error {err:.3e}"
+        g, r = og.reshape(-1, 512), ro.reshape(-1, 512)
+        cos = (g * r).sum(1) / (np.linalg.norm(g, axis=1) * np.linalg.norm(r, axis=1))
+        assert cos.min() >= 0.9999, f"min cosine {cos.min():.8f}"
+        assert np.abs(lg - rl).max() <= 1e-2
+    else:
+        check_attention(og[:, :, keep], ro[:, :, keep], lg[:, :, keep], rl[:, :, keep])
+        # head 3 is that one row's V (values of about 100): relative error
+        assert np.abs(og[0, 0, 3] - ro[0, 0, 3]).max() <= 1e-5 * np.abs(ro[0, 0, 3]).max()
+        assert abs(lg[0, 0, 3] - rl[0, 0, 3]) <= 1e-4 * abs(rl[0, 0, 3])
+
+
 def test_split_combine_parity_direct():
     rng = np.random.default_rng(9)
     rows, ns, H = 3, 5, 64
