@@ -97,7 +97,7 @@ dsa_status_t dsa_indexer_scores(const dsa_batch_t *batch,
  * transform): topk_slots[b,i,j] = slot(b, topk_idx[b,i,j]), -1 for padding.
  *   scores     [B, Q, scores_ld] f32 (only columns t <= pos(b,i) are read; no NaN)
  *   topk_idx   [B, Q, k] int32;  topk_slots [B, Q, k] int32 or NULL
- * Supported: 1 <= k <= 8192, max_seq_len <= 262144.  A few rows (at most 64) of 64K+
+ * Supported: 1 <= k <= 8192, max_seq_len <= 262144.  Up to 128 rows of 64K+
  * columns are ranked in two passes whose candidates (score, column) live in the workspace of
  * dsa_topk_workspace_size() bytes, 256-byte aligned, no initial contents; workspace may be
  * NULL when that size is 0.

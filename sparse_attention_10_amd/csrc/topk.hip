@@ -750,15 +750,15 @@ __global__ __launch_bounds__(256) void page_map_kernel(const int32_t* idx, int64
 namespace {
 
 // Two-pass plan for long rows: the chunk length L (0 = one pass) and chunks per row.  Rows of
-// 64K+ columns are split when they are few (at most 64, a quarter of the compute units), the
-// chunks still fit about one workgroup per compute unit, and a chunk keeps at most a quarter of
-// its columns as candidates.  (Measured on MI355X: a 128K row takes 57 us in one pass and 31 us
-// in chunks of 16K; 128 rows of 64K are faster in one pass.)
+// 64K+ columns are split when they are at most 128 (half the compute units), the chunks still
+// fit one workgroup per compute unit, and a chunk keeps at most a quarter of its columns as
+// candidates.  (Measured on MI355X: a 128K row takes 57 us in one pass and 24 us in chunks of
+// 16K; 128 rows of 64K take 38.7 us in one pass and 36.4 us in chunks of 32K.)
 struct TopkPlan {
   int L, C;
 };
 TopkPlan topk_plan(int64_t rows, int max_seq_len, int k) {
-  if (max_seq_len < 65536 || rows > 64) return {0, 0};
+  if (max_seq_len < 65536 || rows > 128) return {0, 0};
   for (int L = 16384; L <= 32768; L *= 2) {
     const int C = (max_seq_len + L - 1) / L;
     if (L >= 4 * k && C >= 2 && rows * C <= 256) return {L, C};

@@ -98,9 +98,12 @@ def test_topk_workspace_long_rows(L):
     assert need >= 32 * 8 * 2048 * 8
     assert L.dsa_topk(ctypes.byref(long), FAKE, 131072, 2048, FAKE, None, None, 0, None) == 3
     assert L.dsa_topk(ctypes.byref(long), FAKE, 131072, 2048, FAKE, None, FAKE, need - 1, None) == 3
-    # below 64K columns, or many rows (one workgroup per row fills the GPU): one pass
+    # 128 rows of 64K columns: chunks of 32K, two per row
+    verify = _batch(batch=64, q_per_seq=2, max_seq_len=65536, max_pages_per_seq=1024, num_slots=64 * 65536)
+    assert L.dsa_topk_workspace_size(ctypes.byref(verify), 2048) >= 128 * 2 * 2048 * 8
+    # below 64K columns, or more rows than half the compute units: one pass
     assert L.dsa_topk_workspace_size(ctypes.byref(_batch(max_seq_len=65535, max_pages_per_seq=1024)), 2048) == 0
-    many = _batch(batch=64, q_per_seq=2, max_seq_len=65536, max_pages_per_seq=1024, num_slots=64 * 65536)
+    many = _batch(batch=65, q_per_seq=2, max_seq_len=65536, max_pages_per_seq=1024, num_slots=65 * 65536)
     assert L.dsa_topk_workspace_size(ctypes.byref(many), 2048) == 0
 
 

@@ -178,8 +178,11 @@ MLA_CASES = [
     # many query rows at once (32 rows x 8 chunks; 64 sequences x 2 fp8 rows x 2 chunks)
     ("c3", [200] * 32, 2048, 64, 0, 0.0),
     ("c5", [300] * 64, 512, 64, 2, 0.0),
-    # fp8 chunks above the wide kernel's 2048-row staging limit take the 8-wave kernel
+    # chunks above the wide fp8 kernel's 1024-row and the bf16 ring kernel's 2048-row staging
+    # limits take the 8-wave kernels with register-staged (bf16) or narrower (fp8) tiles
     ("c5", [5000], 4096, 64, 1, 0.02),
+    ("c2", [5000], 4096, 64, 1, 0.02),
+    ("c2", [5000], 4096, 32, 2, 0.0),
     # fp8 with fewer heads than the wide kernel's four groups, partial last tiles
     ("c5", [1500], 200, 32, 3, 0.1),
     ("c5", [1500], 200, 48, 0, 0.0),
