@@ -1359,6 +1359,44 @@ __global__ __launch_bounds__(128) void mla_combine_kernel(CombineParams p) {
   }
 }
 
+// Few chunks (n_split <= kFewSplits): one 256-thread workgroup per (row, two heads); thread
+// (head e, quad q) merges all chunks of output values 4q..4q+3 of its head, in chunk order,
+// with every chunk's loads issued at once.  (Measured: 128 rows x 2 chunks merge in 8.4 us
+// against 16.4 us with the quarter-row workgroups above, whose 32K launches of 128 threads
+// cost more than the loads; at 8 chunks the quarter-row kernel stays faster, 11.0 against
+// 13.0 us for 32 rows.)
+constexpr int kFewSplits = 4;
+
+__global__ __launch_bounds__(256) void mla_combine_few_kernel(CombineParams p) {
+  const int tid = threadIdx.x;
+  const int e = tid >> 7, q = tid & 127;
+  const int hp = p.H >> 1;                          // head pairs per row (H is even)
+  const int r = blockIdx.x / hp, h = 2 * (blockIdx.x - r * hp) + e;
+  const int ns = p.n_split;
+  const int64_t base = (int64_t)r * ns * p.H + h;  // partial row of chunk j: base + j * H
+  float mv[kFewSplits], lv[kFewSplits];
+  f32x4 ov[kFewSplits];
+#pragma unroll
+  for (int j = 0; j < kFewSplits; ++j) {
+    lv[j] = 0.f;
+    if (j < ns) {   // (uniform)
+      const int64_t pr = base + (int64_t)j * p.H;
+      mv[j] = p.part_m[pr];
+      lv[j] = p.part_l[pr];
+      ov[j] = *(const f32x4*)(p.part_o + pr * kVDim + 4 * q);
+    }
+  }
+  float M = -INFINITY, den = 0.f;
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < kFewSplits; ++j)
+    if (lv[j] > 0.f) lse_merge(M, den, acc, mv[j], lv[j], ov[j] * lv[j]);
+  float* dst = p.out + ((int64_t)r * p.H + h) * kVDim + 4 * q;
+  const bool live = den > 0.f;
+  *(f32x4*)dst = live ? acc * (1.f / den) : f32x4{0.f, 0.f, 0.f, 0.f};
+  if (p.lse && q == 0) p.lse[(int64_t)r * p.H + h] = live ? M + logf(den) : -INFINITY;
+}
+
 }  // namespace
 
 int mla_default_split(int rows, int H, int k, dsa_dtype_t kv_dtype) {
@@ -1405,7 +1443,10 @@ hipError_t launch_mla(const MlaParams& p0, dsa_dtype_t q_dtype, dsa_dtype_t kv_d
 
 hipError_t launch_combine(const CombineParams& c, hipStream_t s) {
   if (c.rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)(c.rows * c.H * 4)), dim3(128), 0, s, c);
+  if (c.n_split <= kFewSplits && c.H % 2 == 0)
+    hipLaunchKernelGGL(mla_combine_few_kernel, dim3((unsigned)(c.rows * (c.H / 2))), dim3(256), 0, s, c);
+  else
+    hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)(c.rows * c.H * 4)), dim3(128), 0, s, c);
   return hipGetLastError();
 }
 
