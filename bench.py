@@ -395,14 +395,18 @@ def main():
         v["us"] = round(v["us"], 3)
     # the dominant kernel: the stage with the largest average launch time
     dom = max(stage_info, key=lambda s: stage_info[s]["us"])
-    # fp8 rows run on the wide-tile kernel when a split chunk holds at most 1024 rows
-    mla_kern = ("mla_mfma_kernel" if cfg.kv_dtype != "fp8" else
-                "mla_fp8x_kernel" if -(-(-(-k // ns)) // 32) * 32 <= 1024 else "mla_fp8_kernel")
+    # split chunks of at most 1024 (fp8 rows) or 2048 (bf16 rows) selected rows run on the
+    # direct-to-LDS ring kernels
+    chunk = -(-(-(-k // ns)) // 32) * 32
+    if cfg.kv_dtype == "fp8":
+        mla_kern = "mla_fp8x_kernel" if chunk <= 1024 else "mla_fp8_kernel"
+    else:
+        mla_kern = "mla_bf16d_kernel" if chunk <= 2048 else "mla_mfma_kernel"
     # many rows per sequence with bf16 keys run on the prefill indexer (16 rows per workgroup)
     idx_kern = ("indexer_prefill_kernel" if Q >= 16 and cfg.key_dtype == "bf16" and cfg.page_size % 32 == 0
                 else "indexer_mfma_kernel")
     kern = {"indexer": idx_kern, "mla": mla_kern, "topk": "topk_kernel",
-            "combine": "mla_combine_kernel"}[dom]
+            "combine": "mla_combine_few_kernel" if ns <= 4 and H % 2 == 0 else "mla_combine_kernel"}[dom]
     if cfg.name == "c4" and dom in ("indexer", "mla"):
         ach = stage_info[dom]["flops"] / (stage_info[dom]["us"] * 1e-6) / 1e12
         roof = dict(bound="mfma", achieved=round(ach, 2), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
