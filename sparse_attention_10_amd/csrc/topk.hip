@@ -60,7 +60,10 @@ constexpr int kOffECnt = kOffGCnt + kMaxUnits;           // u32 [kMaxUnits]
 constexpr int kOffOut = kOffECnt + kMaxUnits;            // i32 [kMaxTopK] winners' columns
 constexpr int kFineWords = kSmallBins + kSmallBins / 32; // second-digit histogram (padded layout)
 constexpr int kOffFine = kOffOut + kMaxTopK;             // u32 [kFineWords]
-static_assert(kOffFine + kFineWords <= kHistWords, "LDS regions must fit in the histogram's space");
+// 64 lane-indexed dummy words: the output writes of the lanes that take nothing go there, so
+// that the per-key-row writes need no branch (and no exec-mask round trip)
+constexpr int kOffDummy = kOffFine + kFineWords;
+static_assert(kOffDummy + 64 <= kHistWords, "LDS regions must fit in the histogram's space");
 static_assert(kUnitsPerLane <= 6, "unit scan layout");
 static_assert(kBinsPerThread % 4 == 0 && kBinsPerThread <= 64, "histogram layout");
 
@@ -527,8 +530,37 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkParams p) {
         }
       }
     };
+    if constexpr (decltype(G)::value && decltype(PW)::value && !decltype(CE)::value) {
+      // the register block in groups of 8 key rows: counts and ballots first; a group without
+      // a key in the bin (most of them) skips the gather with one uniform branch
+      constexpr int kG = RV < 8 ? RV : 8;
 #pragma unroll
-    for (int j = 0; j < RV; ++j) classify(key[j], wave * RV + j);
+      for (int j0 = 0; j0 < RV; j0 += kG) {
+        uint64_t me[kG], any = 0;
+#pragma unroll
+        for (int i = 0; i < kG; ++i) {
+          const uint32_t kk = key[j0 + i];
+          ug += kk > t_gt ? 1u : 0u;
+          me[i] = __ballot(kk - t_lo <= t_hi - t_lo);
+          any |= me[i];
+        }
+        if (any) {
+#pragma unroll
+          for (int i = 0; i < kG; ++i) {
+            const uint32_t kk = key[j0 + i];
+            if (kk - t_lo <= t_hi - t_lo) {
+              const uint32_t pos = mbcnt(me[i], wave * kCandPerWave + wcount);
+              cand_key[pos] = kk;
+              cand_col[pos] = (uint32_t)(((wave * RV + j0 + i) << 6) + lane);
+            }
+            wcount += (uint32_t)__popcll(me[i]);
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < RV; ++j) classify(key[j], wave * RV + j);
+    }
     unit_done(wave);
     tail_pass(classify, nop, [&](int s) { unit_done(kWaves * (1 + s) + wave); });
   };
@@ -701,12 +733,32 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkParams p) {
         take = kk >= t_take;
       }
       const uint64_t mt = __ballot(take);
-      if (take) out_s[min(mbcnt(mt, obase), (uint32_t)kMaxTopK - 1u)] = (r << 6) + lane;
+      // (a lane that takes nothing writes to its dummy word)
+      out_s[take ? min(mbcnt(mt, obase), (uint32_t)kMaxTopK - 1u) : (uint32_t)(kOffDummy - kOffOut + lane)] = (r << 6) + lane;
       obase += (uint32_t)__popcll(mt);
     };
     unit_start(wave, obase, eqr);
+    if constexpr (!decltype(TIES)::value) {
+      // the register block in groups of 8 key rows: the 8 ballots first, then the offsets and
+      // writes, so that consecutive rows do not wait on each other's count
+      constexpr int kG = RV < 8 ? RV : 8;
 #pragma unroll
-    for (int j = 0; j < RV; ++j) emit(key[j], wave * RV + j);
+      for (int j0 = 0; j0 < RV; j0 += kG) {
+        uint64_t mt[kG];
+#pragma unroll
+        for (int i = 0; i < kG; ++i) mt[i] = __ballot(key[j0 + i] >= t_take);
+#pragma unroll
+        for (int i = 0; i < kG; ++i) {
+          const bool take = key[j0 + i] >= t_take;
+          out_s[take ? min(mbcnt(mt[i], obase), (uint32_t)kMaxTopK - 1u) : (uint32_t)(kOffDummy - kOffOut + lane)] =
+              ((wave * RV + j0 + i) << 6) + lane;
+          obase += (uint32_t)__popcll(mt[i]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < RV; ++j) emit(key[j], wave * RV + j);
+    }
     tail_pass(emit, [&](int s) { unit_start(kWaves * (1 + s) + wave, obase, eqr); }, nop);
   };
   if (ties) emit_all(Flag<true>());
