@@ -140,6 +140,10 @@ struct IndexerParams {
   int32_t tiles_per_wg;   // matrix-core paths: key tiles (stages) per workgroup
   int32_t groups;         // matrix-core paths: key ranges (workgroups per row group) per sequence
   int32_t p_shift;        // log2(P) when the page size is a power of two, else -1
+  // matrix-core decode path, several sequences: key ranges sized from the actual lengths.
+  // 0 = ranges of tiles_per_wg tiles over max_seq_len for every sequence; else the number of
+  // ranges to aim for (each workgroup derives the partition from seq_lens, see the kernel)
+  int32_t balanced;
 };
 
 struct TopkParams {

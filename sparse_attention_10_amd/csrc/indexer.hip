@@ -118,6 +118,40 @@ struct Geo {
 template <bool FP8>
 __device__ __forceinline__ int swz(int r) { return FP8 ? ((r >> 1) & 7) : (r & 15); }
 
+// Sum and inclusive prefix sum of one int per thread over the 512-thread workgroup (wave
+// shuffles, then the 8 wave totals through LDS; `red` holds at least 8 ints).
+__device__ __forceinline__ int wave_incl_scan_i(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(v, o);
+    v += lane >= o ? u : 0;
+  }
+  return v;
+}
+__device__ __forceinline__ int block_incl_scan(int v, int32_t* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int w = wave_incl_scan_i(v);
+  if (lane == 63) red[wave] = w;
+  __syncthreads();
+  int before = 0;
+#pragma unroll
+  for (int k = 0; k < kThreadsI / 64; ++k) before += k < wave ? red[k] : 0;
+  __syncthreads();
+  return w + before;
+}
+__device__ __forceinline__ int block_sum(int v, int32_t* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int w = wave_incl_scan_i(v);
+  if (lane == 63) red[wave] = w;
+  __syncthreads();
+  int t = 0;
+#pragma unroll
+  for (int k = 0; k < kThreadsI / 64; ++k) t += red[k];
+  __syncthreads();
+  return t;
+}
+
 // Shared memory of indexer_mfma_kernel: ring stage = keys, then (fp8) their per-token scales.
 template <bool FP8, int QB>
 struct ISmem {
@@ -126,6 +160,7 @@ struct ISmem {
   float w[QB][kHi];
   int32_t pt[kMaxWgPages];
   float xs[2][4][kSub];    // one row: head sums of heads 32..63, by stage parity and sub-tile
+  int32_t part[20];        // the balanced partition: wave partial sums, then (b, first range, ranges)
 };
 
 
@@ -150,11 +185,46 @@ __global__ __launch_bounds__(kThreadsI) void indexer_mfma_kernel(IndexerParams p
   const int blk = (int)blockIdx.x / (8 * nq);
   const int rem = (int)blockIdx.x - blk * 8 * nq;
   const int kr = 8 * blk + (rem & 7);
-  if (kr >= p.B * p.groups) return;           // grid padding (uniform)
-  const int b = kr / p.groups;
-  const int grp_id = kr - b * p.groups;
   const int qb0 = (rem >> 3) * QB;            // first query row of the block
-  const int tile_base = grp_id * p.tiles_per_wg * kTile;
+  int b, grp_id, tpw;                         // sequence, range within it, tiles per range
+  if (p.balanced == 0) {
+    if (kr >= p.B * p.groups) return;         // grid padding (uniform)
+    b = kr / p.groups;
+    grp_id = kr - b * p.groups;
+    tpw = p.tiles_per_wg;
+  } else {
+    // Ranges of T tiles over each sequence's own length: T = ceil(total tiles / p.balanced),
+    // sequence b gets ceil(tiles_b / T) ranges, numbered in sequence order.  Every workgroup
+    // derives the same partition from seq_lens (thread i holds sequence i; B <= 128).
+    const int i = threadIdx.x;
+    const int Li = i < p.B ? min(p.seq_lens[i], p.max_seq_len) : 0;
+    const int ti = (max(Li, 0) + kTile - 1) / kTile;
+    const int total = block_sum(ti, sm.part);
+    // the smallest T (a few tries upwards from total / R) whose ranges fit R = balanced + B;
+    // T = ceil(total / balanced) always does
+    const int R = p.balanced + p.B;
+    int T = max(1, (total + R - 1) / R);
+    const int T_safe = max(1, (total + p.balanced - 1) / p.balanced);
+    for (int it = 0; it < 4 && T < T_safe; ++it) {
+      const int cnt = block_sum((ti + T - 1) / T, sm.part);
+      if (cnt <= R) break;
+      T = min(T_safe, max(T + 1, (int)(((int64_t)T * cnt + R - 1) / R)));
+    }
+    if (T < T_safe && block_sum((ti + T - 1) / T, sm.part) > R) T = T_safe;
+    const int gi = (ti + T - 1) / T;
+    const int incl = block_incl_scan(gi, sm.part);
+    if (i < p.B && kr >= incl - gi && kr < incl) {
+      sm.part[16] = i;
+      sm.part[17] = incl - gi;
+    }
+    if (i == kThreadsI - 1) sm.part[18] = incl;   // ranges in all
+    __syncthreads();
+    if (kr >= sm.part[18]) return;            // (uniform)
+    b = sm.part[16];
+    grp_id = kr - sm.part[17];
+    tpw = T;
+  }
+  const int tile_base = grp_id * tpw * kTile;
   const int32_t* ptab_g = p.page_table + (int64_t)b * p.maxP;
 
   // Stage v covers tokens tile_base + v*ST ..; this thread's load c fills LDS bytes
@@ -181,7 +251,7 @@ __global__ __launch_bounds__(kThreadsI) void indexer_mfma_kernel(IndexerParams p
   // arrives (bounded by max_seq_len alone), so the first copies wait one round trip less
   int32_t pre_pe[NB - 1][NL];
   {
-    const int t_cap = min(tile_base + p.tiles_per_wg * kTile, p.max_seq_len);
+    const int t_cap = min(tile_base + tpw * kTile, p.max_seq_len);
 #pragma unroll
     for (int v = 0; v < NB - 1; ++v)
 #pragma unroll
@@ -192,7 +262,7 @@ __global__ __launch_bounds__(kThreadsI) void indexer_mfma_kernel(IndexerParams p
   }
   const int L = min(p.seq_lens[b], p.max_seq_len);
   if (tile_base >= L) return;                 // uniform early exit
-  const int tile_end = min(L, tile_base + p.tiles_per_wg * kTile);
+  const int tile_end = min(L, tile_base + tpw * kTile);
   const int pos_last = L - p.Q + qb0 + QB - 1;  // the block's largest position
   const int t_stop = min(tile_end, pos_last + 1);  // tokens at or past this are never scored
   const int nstage = t_stop > tile_base ? (t_stop - tile_base + G::ST - 1) / G::ST : 0;
@@ -679,7 +749,18 @@ hipError_t launch_indexer(const IndexerParams& p0, dsa_dtype_t q_dtype, dsa_dtyp
     p.p_shift = (p.P & (p.P - 1)) == 0 ? __builtin_ctz((unsigned)p.P) : -1;
     const int64_t groups = (tiles + tpw - 1) / tpw;
     p.groups = (int32_t)groups;
-    const int64_t ranges = (groups * p.B + 7) / 8 * 8;
+    int64_t ranges = (groups * p.B + 7) / 8 * 8;
+    // Several sequences of possibly different lengths: ranges sized from the actual lengths so
+    // that all of them run in one round of one workgroup per compute unit.  With
+    // T = ceil(total / (R - B)) tiles per range there are at most total/T + B <= R ranges,
+    // R = 256 / (row groups); used when B <= R/2 and the largest T the partition can produce,
+    // ceil(B * tiles / (R - B)), still fits the page-table staging.
+    const int64_t R = 256 / (p.Q / QB);
+    p.balanced = 0;
+    if (p.B >= 2 && 2 * p.B <= R && (p.B * tiles + (R - p.B) - 1) / (R - p.B) <= max_tpw) {
+      p.balanced = (int32_t)(R - p.B);
+      ranges = (R + 7) / 8 * 8;
+    }
     const dim3 grid((unsigned)(ranges * (p.Q / QB)));
     const bool f8 = k_dtype == DSA_FP8_E4M3FN;
 #define DSA_IDX_MFMA(F8, CT, QBV) hipLaunchKernelGGL((indexer_mfma_kernel<F8, CT, QBV>), grid, dim3(kThreadsI), 0, s, p)
