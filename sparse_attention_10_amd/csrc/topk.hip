@@ -600,6 +600,30 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkParams p) {
       rb[0] = 0;
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) rb[w + 1] = rb[w] + wave_cnt[w];
+      if (cnt <= 64u) {
+        // few candidates (the usual case): each wave holds them one per lane and finds T by a
+        // ballot-count bit search over all bits below the first digit's prefix, no histogram
+        uint32_t c1 = 0u;                            // 0 never matches a prefix
+        if ((uint32_t)lane < cnt) {
+          int w = 0;
+#pragma unroll
+          for (int ww = 1; ww < kWaves; ++ww) w += (uint32_t)lane >= rb[ww];
+          c1 = cand_key[w * kCandPerWave + ((uint32_t)lane - rb[w])];
+        }
+        for (int bit = 31 - plen; bit >= 0; --bit) {
+          const uint32_t m = pmask | (1u << bit), v = pval | (1u << bit);
+          const uint32_t cb = (uint32_t)__popcll(__ballot((c1 & m) == v));
+          if (cb >= kr) pval = v;
+          else kr -= cb;
+          pmask = m;
+        }
+        T = pval;
+        for (int j = lane; j < (int)wave_cnt[wave]; j += 64) fix(wave * kCandPerWave + j);
+        Tg = T;
+        quota = kr;
+        __syncthreads();
+        goto threshold_done;
+      }
       // the second digit (the D2 key bits below the prefix): one candidate per thread is counted
       static_assert(kCandPerWave <= kThreads, "one candidate per thread");
       if ((uint32_t)tid < cnt) {
@@ -668,6 +692,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkParams p) {
     quota = kr;
     __syncthreads();
   }
+threshold_done:
 
   // ---- order-preserving output.  Every wave scans all units' counts (no barrier): a unit's
   // output offset counts the keys taken in earlier units, where the keys equal to Tg are taken
