@@ -60,10 +60,11 @@ constexpr int kOffECnt = kOffGCnt + kMaxUnits;           // u32 [kMaxUnits]
 constexpr int kOffOut = kOffECnt + kMaxUnits;            // i32 [kMaxTopK] winners' columns
 constexpr int kFineWords = kSmallBins + kSmallBins / 32; // second-digit histogram (padded layout)
 constexpr int kOffFine = kOffOut + kMaxTopK;             // u32 [kFineWords]
-// 64 lane-indexed dummy words: the output writes of the lanes that take nothing go there, so
-// that the per-key-row writes need no branch (and no exec-mask round trip)
+// 64 lane-indexed dummy words (and, seen from the candidate columns array, 64 more kCandCap
+// words further): the writes of the lanes that keep nothing go there, so that the per-key-row
+// writes need no branch (and no exec-mask round trip)
 constexpr int kOffDummy = kOffFine + kFineWords;
-static_assert(kOffDummy + 64 <= kHistWords, "LDS regions must fit in the histogram's space");
+static_assert(kOffDummy + kCandCap + 64 <= kHistWords, "LDS regions must fit in the histogram's space");
 static_assert(kUnitsPerLane <= 6, "unit scan layout");
 static_assert(kBinsPerThread % 4 == 0 && kBinsPerThread <= 64, "histogram layout");
 
@@ -545,14 +546,18 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkParams p) {
           any |= me[i];
         }
         if (any) {
+          // (lanes outside the bin write to their dummy words: cand_key + kOffDummy + lane and
+          // cand_col + kOffDummy + lane lie past every other region; an arithmetic select, since
+          // a conditional here compiles to exec-mask branches)
 #pragma unroll
           for (int i = 0; i < kG; ++i) {
             const uint32_t kk = key[j0 + i];
-            if (kk - t_lo <= t_hi - t_lo) {
-              const uint32_t pos = mbcnt(me[i], wave * kCandPerWave + wcount);
-              cand_key[pos] = kk;
-              cand_col[pos] = (uint32_t)(((wave * RV + j0 + i) << 6) + lane);
-            }
+            const uint32_t in = (uint32_t)-(int32_t)(kk - t_lo <= t_hi - t_lo);
+            const uint32_t at = mbcnt(me[i], wave * kCandPerWave + wcount);
+            const uint32_t ad = (uint32_t)(kOffDummy - kOffCandKey + lane);
+            const uint32_t pos = ad ^ ((at ^ ad) & in);
+            cand_key[pos] = kk;
+            cand_col[pos] = (uint32_t)(((wave * RV + j0 + i) << 6) + lane);
             wcount += (uint32_t)__popcll(me[i]);
           }
         }
@@ -774,9 +779,11 @@ threshold_done:
         for (int i = 0; i < kG; ++i) mt[i] = __ballot(key[j0 + i] >= t_take);
 #pragma unroll
         for (int i = 0; i < kG; ++i) {
-          const bool take = key[j0 + i] >= t_take;
-          out_s[take ? min(mbcnt(mt[i], obase), (uint32_t)kMaxTopK - 1u) : (uint32_t)(kOffDummy - kOffOut + lane)] =
-              ((wave * RV + j0 + i) << 6) + lane;
+          // (an arithmetic select: a conditional expression here compiles to exec-mask branches)
+          const uint32_t tk = (uint32_t)-(int32_t)(key[j0 + i] >= t_take);   // all ones if taken
+          const uint32_t at = min(mbcnt(mt[i], obase), (uint32_t)kMaxTopK - 1u);
+          const uint32_t ad = (uint32_t)(kOffDummy - kOffOut + lane);
+          out_s[ad ^ ((at ^ ad) & tk)] = ((wave * RV + j0 + i) << 6) + lane;
           obase += (uint32_t)__popcll(mt[i]);
         }
       }
