@@ -89,7 +89,7 @@ constexpr int kHi = 64, kDi = 128;
 constexpr int kSub = 32;                  // tokens per sub-tile (the MFMA N)
 constexpr int kWaves = 8;
 constexpr int kThreadsI = 64 * kWaves;
-constexpr int kTile = 256;                // grid granularity: tokens per tile
+constexpr int kTile = 256;                // grid granularity: tokens per tile (128 for one-row blocks)
 constexpr int kMaxTpwAny = 8;             // tiles per workgroup, any page size
 constexpr int kMaxTpwContig = 128;        // tiles per workgroup when 32 | P (pages of >= 32 tokens)
 constexpr int kMaxWgPages = kMaxTpwAny * kTile + 1;   // page-table entries a workgroup can span
@@ -171,6 +171,10 @@ __global__ __launch_bounds__(kThreadsI) void indexer_mfma_kernel(IndexerParams p
   using G = Geo<FP8, QB>;
   using Smem = ISmem<FP8, QB>;
   constexpr int NB = G::NB;
+  // key ranges are whole tiles of TL tokens: one stage for one-row blocks, so that a single
+  // short sequence still spreads over every compute unit
+  constexpr int TL = QB == 1 ? G::ST : kTile;
+  static_assert(kTile % TL == 0, "tile sizes");
   static_assert(NB >= 2 && (NB - 2) * (G::ND + 1) < 64, "ring depth");
   __shared__ __attribute__((aligned(16))) Smem sm;
 
@@ -198,7 +202,7 @@ __global__ __launch_bounds__(kThreadsI) void indexer_mfma_kernel(IndexerParams p
     // derives the same partition from seq_lens (thread i holds sequence i; B <= 128).
     const int i = threadIdx.x;
     const int Li = i < p.B ? min(p.seq_lens[i], p.max_seq_len) : 0;
-    const int ti = (max(Li, 0) + kTile - 1) / kTile;
+    const int ti = (max(Li, 0) + TL - 1) / TL;
     const int total = block_sum(ti, sm.part);
     // the smallest T (a few tries upwards from total / R) whose ranges fit R = balanced + B;
     // T = ceil(total / balanced) always does
@@ -224,7 +228,7 @@ __global__ __launch_bounds__(kThreadsI) void indexer_mfma_kernel(IndexerParams p
     grp_id = kr - sm.part[17];
     tpw = T;
   }
-  const int tile_base = grp_id * tpw * kTile;
+  const int tile_base = grp_id * tpw * TL;
   const int32_t* ptab_g = p.page_table + (int64_t)b * p.maxP;
 
   // Stage v covers tokens tile_base + v*ST ..; this thread's load c fills LDS bytes
@@ -251,7 +255,7 @@ __global__ __launch_bounds__(kThreadsI) void indexer_mfma_kernel(IndexerParams p
   // arrives (bounded by max_seq_len alone), so the first copies wait one round trip less
   int32_t pre_pe[NB - 1][NL];
   {
-    const int t_cap = min(tile_base + tpw * kTile, p.max_seq_len);
+    const int t_cap = min(tile_base + tpw * TL, p.max_seq_len);
 #pragma unroll
     for (int v = 0; v < NB - 1; ++v)
 #pragma unroll
@@ -262,7 +266,7 @@ __global__ __launch_bounds__(kThreadsI) void indexer_mfma_kernel(IndexerParams p
   }
   const int L = min(p.seq_lens[b], p.max_seq_len);
   if (tile_base >= L) return;                 // uniform early exit
-  const int tile_end = min(L, tile_base + tpw * kTile);
+  const int tile_end = min(L, tile_base + tpw * TL);
   const int pos_last = L - p.Q + qb0 + QB - 1;  // the block's largest position
   const int t_stop = min(tile_end, pos_last + 1);  // tokens at or past this are never scored
   const int nstage = t_stop > tile_base ? (t_stop - tile_base + G::ST - 1) / G::ST : 0;
@@ -736,13 +740,17 @@ hipError_t launch_indexer(const IndexerParams& p0, dsa_dtype_t q_dtype, dsa_dtyp
     return hipGetLastError();
   }
   if (indexer_uses_mfma(p.Hi, p.Di, q_dtype, k_dtype)) {
-    const int64_t tiles = ((int64_t)p.max_seq_len + kTile - 1) / kTile;
     // about one round of the 256 workgroups the GPU holds at once (one per CU): a workgroup's
     // q / page-table staging and first copies take several microseconds, paid once per CU
     const bool contig = p.P % kSub == 0;
     const int QB = (p.Q % 2 == 0) ? 2 : 1;
+    // tile size of the kernel's key ranges (one stage for one-row blocks)
+    static_assert(Geo<false, 1>::ST == 128 && Geo<true, 1>::ST == 128, "one-row stage");
+    const int TL = QB == 1 ? 128 : kTile;
+    const int64_t tiles = ((int64_t)p.max_seq_len + TL - 1) / TL;
     const int64_t work = tiles * p.B * (p.Q / QB);
-    const int max_tpw = contig ? kMaxTpwContig : kMaxTpwAny;
+    // (the same token spans as kMaxTpw* tiles of kTile tokens: the page-table staging bound)
+    const int max_tpw = (contig ? kMaxTpwContig : kMaxTpwAny) * (kTile / TL);
     int tpw = (int)(work / 256);
     tpw = tpw < 1 ? 1 : (tpw > max_tpw ? max_tpw : tpw);
     p.tiles_per_wg = tpw;
