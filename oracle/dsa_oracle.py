@@ -33,6 +33,12 @@ top-k + page-mapping transform, MLA sparse decode):
                       k >= context the sparse path must equal it, as colibri's
                       attention is dense and exact up to 2048 tokens (same page,
                       main-features section, DSA bullet).
+  7. cache_append     the write that precedes the path on every decode step: each
+                      new token's latent row and indexer key go to slot(b, pos(b,i));
+                      an fp8 cache stores per-token scale = max|row| / 448 and the
+                      nearest-even e4m3fn codes of row / scale (README usage section:
+                      fp8_e4m3 KV cache; Show HN main-features section: per-row
+                      scales, dequantized on use).
 
 Every array is decoded from its stored bits here (bf16 and fp8 e4m3fn decoders
 written from the format definitions) and all arithmetic is float64.
@@ -280,3 +286,68 @@ def decode_step(inp: dict, cfg) -> dict:
     out, lse = sparse_mla(inp["q_mla"], cfg.q_mla_dtype, inp["kv_cache"], cfg.kv_dtype,
                           inp["kv_scale"], slots, cfg.sm_scale)
     return {"scores": s, "idx": idx, "slots": slots, "out": out, "lse": lse}
+
+
+# ---------------------------------------------------------------------------
+# 7. cache append: the write of the new tokens' rows before the path reads them
+
+FP8_MAX = 448.0
+# below this row maximum the per-token scale is 1 (the all-zero row's scale): every value
+# then encodes to a signed zero, and no scale can underflow the binary32 range
+SCALE_FLOOR = 2.0 ** -100
+
+
+def encode_e4m3fn(y) -> np.ndarray:
+    """binary32 values -> OCP FP8 E4M3FN codes, round to nearest with ties to the
+    even code, from the format definition: the candidates are the finite
+    non-negative magnitudes of codes 0x00..0x7E (decode_e4m3fn), a magnitude
+    above 448 saturates to 448, and the sign bit is copied from y (so -0.0 and a
+    negative value that rounds to zero give 0x80).  NaN inputs are not defined."""
+    a = np.minimum(np.abs(np.asarray(y, dtype=np.float32).astype(np.float64)), FP8_MAX)
+    neg = np.signbit(np.asarray(y, dtype=np.float32))
+    vals = decode_e4m3fn(np.arange(0x7F, dtype=np.uint8))          # strictly increasing
+    hi = np.clip(np.searchsorted(vals, a, side="left"), 0, 0x7E)    # vals[hi-1] < a <= vals[hi]
+    lo = np.maximum(hi - 1, 0)
+    d_lo, d_hi = a - vals[lo], vals[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    return np.where(neg, code | np.uint8(0x80), code).astype(np.uint8)
+
+
+def quantize_row_fp8(x):
+    """One token row (float64 holding exact binary32 or bf16 values) -> (codes uint8,
+    scale float32).  scale = binary32(max|x| / 448), or 1 when max|x| < 2^-100 (the
+    all-zero row included); y = binary32(x / scale) value by value; codes =
+    encode_e4m3fn(y).  A binary64 quotient rounded to binary32 is the correctly
+    rounded binary32 quotient (53 >= 2*24 + 2 bits), so both roundings are the
+    IEEE single-precision divisions."""
+    x = np.asarray(x, dtype=np.float64)
+    amax = float(np.max(np.abs(x))) if x.size else 0.0
+    scale = np.float32(amax / FP8_MAX) if amax >= SCALE_FLOOR else np.float32(1.0)
+    y = (x / np.float64(scale)).astype(np.float32)
+    return encode_e4m3fn(y), scale
+
+
+def cache_append(cache, cache_dtype: str, scale, new_rows, new_dtype: str, seq_lens, page_table,
+                 q_per_seq: int, page_size: int):
+    """Write the Q new tokens of each sequence into the paged cache: the row of
+    query i of sequence b goes to slot(b, pos(b,i)), pos(b,i) = L_b - Q + i.
+    cache [num_slots, D] in cache_dtype ('f32', 'bf16' or 'fp8'); scale [num_slots]
+    f32 for 'fp8' (else None); new_rows [B, Q, D] in new_dtype ('f32' or 'bf16').
+    A cache of the rows' own dtype receives their stored bits; an fp8 cache
+    receives quantize_row_fp8 of each row and its scale.  Returns new arrays
+    (cache, scale); every other slot keeps its contents."""
+    cache = np.array(cache, copy=True)
+    scale = None if scale is None else np.array(scale, dtype=np.float32, copy=True)
+    x = dequantize(new_rows, new_dtype)
+    pos = query_positions(seq_lens, q_per_seq)
+    for b in range(pos.shape[0]):
+        slots = token_slots(np.asarray(page_table)[b], pos[b], page_size)
+        for i, s in enumerate(slots):
+            if cache_dtype == "fp8":
+                cache[s], scale[s] = quantize_row_fp8(x[b, i])
+            elif cache_dtype == new_dtype:
+                cache[s] = np.asarray(new_rows)[b, i]
+            else:
+                raise ValueError(f"no append from {new_dtype} rows into a {cache_dtype} cache")
+    return cache, scale

@@ -441,3 +441,108 @@ def test_decode_step_sparse_differs_from_dense_when_k_small():
                            cfg.page_size, cfg.sm_scale)
     assert np.abs(step["out"] - dense).max() > 1e-4
     assert (step["idx"] >= 0).sum() == 64
+
+
+# ---------------------------------------------------------------------------
+# cache append (the write of new tokens before the path reads them)
+
+def _e4m3_probe_values():
+    """Every finite e4m3fn magnitude, every midpoint between neighbours, one binary32
+    step either side of each midpoint, values above 448, signed zeros and a
+    log-uniform sweep, with both signs."""
+    import torch
+    mags = O.decode_e4m3fn(np.arange(0x7F, dtype=np.uint8))
+    mids = (mags[:-1] + mags[1:]) / 2                      # exact in binary32
+    m32 = mids.astype(np.float32)
+    near = np.concatenate([np.nextafter(m32, np.float32(0)), np.nextafter(m32, np.float32(1e9))])
+    big = np.array([448.0, 448.5, 455.0, 463.9], dtype=np.float32)
+    r = np.random.default_rng(7)
+    sweep = np.exp2(r.uniform(-14, 8.8, 4000)).astype(np.float32)
+    v = np.concatenate([mags.astype(np.float32), m32, near, big, sweep, np.float32([0.0])])
+    return np.concatenate([v, -v]).astype(np.float32), torch
+
+
+def test_encode_e4m3fn_matches_torch():
+    """The nearest-even encoder written from the format definition against torch's CPU
+    float8_e4m3fn conversion, an independent routine, on every code, every tie and its
+    binary32 neighbours (magnitudes below 464 so torch's conversion does not overflow)."""
+    v, torch = _e4m3_probe_values()
+    got = O.encode_e4m3fn(v)
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(got, ref)
+    assert O.encode_e4m3fn(np.float32([-0.0]))[0] == 0x80
+    assert O.encode_e4m3fn(np.float32([1e6, -1e6])).tolist() == [0x7E, 0xFE]    # saturates
+
+
+def test_encode_e4m3fn_round_trip_and_ties():
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    assert np.array_equal(O.encode_e4m3fn(O.decode_e4m3fn(codes).astype(np.float32)), codes)
+    # ties go to the even code: 1.0625 lies halfway between 1.0 (0x38) and 1.125 (0x39)
+    assert O.encode_e4m3fn(np.float32([1.0625, 1.1875, 2.0 ** -10, 3 * 2.0 ** -10])).tolist() == \
+        [0x38, 0x3A, 0x00, 0x02]
+
+
+def test_quantize_row_fp8_bounds_and_special_rows():
+    r = np.random.default_rng(11)
+    for _ in range(50):
+        x = (r.standard_normal(576) * np.exp2(r.uniform(-20, 20))).astype(np.float32).astype(np.float64)
+        codes, sc = O.quantize_row_fp8(x)
+        back = O.decode_e4m3fn(codes) * np.float64(sc)
+        # half a unit in the last place: 2^-4 relative for normal codes, 2^-10 * scale below 2^-6
+        assert np.all(np.abs(back - x) <= np.abs(x) * 2.0 ** -4 * (1 + 1e-6) + float(sc) * 2.0 ** -10)
+        j = int(np.argmax(np.abs(x)))
+        assert codes[j] == (0xFE if x[j] < 0 else 0x7E)           # the row maximum maps to 448
+        # power-of-two rescaling moves only the scale
+        c2, s2 = O.quantize_row_fp8(x * 2.0 ** 7)
+        assert np.array_equal(c2, codes) and s2 == np.float32(sc * 2.0 ** 7)
+    codes, sc = O.quantize_row_fp8(np.zeros(128))
+    assert sc == 1.0 and not codes.any()
+    codes, sc = O.quantize_row_fp8(np.full(8, -2.0 ** -110))
+    assert sc == 1.0 and np.all(codes == 0x80)
+
+
+def test_quantize_row_fp8_matches_the_input_generator():
+    """The seeded generator quantizes binary32 rows with torch's conversion; on rows that
+    are exact binary32 values both give the same codes and scales."""
+    r = np.random.default_rng(12)
+    x = (r.standard_normal((40, 576)) / 24).astype(np.float32).astype(np.float64)
+    x[3] = 0.0
+    gc, gs = dsa_inputs.encode_fp8_rows(x)
+    for i in range(x.shape[0]):
+        c, s = O.quantize_row_fp8(x[i])
+        assert np.array_equal(c, gc[i]) and s == gs[i]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8", "f32"])
+def test_cache_append_places_rows_and_leaves_the_rest(dtype):
+    r = np.random.default_rng(13)
+    P, B, Q, D = 4, 3, 3, 24
+    lens = np.array([3, 9, 14], dtype=np.int32)
+    pages = r.permutation(12).astype(np.int32)
+    pt = pages.reshape(B, 4)
+    n_slots = 12 * P
+    src_dtype = "f32" if dtype == "f32" else "bf16"
+    x = r.standard_normal((B, Q, D)).astype(np.float32)
+    new = x if src_dtype == "f32" else (x.view(np.uint32) >> 16).astype(np.uint16)
+    old = (r.integers(0, 255, (n_slots, D), dtype=np.uint8) if dtype == "fp8" else
+           r.standard_normal((n_slots, D)).astype(np.float32) if dtype == "f32" else
+           r.integers(0, 2 ** 15, (n_slots, D), dtype=np.uint16))
+    old_sc = r.random(n_slots).astype(np.float32) + 1 if dtype == "fp8" else None
+    cache, sc = O.cache_append(old, dtype, old_sc, new, src_dtype, lens, pt, Q, P)
+    written = set()
+    for b in range(B):
+        for i in range(Q):
+            t = lens[b] - Q + i
+            s = pt[b, t // P] * P + t % P                     # slot(b, t) written out by hand
+            written.add(s)
+            got = O.dequantize(cache[s:s + 1], dtype, None if sc is None else sc[s:s + 1])[0]
+            want = O.dequantize(new[b, i], src_dtype)
+            if dtype == "fp8":
+                assert np.all(np.abs(got - want) <= np.abs(want) * 2.0 ** -4 * (1 + 1e-6) + sc[s] * 2.0 ** -10)
+            else:
+                assert np.array_equal(got, want)
+    rest = np.array(sorted(set(range(n_slots)) - written))
+    assert len(written) == B * Q
+    assert np.array_equal(cache[rest], old[rest])
+    if sc is not None:
+        assert np.array_equal(sc[rest], old_sc[rest])
