@@ -194,8 +194,10 @@ def load_traffic(cfg_name, kernel):
         return None
     if d.get("kernel_source_hash") != kernel_hash():
         return None
-    k = d.get("kernels", {}).get(kernel)
-    return None if k is None else k.get("bytes_per_launch")
+    ks = d.get("kernels", {})
+    # a kernel with several template instances in the run is listed once per instance
+    hits = [v for n, v in ks.items() if n == kernel or n.startswith(kernel + "<")]
+    return hits[0].get("bytes_per_launch") if len(hits) == 1 else None
 
 
 def log(msg):
@@ -380,6 +382,19 @@ def main():
                             for _ in range(KS)], stream)
         stage["combine"] = ms / KS
         stage["mla"] -= stage["combine"]        # the MLA stage timing above includes its merge
+    # the write before the path (not part of the timed step): the step's B*Q new tokens go
+    # into both caches of each replica, bf16 rows into the workload's cache dtype
+    kv_new = (torch.randn((B, Q, 576), device=dev) / 24).to(torch.bfloat16)
+    k_new = (torch.randn((B, Q, cfg.idx_dim), device=dev) / math.sqrt(cfg.idx_dim)).to(torch.bfloat16)
+    _, ms = time_graph([(lambda j=j: dsa.dsa_kv_cache_append(
+        batches[j % R], kv_new, reps[j % R]["kv_cache"], reps[j % R]["kv_scale"], k_new, reps[j % R]["k_cache"],
+        reps[j % R]["k_scale"], stream=stream)) for j in range(KS)], stream)
+    esz = {"f32": 4, "bf16": 2, "fp8": 1}
+    per_tok = (576 + cfg.idx_dim) * 2 + 576 * esz[cfg.kv_dtype] + cfg.idx_dim * esz[cfg.key_dtype] + \
+        4 * (cfg.kv_dtype == "fp8") + 4 * (cfg.key_dtype == "fp8") + 4
+    append_info = dict(us=round(ms / KS * 1e3, 3), bytes=rows * per_tok + B * 4,
+                       kernel="cache_append_kernel", timing="hip-graph of launches, replicas cycled")
+    append_info["GBps"] = round(append_info["bytes"] / (append_info["us"] * 1e-6) / 1e9, 1)
     fl = step_flops(cfg, lens)
     stage_info = {
         "indexer": dict(us=stage["indexer"] * 1e3, bytes=by["indexer"], flops=fl["indexer"]),
@@ -440,6 +455,7 @@ def main():
         "timing": "hip-graph replay" if not args.eager else "eager",
         "stages": stage_info,
         "roofline": roof,
+        "outside_step": {"kv_cache_append": append_info},
     }
     if not args.no_cpu_baseline:
         log("cpu baseline (fp64 oracle)")

@@ -202,6 +202,34 @@ dsa_status_t dsa_decode_step(const dsa_decode_step_args_t *args,
                              void *workspace, size_t workspace_bytes, void *stream);
 size_t dsa_decode_step_workspace_size(const dsa_decode_step_args_t *args);
 
+/*
+ * Cache append: the write that precedes the path on every decode step (the README's usage
+ * section serves with an fp8_e4m3 KV cache; the Show HN page "Chay GLM 5.2 tren may tinh
+ * cham", main-features list, keeps per-row scales and dequantizes on use).  The row of new
+ * token i of sequence b goes to slot(b, pos(b,i)), pos(b,i) = L_b - Q + i, so seq_lens must
+ * already count the Q new tokens.
+ *   kv_new  [B, Q, 576]       f32 or bf16 new latent rows, or NULL to leave the latent cache
+ *   k_new   [B, Q, head_dim]  f32 or bf16 new indexer keys, or NULL to leave the key cache
+ *   kv_cache, k_cache         the paged caches of dsa_sparse_mla_decode / dsa_indexer_scores
+ *   kv_scale, k_scale         [num_slots] f32, written for fp8 caches, NULL otherwise
+ * Per destination dtype:
+ *   same dtype as the rows    the stored bits are copied (f32 -> f32, bf16 -> bf16)
+ *   DSA_FP8_E4M3FN            scale = max|row| / 448 (1 when max|row| < 2^-100, e.g. an
+ *                             all-zero row); codes = e4m3fn(row / scale), round to nearest
+ *                             with ties to even, magnitudes clamped to 448, the sign kept
+ *                             (-0 gives 0x80); both divisions are IEEE binary32 divisions
+ * Other pairs (f32 rows into a bf16 cache, anything into f32 from bf16) are DSA_ERR_UNSUPPORTED.
+ * Supported: head_dim a multiple of 8 in 8..1024.  Rows that are NaN or infinite are outside
+ * the supported set.  Two new tokens must not map to one slot (a valid page table ensures it).
+ * Every other slot is left as it was.
+ */
+dsa_status_t dsa_kv_cache_append(const dsa_batch_t *batch,
+                                 const void *kv_new, dsa_dtype_t kv_new_dtype,
+                                 void *kv_cache, dsa_dtype_t kv_dtype, float *kv_scale,
+                                 const void *k_new, dsa_dtype_t k_new_dtype, int32_t head_dim,
+                                 void *k_cache, dsa_dtype_t k_dtype, float *k_scale,
+                                 void *stream);
+
 const char *dsa_status_string(dsa_status_t status);
 const char *dsa_last_error(void);   /* thread-local detail for the last non-OK status */
 int32_t dsa_abi_version(void);

@@ -24,7 +24,7 @@ V_DIM = 512
 
 EXPORTS = ("dsa_indexer_scores", "dsa_topk", "dsa_topk_workspace_size", "dsa_page_map",
            "dsa_sparse_mla_decode", "dsa_sparse_mla_workspace_size", "dsa_sparse_mla_default_split",
-           "dsa_mla_combine", "dsa_decode_step", "dsa_decode_step_workspace_size",
+           "dsa_mla_combine", "dsa_decode_step", "dsa_decode_step_workspace_size", "dsa_kv_cache_append",
            "dsa_status_string", "dsa_last_error", "dsa_abi_version")
 
 
@@ -78,6 +78,7 @@ def lib() -> ctypes.CDLL:
             "dsa_mla_combine": (e, [i32, i32, i32, vp, vp, vp, vp, vp, vp]),
             "dsa_decode_step": (e, [ctypes.POINTER(DsaDecodeStepArgs), vp, sz, vp]),
             "dsa_decode_step_workspace_size": (sz, [ctypes.POINTER(DsaDecodeStepArgs)]),
+            "dsa_kv_cache_append": (e, [bp, vp, e, vp, e, vp, vp, e, i32, vp, e, vp, vp]),
             "dsa_status_string": (ctypes.c_char_p, [e]),
             "dsa_last_error": (ctypes.c_char_p, []),
             "dsa_abi_version": (i32, []),
@@ -229,3 +230,20 @@ def decode_step_workspace_bytes(args: DsaDecodeStepArgs) -> int:
 def dsa_decode_step(args: DsaDecodeStepArgs, workspace: Optional[torch.Tensor], stream=None):
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().dsa_decode_step(ctypes.byref(args), _ptr(workspace), nbytes, _stream(stream)))
+
+
+def dsa_kv_cache_append(batch: DsaBatch, kv_new: Optional[torch.Tensor], kv_cache: Optional[torch.Tensor],
+                        kv_scale: Optional[torch.Tensor], k_new: Optional[torch.Tensor] = None,
+                        k_cache: Optional[torch.Tensor] = None, k_scale: Optional[torch.Tensor] = None,
+                        stream=None):
+    """Write the new tokens' rows into their paged slots (see dsa.h): kv_new [B,Q,576] into
+    kv_cache [slots,576] (+ kv_scale for fp8), k_new [B,Q,Di] into k_cache [slots,Di] (+ k_scale).
+    Either pair may be None."""
+    def code(t):
+        return DSA_F32 if t is None else dtype_code(t)
+    head_dim = 0 if k_new is None else k_new.shape[-1]
+    _check(lib().dsa_kv_cache_append(ctypes.byref(batch), _ptr(kv_new), code(kv_new),
+                                     _ptr(kv_cache if kv_new is not None else None), code(kv_cache), _ptr(kv_scale),
+                                     _ptr(k_new), code(k_new), head_dim,
+                                     _ptr(k_cache if k_new is not None else None), code(k_cache), _ptr(k_scale),
+                                     _stream(stream)))

@@ -204,6 +204,23 @@ dsa_status_t run_mla(int64_t rows, const void* q, dsa_dtype_t q_dtype, const voi
   return launched(launch_mla(p, q_dtype, kv_dtype, s), "sparse MLA");
 }
 
+// One side (latent rows or indexer keys) of a cache append.
+dsa_status_t check_append_side(const char* what, const void* src, dsa_dtype_t sdt, const void* dst,
+                               dsa_dtype_t ddt, const float* scale, int32_t width) {
+  if (src == nullptr && dst == nullptr) return DSA_OK;
+  DSA_REQUIRE(src && dst, "cache_append: %s rows and cache must both be given or both be NULL", what);
+  DSA_REQUIRE(valid_dtype(sdt) && valid_dtype(ddt), "cache_append: invalid %s dtype", what);
+  DSA_SUPPORT(sdt == DSA_F32 || sdt == DSA_BF16, "cache_append: %s rows must be f32 or bf16", what);
+  DSA_SUPPORT(ddt == sdt || ddt == DSA_FP8_E4M3FN,
+              "cache_append: %s rows of dtype %d cannot go into a cache of dtype %d", what, (int)sdt, (int)ddt);
+  DSA_SUPPORT(width >= 8 && width <= 1024 && width % 8 == 0,
+              "cache_append: %s width %d must be a multiple of 8 in 8..1024", what, width);
+  DSA_REQUIRE(ddt != DSA_FP8_E4M3FN || scale != nullptr, "cache_append: an fp8 %s cache needs its scale", what);
+  DSA_REQUIRE(aligned(src, 16) && aligned(dst, 16) && (!scale || aligned(scale, 4)),
+              "cache_append: %s arrays must be 16-byte aligned", what);
+  return DSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -411,6 +428,37 @@ dsa_status_t dsa_decode_step(const dsa_decode_step_args_t* a, void* workspace, s
   const size_t mla_bytes = workspace_bytes - w.mla_off;
   return run_mla(rows, a->q_mla, a->q_mla_dtype, a->kv_cache, a->kv_dtype, a->kv_scale, b->num_slots, slots, a->top_k,
                  a->mla_heads, a->sm_scale, a->out, a->lse, w.ns, ws + w.mla_off, mla_bytes, s);
+}
+
+dsa_status_t dsa_kv_cache_append(const dsa_batch_t* b, const void* kv_new, dsa_dtype_t kv_new_dtype, void* kv_cache,
+                                 dsa_dtype_t kv_dtype, float* kv_scale, const void* k_new, dsa_dtype_t k_new_dtype,
+                                 int32_t head_dim, void* k_cache, dsa_dtype_t k_dtype, float* k_scale,
+                                 void* stream) {
+  DSA_TRY(check_batch(b));
+  DSA_REQUIRE(kv_new || k_new, "cache_append: no latent rows and no indexer keys given");
+  DSA_TRY(check_append_side("latent", kv_new, kv_new_dtype, kv_cache, kv_dtype, kv_scale, (int32_t)kRowDim));
+  DSA_TRY(check_append_side("key", k_new, k_new_dtype, k_cache, k_dtype, k_scale, head_dim));
+  DSA_TRY(check_device());
+  AppendParams p{};
+  p.seq_lens = b->seq_lens;
+  p.page_table = b->page_table;
+  p.kv_src = kv_new;
+  p.kv_dst = kv_new ? kv_cache : nullptr;
+  p.kv_scale = kv_dtype == DSA_FP8_E4M3FN ? kv_scale : nullptr;
+  p.k_src = k_new;
+  p.k_dst = k_new ? k_cache : nullptr;
+  p.k_scale = k_dtype == DSA_FP8_E4M3FN ? k_scale : nullptr;
+  p.rows = (int64_t)b->batch * b->q_per_seq;
+  p.Q = b->q_per_seq;
+  p.P = b->page_size;
+  p.maxP = b->max_pages_per_seq;
+  p.kv_width = (int32_t)kRowDim;
+  p.k_width = head_dim;
+  p.kv_src_dtype = kv_new_dtype;
+  p.kv_dst_dtype = kv_dtype;
+  p.k_src_dtype = k_new_dtype;
+  p.k_dst_dtype = k_dtype;
+  return launched(launch_cache_append(p, (hipStream_t)stream), "cache append");
 }
 
 }  // extern "C"

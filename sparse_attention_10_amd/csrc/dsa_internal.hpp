@@ -187,6 +187,23 @@ struct CombineParams {
   int32_t rows, H, n_split;
 };
 
+// Cache append: row r = b*Q + i of each source goes to slot(b, L_b - Q + i) of its cache.  A
+// NULL destination skips that cache.  Widths are multiples of 8, at most 1024.
+struct AppendParams {
+  const int32_t* seq_lens;
+  const int32_t* page_table;
+  const void* kv_src;
+  void* kv_dst;
+  float* kv_scale;
+  const void* k_src;
+  void* k_dst;
+  float* k_scale;
+  int64_t rows;
+  int32_t Q, P, maxP;
+  int32_t kv_width, k_width;
+  int32_t kv_src_dtype, kv_dst_dtype, k_src_dtype, k_dst_dtype;
+};
+
 // launchers (return hipGetLastError() of the launch)
 hipError_t launch_indexer(const IndexerParams& p, dsa_dtype_t q_dtype, dsa_dtype_t k_dtype,
                           hipStream_t s);
@@ -201,5 +218,6 @@ hipError_t launch_page_map(const int32_t* idx, int64_t total, int k, int Q, cons
 hipError_t launch_mla(const MlaParams& p, dsa_dtype_t q_dtype, dsa_dtype_t kv_dtype, hipStream_t s);
 hipError_t launch_combine(const CombineParams& p, hipStream_t s);
 int mla_default_split(int rows, int H, int k, dsa_dtype_t kv_dtype);
+hipError_t launch_cache_append(const AppendParams& p, hipStream_t s);
 
 }  // namespace dsa

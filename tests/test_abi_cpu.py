@@ -160,3 +160,27 @@ def test_valid_call_without_gpu_reports_instead_of_crashing(L):
         pytest.skip("a GPU is present")
     st = _indexer(L, _batch())
     assert st in (dsa.DSA_ERR_HIP, dsa.DSA_ERR_UNSUPPORTED)
+
+
+def _append(L, batch, **kw):
+    a = dict(kv=FAKE, kvd=dsa.DSA_BF16, kc=FAKE, kcd=dsa.DSA_BF16, ks=None,
+             k=FAKE, kd=dsa.DSA_BF16, Di=128, kk=FAKE, kkd=dsa.DSA_FP8_E4M3FN, kks=FAKE)
+    a.update(kw)
+    return L.dsa_kv_cache_append(ctypes.byref(batch), a["kv"], a["kvd"], a["kc"], a["kcd"], a["ks"],
+                                 a["k"], a["kd"], a["Di"], a["kk"], a["kkd"], a["kks"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(kv=None, k=None), 1),                       # nothing to append
+    (dict(kc=None), 1),                               # rows without a cache
+    (dict(kvd=dsa.DSA_F32), 2),                       # f32 rows into a bf16 cache
+    (dict(kvd=dsa.DSA_FP8_E4M3FN, kcd=dsa.DSA_FP8_E4M3FN, ks=FAKE), 2),   # fp8 rows
+    (dict(kks=None), 1),                              # fp8 key cache without scales
+    (dict(Di=100), 2),
+    (dict(Di=2048), 2),
+    (dict(k=FAKE + 8), 1),                            # misaligned rows
+    (dict(kvd=9), 1),
+])
+def test_cache_append_rejects(L, kw, status):
+    assert _append(L, _batch(), **kw) == status
+    assert len(L.dsa_last_error()) > 0

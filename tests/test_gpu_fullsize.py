@@ -97,9 +97,9 @@ def test_fullsize_c4_chunked_prefill():
     _check_rows(cfg, t, r, [(0, 0), (0, 1), (0, 2047), (0, 4094), (0, 4095)])
 
 
-@pytest.mark.skip(reason="the batch-32 ragged decode workload faulted the GPU once in this build's first "
-                         "benchmark run; no mistake in the code was found that explains it (see the design "
-                         "notes), so the case stays off the GPU until its cause is shown")
+@pytest.mark.skip(reason="the batch-32 ragged decode workload faulted the GPU once, on its first benchmark "
+                         "run; no mistake in the code was found that explains it, so the case stays off "
+                         "the GPU until its cause is shown")
 def test_fullsize_c3_ragged_batch():
     cfg, t, r = _run("c3")
     _check_rows(cfg, t, r, [(0, 0), (17, 0), (31, 0)])
