@@ -1035,6 +1035,8 @@ constexpr int kTDBytes = kTT * kRowDim * 2;               // 36864
 constexpr int kTDCopies = kTDBytes / 1024;                // 36 copies of 1 KiB per tile
 constexpr int kStepsD = kRowDim / 32;                     // 18 K steps of 32
 constexpr int kDBlocksD = kVDim / 16 / 8;                 // 4 output blocks of 16 per wave
+constexpr int kStageLd = kVDim + 16;                       // floats per staged output row
+static_assert(64 * kStageLd * 4 <= kRingD * kTDBytes, "the staged output must fit the tile ring");
 
 __device__ __forceinline__ int bf16_swz(int t) { return ((t >> 4) & 1) | (((t >> 1) & 1) << 1) | (((t >> 3) & 1) << 2); }
 // LDS byte offset of logical piece p of token t inside a tile buffer
@@ -1258,7 +1260,13 @@ __global__ __launch_bounds__(kNT) void mla_bf16d_kernel(MlaParams p) {
     __syncthreads();
   }
 
-  // ---- each wave writes its 64 output values of every head
+  // ---- output: each wave's 64 values of every head are normalised into the idle tile ring
+  // (heads at a padded stride, so the 16 heads of one store fall on different banks), then the
+  // workgroup stores whole 2 KiB head rows, 1 KiB per wave instruction.  Written straight from
+  // the accumulators, every store would scatter sixteen 64-byte pieces, which took 3.8 us per
+  // 128 KiB partial (35 GB/s per compute unit); staged, the partial leaves at the copy rate.
+  // (Every wave has passed the barrier after its last read of the ring.)
+  float* stage = reinterpret_cast<float*>(&sm.ring[0][0]);
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     if (g >= ngroups) break;
@@ -1269,21 +1277,26 @@ __global__ __launch_bounds__(kNT) void mla_bf16d_kernel(MlaParams p) {
     const float m0 = fmaxf(sm.m0[0][head], sm.m0[1][head]);
     const float rh = sm.redo ? (mh > -INFINITY ? mh : 0.f) : (m0 == -INFINITY ? 0.f : m0);
     const float inv = lh > 0.f ? 1.f / lh : 0.f;
-    float* dst;
-    if (p.n_split == 1) {
-      dst = p.out + ((int64_t)r * p.H + head) * kVDim + wave * 64 + grp * 4;
-      if (p.lse && wave == 0 && grp == 0)
-        p.lse[(int64_t)r * p.H + head] = lh > 0.f ? (rh + log2f(lh)) * kLn2 : -INFINITY;
-    } else {
-      const int64_t prow = ((int64_t)r * p.n_split + split) * p.H + head;
-      dst = p.part_o + prow * kVDim + wave * 64 + grp * 4;
-      if (wave == 0 && grp == 0) {
+    if (wave == 0 && grp == 0) {
+      if (p.n_split == 1) {
+        if (p.lse) p.lse[(int64_t)r * p.H + head] = lh > 0.f ? (rh + log2f(lh)) * kLn2 : -INFINITY;
+      } else {
+        const int64_t prow = ((int64_t)r * p.n_split + split) * p.H + head;
         p.part_m[prow] = lh > 0.f ? rh * kLn2 : -INFINITY;
         p.part_l[prow] = lh;
       }
     }
 #pragma unroll
-    for (int db = 0; db < kDBlocksD; ++db) *(f32x4*)(dst + db * 16) = o[g][db] * inv;
+    for (int db = 0; db < kDBlocksD; ++db)
+      *(f32x4*)(stage + head * kStageLd + wave * 64 + db * 16 + grp * 4) = o[g][db] * inv;
+  }
+  lds_barrier();
+  float* dst = p.n_split == 1 ? p.out + (int64_t)r * p.H * kVDim
+                              : p.part_o + ((int64_t)r * p.n_split + split) * p.H * kVDim;
+  const int n4 = p.H * (kVDim / 4);               // f32x4 pieces of the H rows
+  for (int e = threadIdx.x; e < n4; e += kNT) {
+    const int head = e >> 7, c = (e & 127) * 4;
+    *(f32x4*)(dst + head * kVDim + c) = *(const f32x4*)(stage + head * kStageLd + c);
   }
 }
 
