@@ -145,3 +145,29 @@ def test_cache_append_one_side_only_and_rejects():
     assert e.value.status == dsa.DSA_ERR_UNSUPPORTED
     torch.cuda.synchronize()
     assert not _host(kv_c).any()
+
+
+@pytest.mark.parametrize("name,lens,Q", [("c5", [700, 1200], 4), ("c2", [1500, 333], 1)])
+def test_append_then_decode_step_equals_dense_attention(name, lens, Q):
+    """The decode of a verify block: the Q new tokens are appended (bf16 rows into the
+    workload's caches), then the fused step runs on the updated caches with k >= context, so
+    its output must equal dense attention over the oracle's own appended caches."""
+    import dsa_inputs
+    from tests.gpu_helpers import batch_of, check_attention, run_step
+    cfg = dsa_inputs.scaled_config(name, lens, seed=301, q_per_seq=Q, top_k=max(lens))
+    inp = dsa_inputs.make_inputs(cfg)
+    t = dsa_inputs.to_torch(inp, cfg, DEV)
+    r = np.random.default_rng(302)
+    B = len(lens)
+    kv_new = _bf16_bits((r.standard_normal((B, Q, O.ROW_DIM)) / 24).astype(np.float32))
+    k_new = _bf16_bits((r.standard_normal((B, Q, cfg.idx_dim)) / np.sqrt(cfg.idx_dim)).astype(np.float32))
+    print(f"append + step {name}: lens {lens} Q={Q} caches {cfg.kv_dtype}/{cfg.key_dtype}", flush=True)
+    dsa.dsa_kv_cache_append(batch_of(cfg, t), _dev(kv_new, "bf16"), t["kv_cache"], t["kv_scale"],
+                            _dev(k_new, "bf16"), t["k_cache"], t["k_scale"])
+    res = run_step(cfg, t, debug=False)
+    kv_ref, kv_sc = O.cache_append(inp["kv_cache"], cfg.kv_dtype, inp["kv_scale"], kv_new, "bf16",
+                                   inp["seq_lens"], inp["page_table"], Q, cfg.page_size)
+    assert np.array_equal(_host(t["kv_cache"]), kv_ref)
+    do, dl = O.dense_mla(inp["q_mla"], cfg.q_mla_dtype, kv_ref, cfg.kv_dtype, kv_sc, inp["seq_lens"],
+                         inp["page_table"], Q, cfg.page_size, cfg.sm_scale)
+    check_attention(res["out"].cpu().numpy(), do, res["lse"].cpu().numpy(), dl)

@@ -299,7 +299,9 @@ def test_split_invariance_gpu(ns):
 
 
 STEP_CASES = [("c1", [4096], dict()), ("c2", [6000], dict()), ("c3", [4100, 2500, 9000], dict()),
-              ("c5", [5000, 3000], dict()), ("c4", [64 + 3000], dict(q_per_seq=64, top_k=512))]
+              ("c5", [5000, 3000], dict()), ("c4", [64 + 3000], dict(q_per_seq=64, top_k=512)),
+              # deeper speculative verify: draft depth 3 (4 rows per sequence, fp8 caches) and 2
+              ("c5", [5000, 3000, 2100], dict(q_per_seq=4)), ("c2", [4500, 2600], dict(q_per_seq=3))]
 
 
 @pytest.mark.parametrize("name,lens,kw", STEP_CASES, ids=[c[0] for c in STEP_CASES])
@@ -336,7 +338,8 @@ def test_decode_step_staged(name, lens, kw):
                 assert abs(row[tok] - kth) <= 2e-5 * np.abs(row).max()
 
 
-@pytest.mark.parametrize("name,lens,Q", [("c2", [1500], 1), ("c5", [700, 1200], 2), ("c1", [300], 1)])
+@pytest.mark.parametrize("name,lens,Q", [("c2", [1500], 1), ("c5", [700, 1200], 2), ("c1", [300], 1),
+                                         ("c5", [900, 1300, 260], 4)])
 def test_decode_step_dense_when_k_covers_context(name, lens, Q):
     """k >= context: the step must equal dense attention whatever the indexer's numerics."""
     cfg, inp, t = _case(name, lens, seed=107, top_k=max(lens), q_per_seq=Q)
