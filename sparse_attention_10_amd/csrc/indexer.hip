@@ -1,18 +1,21 @@
 // Lightning indexer on gfx950: s[b,i,t] = sum_h w[b,i,h] * ReLU(q[b,i,h,:] . k[slot(b,t),:]).
 //
 // The pages name this stage the "lightning-indexer GEMM" ("GLM-52 Runs on RTX 4090", section
-// "how did he do it"; renning22/glm-5.2-4090 README, section "how it works").  Two kernels:
+// "how did he do it"; renning22/glm-5.2-4090 README, section "how it works").  Three kernels:
 //
-//  * indexer_mfma_kernel (64 heads x 128 dims, bf16 q, bf16 or fp8 keys).  The contraction
-//    runs on v_mfma_f32_32x32x16_bf16 with the indexer heads as M and tokens as N, so one
-//    wave's accumulator holds, for each of its 32 tokens, 32 heads per lane half: the ReLU, the
-//    head weights and the head sum stay in registers plus one exchange between lane halves.
-//    Keys are read straight from HBM into the B operand: lane (token n, half h) loads bytes
-//    [h*128, h*128+128) of its key row, i.e. the contraction index is permuted so that each
-//    lane streams one contiguous run of its row; q is permuted the same way when it is staged.
-//    fp8 keys are widened to bf16 in registers (exact) and the per-token scale is applied after
-//    the head sum (it is positive, so it commutes with the ReLU).
+//  * indexer_reg_kernel (decode: 64 heads x 128 dims, bf16 q, bf16 or fp8 keys, up to 4 query
+//    rows of a sequence per workgroup).  v_mfma_f32_16x16x32_bf16 with 16 heads as M and 16
+//    tokens as N; keys stream HBM -> registers with 1 KB coalesced loads, turn around in a
+//    per-wave LDS area into the operand layout, and every key is read once for all the rows of
+//    its workgroup.  ReLU, head weights and the head sum stay in registers.
+//  * indexer_prefill_kernel (many query rows per sequence, bf16 keys): 16 rows per workgroup
+//    over a shared LDS ring of key stages, so each key byte feeds 16 rows and the matrix cores
+//    bound the kernel.
 //  * indexer_valu_kernel: any head count / dim / dtype pair, one token per thread, f32 math.
+// fp8 keys are widened to bf16 exactly and their per-token scale multiplies the head sum (it is
+// positive, so it commutes with the ReLU).
+#include <algorithm>
+
 #include "dsa_internal.hpp"
 
 namespace dsa {
@@ -71,55 +74,16 @@ __global__ __launch_bounds__(256) void indexer_valu_kernel(IndexerParams p) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// matrix-core path: Hi = 64, Di = 128, QB = 1 or 2 query rows per workgroup
-//
-// 8 waves (two per SIMD) stream the keys of one token range through an LDS ring of NB stages.
-// A stage holds ST = 32 * 8 / QB tokens; it is filled by direct-to-LDS copies (through a
-// buffer resource over the key rows) in which consecutive lanes fetch consecutive 16-byte
-// pieces of key rows, so each copy moves 1 KB in few cache lines, and piece p of row r is
-// stored at slot p ^ swz(r) of its LDS row so that the MFMA operand reads are free of bank
-// conflicts.  Every key is read from memory once per workgroup: with QB = 2 the waves 0-3 score
-// row 0 and the waves 4-7 row 1 on the same 32-token sub-tiles.  One barrier per stage (waiting
-// only for LDS operations): after it the stage has landed for every wave and the stage read
-// before it is free to be refilled.  The loop body reads LDS only through a restrict pointer
-// and writes it only through another (the copies), so the compiler's waits for its LDS reads
-// never cover the copies in flight.
+// shared by the matrix-core kernels (Hi = 64, Di = 128)
 
 constexpr int kHi = 64, kDi = 128;
-constexpr int kSub = 32;                  // tokens per sub-tile (the MFMA N)
-constexpr int kWaves = 8;
-constexpr int kThreadsI = 64 * kWaves;
-constexpr int kTile = 256;                // grid granularity: tokens per tile (128 for one-row blocks)
-constexpr int kMaxTpwAny = 8;             // tiles per workgroup, any page size
-constexpr int kMaxTpwContig = 128;        // tiles per workgroup when 32 | P (pages of >= 32 tokens)
-constexpr int kMaxWgPages = kMaxTpwAny * kTile + 1;   // page-table entries a workgroup can span
-static_assert(kMaxTpwContig * kTile / 32 + 1 <= kMaxWgPages, "page-table staging covers both layouts");
+constexpr int kSub = 32;                  // tokens per sub-tile of the prefill kernel (its MFMA N)
 
-template <bool FP8, int QB>
-struct Geo {
-  static constexpr int RB = FP8 ? kDi : 2 * kDi;       // key row bytes
-  static constexpr int WPR = kWaves / QB;              // waves per query row
-  // one row: the two waves of a sub-tile take 32 heads each (HS = 2) and add their head sums
-  // through LDS, so a stage is 128 tokens and the ring holds four; two rows: a wave takes all
-  // 64 heads of its sub-tiles
-  static constexpr int HS = QB == 1 ? 2 : 1;           // waves per sub-tile (head halves)
-  static constexpr int MBW = 2 / HS;                   // 32-head M-blocks per wave
-  static constexpr int SPS = WPR / HS;                 // sub-tile slots per stage
-  // sub-tiles per wave and stage: two for fp8 keys and two rows, so that a stage (and the
-  // barrier that closes it) covers 256 tokens
-  static constexpr int SPW = (FP8 && QB == 2) ? 2 : 1;
-  static constexpr int ST = kSub * SPS * SPW;          // tokens per stage
-  static constexpr int SB = ST * RB;                   // stage bytes
-  static constexpr int ND = SB / (kThreadsI * 16);     // 16-byte loads per thread per stage
-  static constexpr int NB = QB == 1 ? 4 : 3;           // ring depth (stages of 16 / 32 KB)
-  static constexpr int NSW = FP8 ? ST / 64 : 0;        // waves that also load the stage's scales
-  static_assert(HS == 1 || SPW == 1, "a head-split wave keeps one pending head sum per stage");
-};
+// 16-byte piece slot swizzle of a key row staged in LDS (bank-conflict-free operand reads)
 template <bool FP8>
 __device__ __forceinline__ int swz(int r) { return FP8 ? ((r >> 1) & 7) : (r & 15); }
 
-// Sum and inclusive prefix sum of one int per thread over the 512-thread workgroup (wave
-// shuffles, then the 8 wave totals through LDS; `red` holds at least 8 ints).
+// Inclusive prefix sum of one int per lane over a wave.
 __device__ __forceinline__ int wave_incl_scan_i(int v) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
@@ -129,405 +93,6 @@ __device__ __forceinline__ int wave_incl_scan_i(int v) {
   }
   return v;
 }
-__device__ __forceinline__ int block_incl_scan(int v, int32_t* red) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int w = wave_incl_scan_i(v);
-  if (lane == 63) red[wave] = w;
-  __syncthreads();
-  int before = 0;
-#pragma unroll
-  for (int k = 0; k < kThreadsI / 64; ++k) before += k < wave ? red[k] : 0;
-  __syncthreads();
-  return w + before;
-}
-__device__ __forceinline__ int block_sum(int v, int32_t* red) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int w = wave_incl_scan_i(v);
-  if (lane == 63) red[wave] = w;
-  __syncthreads();
-  int t = 0;
-#pragma unroll
-  for (int k = 0; k < kThreadsI / 64; ++k) t += red[k];
-  __syncthreads();
-  return t;
-}
-
-// Shared memory of indexer_mfma_kernel: ring stage = keys, then (fp8) their per-token scales.
-template <bool FP8, int QB>
-struct ISmem {
-  uint8_t ring[Geo<FP8, QB>::NB][Geo<FP8, QB>::SB + (FP8 ? Geo<FP8, QB>::ST * 4 : 0)];
-  __bf16 q[QB][kHi][kDi];
-  float w[QB][kHi];
-  int32_t pt[kMaxWgPages];
-  float xs[2][4][kSub];    // one row: head sums of heads 32..63, by stage parity and sub-tile
-  int32_t part[20];        // the balanced partition: wave partial sums, then (b, first range, ranges)
-};
-
-
-// CONTIG (32 divides P): a sub-tile's 32 tokens are one 32-aligned run inside one page, so its
-// key rows are contiguous in the cache and one page lookup per sub-tile gives every address.
-template <bool FP8, bool CONTIG, int QB>
-__global__ __launch_bounds__(kThreadsI) void indexer_mfma_kernel(IndexerParams p) {
-  using G = Geo<FP8, QB>;
-  using Smem = ISmem<FP8, QB>;
-  constexpr int NB = G::NB;
-  // key ranges are whole tiles of TL tokens: one stage for one-row blocks, so that a single
-  // short sequence still spreads over every compute unit
-  constexpr int TL = QB == 1 ? G::ST : kTile;
-  static_assert(kTile % TL == 0, "tile sizes");
-  static_assert(NB >= 2 && (NB - 2) * (G::ND + 1) < 64, "ring depth");
-  __shared__ __attribute__((aligned(16))) Smem sm;
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // One workgroup = QB query rows x one key range (p.tiles_per_wg tiles of one sequence).  Key
-  // ranges are numbered over all sequences, kr = b * groups + g, and the grid is ordered so that
-  // the Q/QB row groups of one key range get ids 8 apart (ids go to the 8 XCDs round-robin):
-  // they run on one XCD, close together, and the groups after the first read the keys from its
-  // L2.   id = 8NQ*m + 8*i + j  ->  row group i, key range kr = 8m + j
-  const int nq = p.Q / QB;
-  const int blk = (int)blockIdx.x / (8 * nq);
-  const int rem = (int)blockIdx.x - blk * 8 * nq;
-  const int kr = 8 * blk + (rem & 7);
-  const int qb0 = (rem >> 3) * QB;            // first query row of the block
-  int b, grp_id, tpw;                         // sequence, range within it, tiles per range
-  if (p.balanced == 0) {
-    if (kr >= p.B * p.groups) return;         // grid padding (uniform)
-    b = kr / p.groups;
-    grp_id = kr - b * p.groups;
-    tpw = p.tiles_per_wg;
-  } else {
-    // Ranges of T tiles over each sequence's own length: T = ceil(total tiles / p.balanced),
-    // sequence b gets ceil(tiles_b / T) ranges, numbered in sequence order.  Every workgroup
-    // derives the same partition from seq_lens (thread i holds sequence i; B <= 128).
-    const int i = threadIdx.x;
-    const int Li = i < p.B ? min(p.seq_lens[i], p.max_seq_len) : 0;
-    const int ti = (max(Li, 0) + TL - 1) / TL;
-    const int total = block_sum(ti, sm.part);
-    // the smallest T (a few tries upwards from total / R) whose ranges fit R = balanced + B;
-    // T = ceil(total / balanced) always does
-    const int R = p.balanced + p.B;
-    int T = max(1, (total + R - 1) / R);
-    const int T_safe = max(1, (total + p.balanced - 1) / p.balanced);
-    for (int it = 0; it < 4 && T < T_safe; ++it) {
-      const int cnt = block_sum((ti + T - 1) / T, sm.part);
-      if (cnt <= R) break;
-      T = min(T_safe, max(T + 1, (int)(((int64_t)T * cnt + R - 1) / R)));
-    }
-    if (T < T_safe && block_sum((ti + T - 1) / T, sm.part) > R) T = T_safe;
-    const int gi = (ti + T - 1) / T;
-    const int incl = block_incl_scan(gi, sm.part);
-    if (i < p.B && kr >= incl - gi && kr < incl) {
-      sm.part[16] = i;
-      sm.part[17] = incl - gi;
-    }
-    if (i == kThreadsI - 1) sm.part[18] = incl;   // ranges in all
-    __syncthreads();
-    if (kr >= sm.part[18]) return;            // (uniform)
-    b = sm.part[16];
-    grp_id = kr - sm.part[17];
-    tpw = T;
-  }
-  const int tile_base = grp_id * tpw * TL;
-  const int32_t* ptab_g = p.page_table + (int64_t)b * p.maxP;
-
-  // Stage v covers tokens tile_base + v*ST ..; this thread's load c fills LDS bytes
-  // [off, off+16) of the stage, off = ((c*8 + wave)*64 + lane)*16: row r = off / RB and slot
-  // off % RB / 16, fetched from piece (slot ^ swz(r)) of that token's key row.
-  int lane_row[G::ND];     // stage row of this lane's piece in copy c
-  int lane_boff[G::ND];    // byte offset of that piece inside its key row
-#pragma unroll
-  for (int c = 0; c < G::ND; ++c) {
-    const int off = ((c * kWaves + wave) * 64 + lane) * 16;
-    const int r = off / G::RB, q = (off % G::RB) / 16;
-    lane_row[c] = r;
-    lane_boff[c] = 16 * (q ^ swz<FP8>(r));
-  }
-  const bool scale_wave = FP8 && wave < G::NSW;
-  // token whose cache row copy c (c = ND: the scale copy) of stage v starts at
-  auto tok = [&](int v, int c) {
-    const int t0 = tile_base + v * G::ST;
-    if (c == G::ND) return t0 + wave * 64 + lane;
-    return CONTIG ? t0 + (lane_row[c] & ~(kSub - 1)) : t0 + lane_row[c];
-  };
-  constexpr int NL = G::ND + (FP8 ? 1 : 0);
-  // the page-table entries of the first NB-1 stages are requested before the sequence length
-  // arrives (bounded by max_seq_len alone), so the first copies wait one round trip less
-  int32_t pre_pe[NB - 1][NL];
-  {
-    const int t_cap = min(tile_base + tpw * TL, p.max_seq_len);
-#pragma unroll
-    for (int v = 0; v < NB - 1; ++v)
-#pragma unroll
-      for (int c = 0; c < NL; ++c) {
-        const int t = tok(v, c);
-        pre_pe[v][c] = t < t_cap && (c < G::ND || scale_wave) ? ptab_g[t / p.P] : 0;
-      }
-  }
-  const int L = min(p.seq_lens[b], p.max_seq_len);
-  if (tile_base >= L) return;                 // uniform early exit
-  const int tile_end = min(L, tile_base + tpw * TL);
-  const int pos_last = L - p.Q + qb0 + QB - 1;  // the block's largest position
-  const int t_stop = min(tile_end, pos_last + 1);  // tokens at or past this are never scored
-  const int nstage = t_stop > tile_base ? (t_stop - tile_base + G::ST - 1) / G::ST : 0;
-
-  const int ri = wave / G::WPR;               // the row this wave scores
-  const int wl = wave - ri * G::WPR;
-  const int si = wl % G::SPS;                 // its first sub-tile within a stage is si * SPW
-  const int mh = wl / G::SPS;                 // its head half (one row), else 0
-  const int pos = L - p.Q + qb0 + ri;         // that row sees tokens t <= pos
-  const int n_in_sub = lane & 31;
-  const int half = lane >> 5;
-  const int page0 = tile_base / p.P;
-  const int npg = (t_stop > tile_base) ? (t_stop - 1) / p.P - page0 + 1 : 0;
-  const __amdgpu_buffer_rsrc_t k_rs = rows_rsrc(p.k_cache, G::RB, p.num_slots);
-  const __amdgpu_buffer_rsrc_t s_rs = rows_rsrc(FP8 ? (const void*)p.k_scale : p.k_cache, 4, FP8 ? p.num_slots : 0);
-
-  // Cache rows of this lane's copies of one stage: copy c fetches row slot[c] (CONTIG: the first
-  // row of the copy's 32-token run, which the lane offsets by r % 32), the scale copy row sslot.
-  struct Rows {
-    int32_t slot[G::ND];
-    int32_t sslot;
-  };
-  // copies of one stage into ring stage `dst` (keys, then the scales behind them)
-  auto issue = [&](uint8_t* __restrict__ dst, const Rows& rw) {
-#pragma unroll
-    for (int c = 0; c < G::ND; ++c) {
-      const int off = ((c * kWaves + wave) * 64) * 16;     // this copy's 1-KB block of the stage
-      const int row = CONTIG ? (int)rw.slot[c] + (lane_row[c] & (kSub - 1)) : (int)rw.slot[c];
-      lds_dma16_row(k_rs, row, lane_boff[c], dst + off);
-    }
-    if constexpr (FP8) {
-      if (scale_wave) lds_dma4_row(s_rs, (int)rw.sslot, dst + G::SB + wave * 256);
-    }
-  };
-  // the first NB-1 stages are requested before q is staged, from the prefetched page-table
-  // entries
-#pragma unroll
-  for (int v = 0; v < NB - 1; ++v)
-    if (v < nstage) {
-      Rows rw;
-#pragma unroll
-      for (int c = 0; c < G::ND; ++c) {
-        const int t = tok(v, c);
-        rw.slot[c] = t < t_stop ? pre_pe[v][c] * p.P + t % p.P : 0;
-      }
-      rw.sslot = 0;
-      if constexpr (FP8) {
-        const int t = tok(v, G::ND);
-        rw.sslot = scale_wave && t < t_stop ? pre_pe[v][G::ND] * p.P + t % p.P : 0;
-      }
-      issue(sm.ring[v], rw);
-    }
-
-  // stage q (bf16), w and the page-table entries of this workgroup's tokens
-  {
-    const int64_t row0 = (int64_t)b * p.Q + qb0;
-    const u32x4* qsrc = (const u32x4*)((const __bf16*)p.q + row0 * kHi * kDi);
-    u32x4* qdst = (u32x4*)&sm.q[0][0][0];
-    constexpr int kPer = QB * kHi * kDi / 8 / kThreadsI;
-    u32x4 qv[kPer];
-#pragma unroll
-    for (int c = 0; c < kPer; ++c) qv[c] = qsrc[c * kThreadsI + threadIdx.x];
-    const float wv = threadIdx.x < QB * kHi ? p.w[row0 * kHi + threadIdx.x] : 0.f;
-    constexpr int kPtPer = (kMaxWgPages + kThreadsI - 1) / kThreadsI;
-    int32_t pv[kPtPer];
-#pragma unroll
-    for (int c = 0; c < kPtPer; ++c)   // (uniform: only the blocks of entries the workgroup spans)
-      pv[c] = c * kThreadsI < npg ? ptab_g[page0 + min(c * kThreadsI + (int)threadIdx.x, npg - 1)] : 0;
-#pragma unroll
-    for (int c = 0; c < kPer; ++c) qdst[c * kThreadsI + threadIdx.x] = qv[c];
-    if (threadIdx.x < QB * kHi) (&sm.w[0][0])[threadIdx.x] = wv;
-#pragma unroll
-    for (int c = 0; c < kPtPer; ++c)
-      if (c * kThreadsI + (int)threadIdx.x < npg) sm.pt[c * kThreadsI + threadIdx.x] = pv[c];
-  }
-  __syncthreads();
-
-  // A fragments of this wave's row: lane (head m = lane%32 of M-block mb, half h) holds, for
-  // k-step s, q dims [h*64 + s*8, +8) (the contraction index is permuted the same way for keys)
-  // (this wave's M-blocks: mh*MBW .. +MBW)
-  bf16x8 afrag[G::MBW][8];
-#pragma unroll
-  for (int mb = 0; mb < G::MBW; ++mb)
-#pragma unroll
-    for (int s = 0; s < 8; ++s)
-      afrag[mb][s] = *(const bf16x8*)&sm.q[ri][(mh * G::MBW + mb) * 32 + n_in_sub][half * 64 + s * 8];
-  // head weights of the heads this lane holds: m = (mh*MBW + mb)*32 + g*8 + half*4 + j
-  float wr[G::MBW][4][4];
-#pragma unroll
-  for (int mb = 0; mb < G::MBW; ++mb)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const f32x4 wv = *(const f32x4*)&sm.w[ri][(mh * G::MBW + mb) * 32 + g * 8 + half * 4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) wr[mb][g][j] = wv[j];
-    }
-
-  const int P = p.P;
-  float* out = p.scores + ((int64_t)b * p.Q + qb0 + ri) * p.ld;
-  // Rows of the next stage to request are looked up one stage ahead, so the page-table reads
-  // from LDS are long done when the copies are issued.  Copy c (c < ND: keys, c = ND: scales)
-  // of stage v starts at token tok(v, c); (lk_pg, lk_of) = its page and offset in that page for
-  // the stage to look up next, stepped by ST tokens per stage (no division in the loop).
-  int lk_pg[NL], lk_of[NL];
-#pragma unroll
-  for (int c = 0; c < NL; ++c) {
-    const int t = tok(NB - 1, c);
-    lk_pg[c] = t / P;
-    lk_of[c] = t - lk_pg[c] * P;
-  }
-  const int st_pg = G::ST / P, st_of = G::ST - st_pg * P;
-  auto lookup = [&](const Smem* __restrict__ rd, int v) {
-    Rows rw;
-    rw.sslot = 0;
-#pragma unroll
-    for (int c = 0; c < NL; ++c) {
-      // (tokens at or past t_stop read an entry inside the staged table, or zeros past it,
-      // and take row 0)
-      const int32_t sl = rd->pt[lk_pg[c] - page0] * P + lk_of[c];
-      const int32_t val = tok(v, c) < t_stop ? sl : 0;
-      // (CONTIG: the copy's run start is the same for the whole wave)
-      if (c < G::ND) rw.slot[c] = CONTIG ? __builtin_amdgcn_readfirstlane(val) : val;
-      else rw.sslot = scale_wave ? val : 0;
-      lk_pg[c] += st_pg;
-      lk_of[c] += st_of;
-      if (lk_of[c] >= P) {
-        lk_of[c] -= P;
-        ++lk_pg[c];
-      }
-    }
-    return rw;
-  };
-  Rows next = lookup(&sm, NB - 1);
-
-  // The head reduction of a sub-tile runs one stage late: the MFMAs of stage v are issued next
-  // to the ReLU / weight / head-sum work of stage v-1, so the matrix core and the vector ALU
-  // overlap.  (acc_prev, t_prev, ks_prev) = stage v-1's accumulators, lane token and scale.
-  f32x16 acc_prev[G::MBW];
-#pragma unroll
-  for (int mb = 0; mb < G::MBW; ++mb) acc_prev[mb] = f32x16{};
-  int t_prev = -1, par_prev = 0;
-  float ks_prev = 0.f;
-  // one row (HS = 2): the head half 0 waves keep the head sum of heads 0..31 of stage u (pend_*)
-  // until, after the next barrier, the half 1 waves' sum of heads 32..63 is in xs[u & 1]
-  float pend_part = 0.f, pend_ks = 0.f;
-  int pend_t = -1, pend_par = 0;
-  auto store = [&](int t, float part, float ks) {
-    if (half == 0 && t >= 0 && t < tile_end) out[t] = t <= pos ? part * ks : -INFINITY;
-  };
-  auto complete = [&](const Smem* __restrict__ rd) {   // (HS = 2, head half 0)
-    if (pend_t >= 0) store(pend_t, pend_part + rd->xs[pend_par][si][n_in_sub], pend_ks);
-    pend_t = -1;
-  };
-  auto finish = [&](Smem* __restrict__ rd, const f32x16 (&acc)[G::MBW], int t, float ks, int par) {
-    float part = 0.f;
-#pragma unroll
-    for (int mb = 0; mb < G::MBW; ++mb)
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj)   // ReLU as one integer max on the bits (negatives -> +0)
-          part = fmaf(wr[mb][g][jj], __int_as_float(max(__float_as_int(acc[mb][4 * g + jj]), 0)), part);
-    // add the other lane half's partial sum (lanes l and l ^ 32 hold the same token)
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
-    part = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-    if constexpr (G::HS == 1) {
-      store(t, part, ks);
-    } else if (t >= 0) {
-      if (mh == 1) {
-        if (half == 0) rd->xs[par][si][n_in_sub] = part;
-      } else {
-        pend_part = part;
-        pend_ks = ks;
-        pend_t = t;
-        pend_par = par;
-      }
-    }
-  };
-
-  // one stage: request stage v + NB - 1 into ring stage `dst` and look up the rows of stage
-  // v + NB; per sub-tile of this wave in stage v: B fragments (lane: token n, half h) from LDS,
-  // 32x32x16 MFMAs over the two 32-head M-blocks, then the head reduction of the sub-tile
-  // before it
-  auto compute = [&](Smem* __restrict__ rd, int v) {
-    if constexpr (G::HS == 2) {
-      if (mh == 0) complete(rd);   // stage v-2's sum: its other half was written before the barrier
-    }
-#pragma unroll
-    for (int j = 0; j < G::SPW; ++j) {
-      const int sub = si * G::SPW + j;
-      const int t = tile_base + v * G::ST + sub * kSub + n_in_sub;
-      const uint8_t* rows = &rd->ring[v % NB][sub * kSub * G::RB];
-      bf16x8 kf[8];
-      if constexpr (FP8) {
-#pragma unroll
-        for (int s2 = 0; s2 < 4; ++s2) {          // dims h*64 + 16*s2 .. +16 = piece 4h + s2
-          const u32x4 raw = *(const u32x4*)(rows + n_in_sub * G::RB + 16 * ((4 * half + s2) ^ swz<FP8>(n_in_sub)));
-          __bf16 tmp[16];
-#pragma unroll
-          for (int d = 0; d < 4; ++d) fp8x4_to_bf16x4(raw[d], tmp + 4 * d);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            kf[2 * s2][e] = tmp[e];
-            kf[2 * s2 + 1][e] = tmp[8 + e];
-          }
-        }
-      } else {
-#pragma unroll
-        for (int s = 0; s < 8; ++s)               // dims h*64 + 8s .. +8 = piece 8h + s
-          kf[s] = *(const bf16x8*)(rows + n_in_sub * G::RB + 16 * ((8 * half + s) ^ swz<FP8>(n_in_sub)));
-      }
-      const float ks = FP8 ? ((const float*)(&rd->ring[v % NB][G::SB]))[sub * kSub + n_in_sub] : 1.f;
-      // (sub-tiles wholly past the row's position are computed too, on valid rows, and written
-      // as -inf by the reduction)
-      f32x16 acc[G::MBW];
-#pragma unroll
-      for (int mb = 0; mb < G::MBW; ++mb) acc[mb] = f32x16{};
-#pragma unroll
-      for (int s = 0; s < 8; ++s)
-#pragma unroll
-        for (int mb = 0; mb < G::MBW; ++mb)
-          acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag[mb][s], kf[s], acc[mb], 0, 0, 0);
-      finish(rd, acc_prev, t_prev, ks_prev, par_prev);
-#pragma unroll
-      for (int mb = 0; mb < G::MBW; ++mb) acc_prev[mb] = acc[mb];
-      t_prev = t;
-      ks_prev = ks;
-      par_prev = v & 1;
-    }
-  };
-
-  for (int v = 0; v < nstage; ++v) {
-    // stage v must have landed: at most the loads of the later stages requested so far
-    // (v+1 .. v+NB-2) may still be outstanding (vector-memory loads complete in order)
-    const int later = min(NB - 2, nstage - 1 - v);
-    if (scale_wave) wait_vmcnt_later<G::ND + 1, NB - 2>(later);
-    else wait_vmcnt_later<G::ND, NB - 2>(later);
-    lds_barrier();   // stage v landed for every wave; stage v-1 is no longer read
-    if (v + NB - 1 < nstage) {
-      issue(sm.ring[(v + NB - 1) % NB], next);
-      if (v + NB < nstage) next = lookup(&sm, v + NB);
-    }
-    compute(&sm, v);
-  }
-  if constexpr (G::HS == 2) {
-    // stage nstage-2's other half was written in the last iteration; stage nstage-1's now
-    lds_barrier();
-    if (mh == 0) complete(&sm);
-    finish(&sm, acc_prev, t_prev, ks_prev, par_prev);
-    lds_barrier();
-    if (mh == 0) complete(&sm);
-  } else {
-    finish(&sm, acc_prev, t_prev, ks_prev, par_prev);
-  }
-  // tokens of [tile_base, tile_end) past the block's last position: -inf (their stages are not
-  // computed)
-  for (int t = max(t_stop, tile_base) + (int)threadIdx.x; t < tile_end; t += kThreadsI)
-#pragma unroll
-    for (int qq = 0; qq < QB; ++qq) p.scores[((int64_t)b * p.Q + qb0 + qq) * p.ld + t] = -INFINITY;
-}
-
 
 // ---------------------------------------------------------------------------------------------
 // matrix-core path for many query rows per sequence (a chunked prefill): Hi = 64, Di = 128, bf16
@@ -716,6 +281,335 @@ __global__ __launch_bounds__(kPfThreads) void indexer_prefill_kernel(IndexerPara
     out_b[(int64_t)(e / n_tail) * p.ld + t_tail + e % n_tail] = -INFINITY;
 }
 
+// ---------------------------------------------------------------------------------------------
+// matrix-core decode path, keys through registers (Hi = 64, Di = 128, bf16 q, bf16 or fp8 keys;
+// QB query rows of one sequence per workgroup)
+//
+// The contraction runs on v_mfma_f32_16x16x32_bf16 with 16 heads as M and a block of 16
+// consecutive tokens as N, so each lane ends with 4 heads of one token per M-block: ReLU, the
+// head weights and the sum over the lane's 16 heads of a row stay in registers, and the four
+// lane groups add up with two row swaps.  The fp8 per-token scale multiplies the head sum (it is
+// positive, so it commutes with the ReLU).
+//
+// Keys: a workgroup owns QB query rows and a range of 16-token blocks of one sequence; its waves
+// take the blocks in turn (wave w: blocks w, w + NW, ...), each keeping the loads of D blocks in
+// flight in a register ring.  Every load instruction reads 1 KB of whole key rows (lane i: 16
+// bytes at 16i), the access pattern that streams fastest from HBM.  Each wave then turns its
+// block around in a private 2-4 KB LDS area (written in load order, read in the MFMA operand
+// layout, 16-byte pieces XOR-swizzled per row): a wave's LDS accesses complete in order, so this
+// needs no barrier, and the waves never wait for each other after the initial staging of q
+// (rows padded so the A-fragment reads are free of bank conflicts), w and the range's
+// page-table entries.  The contraction index is permuted to the layout: in k-step s, lane group
+// g holds dims 32g + 8s .. +8 (q the same way); fp8 keys are widened to bf16 exactly.
+
+constexpr int kRB = 16;                 // tokens per block (the MFMA N)
+constexpr int kQPitch = kDi + 8;        // bf16 per staged q row
+constexpr int kRegMaxPages = 1024;      // page-table entries staged per workgroup
+
+template <bool FP8, int QB, int NW>
+struct RSmem {
+  uint8_t tr[NW][kRB * (FP8 ? kDi : 2 * kDi)];   // per-wave turnaround of one key block
+  __bf16 q[QB][kHi][kQPitch];
+  float w[QB][kHi];
+  int32_t pt[kRegMaxPages];
+  int32_t part[24];
+};
+
+// Sum / inclusive prefix sum of one int per thread over an NW-wave workgroup (red: >= NW ints).
+template <int NW>
+__device__ __forceinline__ int wg_incl_scan(int v, int32_t* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int w = wave_incl_scan_i(v);
+  if (lane == 63) red[wave] = w;
+  __syncthreads();
+  int before = 0;
+#pragma unroll
+  for (int k = 0; k < NW; ++k) before += k < wave ? red[k] : 0;
+  __syncthreads();
+  return w + before;
+}
+template <int NW>
+__device__ __forceinline__ int wg_sum(int v, int32_t* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int w = wave_incl_scan_i(v);
+  if (lane == 63) red[wave] = w;
+  __syncthreads();
+  int t = 0;
+#pragma unroll
+  for (int k = 0; k < NW; ++k) t += red[k];
+  __syncthreads();
+  return t;
+}
+
+template <bool FP8, bool CT, int QB, int NW, int D>
+__global__ __launch_bounds__(NW * 64) void indexer_reg_kernel(IndexerParams p) {
+  constexpr int NT = NW * 64;
+  constexpr int RBY = FP8 ? kDi : 2 * kDi;        // key row bytes
+  constexpr int PPR = RBY / 16;                   // 16-byte pieces per row: 8 or 16
+  constexpr int NLD = kRB * RBY / 1024;           // 1 KB loads per block: 2 or 4
+  constexpr int TPL = 1024 / RBY;                 // rows per load: 8 or 4
+  constexpr int MB = 4 * QB;                      // 16-head M-blocks
+  using Smem = RSmem<FP8, QB, NW>;
+  __shared__ __attribute__((aligned(16))) Smem sm;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15, g = lane >> 4;
+
+  // workgroup -> (key range kr, row group): the row groups of one key range get ids 8 apart, so
+  // they run on one XCD and the later ones read the keys from its L2
+  const int ng = (p.Q + QB - 1) / QB;
+  const int blk = (int)blockIdx.x / (8 * ng);
+  const int rem = (int)blockIdx.x - blk * 8 * ng;
+  const int kr = 8 * blk + (rem & 7);
+  const int q0 = (rem >> 3) * QB;
+  int b, blk0, nblk;                              // sequence, first block of the range, its blocks
+  if (p.balanced == 0) {
+    if (kr >= p.B * p.groups) return;             // grid padding (uniform)
+    b = kr / p.groups;
+    blk0 = (kr - b * p.groups) * p.tiles_per_wg;
+    nblk = p.tiles_per_wg;
+  } else {
+    // Ranges of T blocks over each sequence's own length: sequence b gets ceil(blocks_b / T)
+    // ranges, numbered in sequence order, at most R = balanced + B in all.  T is the smallest of
+    // a few tries upwards from total / R whose ranges fit; T = ceil(total / balanced) always
+    // does.  Every workgroup derives the same partition from seq_lens (thread i: sequence i).
+    const int i = threadIdx.x;
+    const int Li = i < p.B ? min(p.seq_lens[i], p.max_seq_len) : 0;
+    const int ti = (max(Li, 0) + kRB - 1) / kRB;
+    const int total = wg_sum<NW>(ti, sm.part);
+    const int R = p.balanced + p.B;
+    int T = max(1, (total + R - 1) / R);
+    const int T_safe = max(1, (total + p.balanced - 1) / p.balanced);
+    for (int it = 0; it < 4 && T < T_safe; ++it) {
+      const int cnt = wg_sum<NW>((ti + T - 1) / T, sm.part);
+      if (cnt <= R) break;
+      T = min(T_safe, max(T + 1, (int)(((int64_t)T * cnt + R - 1) / R)));
+    }
+    if (T < T_safe && wg_sum<NW>((ti + T - 1) / T, sm.part) > R) T = T_safe;
+    const int gi = (ti + T - 1) / T;
+    const int incl = wg_incl_scan<NW>(gi, sm.part);
+    if (i < p.B && kr >= incl - gi && kr < incl) {
+      sm.part[16] = i;
+      sm.part[17] = incl - gi;
+    }
+    if (i == NT - 1) sm.part[18] = incl;          // ranges in all
+    __syncthreads();
+    if (kr >= sm.part[18]) return;                // (uniform)
+    b = sm.part[16];
+    blk0 = (kr - sm.part[17]) * T;
+    nblk = T;
+  }
+  const int L = min(p.seq_lens[b], p.max_seq_len);
+  const int t_begin = blk0 * kRB;
+  if (t_begin >= L) return;                       // uniform early exit
+  const int t_end = min(L, (blk0 + nblk) * kRB);
+  const int nq = min(QB, p.Q - q0);               // live rows of this group
+  const int pos_last = L - p.Q + q0 + nq - 1;     // the group's largest position
+  const int t_stop = min(t_end, pos_last + 1);    // tokens at or past this are never scored
+  const int nb = t_stop > t_begin ? (t_stop - t_begin + kRB - 1) / kRB : 0;
+  const int nbw = nb > wave ? (nb - wave + NW - 1) / NW : 0;   // this wave's blocks
+  const int P = p.P;
+  const int page0 = t_begin / P;
+  const int npg = nb > 0 ? (t_stop - 1) / P - page0 + 1 : 0;
+  const int32_t* ptab_g = p.page_table + (int64_t)b * p.maxP;
+  const uint8_t* kc = (const uint8_t*)p.k_cache;
+
+  // cache row of token t (row 0 at or past t_stop: read, never scored)
+  auto slot_of = [&](int t, int c, auto&& pt_of) -> int64_t {
+    int pg, of;
+    if (p.p_shift >= 0) {
+      pg = t >> p.p_shift;
+      of = t & (P - 1);
+    } else {
+      pg = t / P;
+      of = t - pg * P;
+    }
+    return t < t_stop ? (int64_t)pt_of(pg, c) * P + of : 0;
+  };
+  // loads of this wave's block jj: load c, lane i -> row TPL*c + i / PPR of the block, piece
+  // i % PPR; fp8: the scale of token n.  Blocks past the wave's last one read row 0 (their
+  // results are never stored), so every ring slot is refilled on every iteration.
+  // CT (16 divides P): a block is 16 consecutive rows of one page, so one page lookup per block
+  // gives a wave-uniform first row and every lane a fixed offset (load c, lane i: bytes
+  // 1024c + 16i of the block).  Otherwise every lane looks up its own row.
+  auto blk_tok = [&](int jj) { return t_begin + (wave + jj * NW) * kRB; };
+  auto blk_row = [&](int jj, int32_t pe) -> int64_t {   // pe: page-table entry of the block's page
+    const int tb = blk_tok(jj);
+    if (tb >= t_stop) return 0;
+    const int pg = p.p_shift >= 0 ? (tb >> p.p_shift) : tb / P;
+    return (int64_t)__builtin_amdgcn_readfirstlane(pe) * P + (tb - pg * P);
+  };
+  auto keys_ct = [&](u32x4 (&dst)[NLD], int64_t row0) {
+    const uint8_t* base = kc + row0 * RBY;
+#pragma unroll
+    for (int c = 0; c < NLD; ++c) dst[c] = __builtin_nontemporal_load((const u32x4*)(base + 1024 * c + 16 * lane));
+  };
+  auto keys_any = [&](u32x4 (&dst)[NLD], int jj, auto&& pt_of) {
+    const int tb = blk_tok(jj);
+#pragma unroll
+    for (int c = 0; c < NLD; ++c) {
+      const int64_t slot = slot_of(tb + TPL * c + lane / PPR, c, pt_of);
+      dst[c] = __builtin_nontemporal_load((const u32x4*)(kc + slot * RBY + 16 * (lane % PPR)));
+    }
+  };
+
+  // prologue: the page-table entries of the first D blocks, q, w and the range's page-table
+  // entries are requested together; once they are in, the first D blocks' keys and scales
+  constexpr int NPE = NLD + (FP8 ? 1 : 0);
+  int32_t pe[D][NPE];
+#pragma unroll
+  for (int u = 0; u < D; ++u)
+#pragma unroll
+    for (int c = 0; c < NPE; ++c) {
+      const int t = blk_tok(u) + (c < NLD ? TPL * c + lane / PPR : n);
+      int pg = p.p_shift >= 0 ? (t >> p.p_shift) : t / P;
+      pe[u][c] = t < t_stop ? ptab_g[pg] : 0;
+    }
+  constexpr int kQPer = (QB * kHi * kDi / 8 + NT - 1) / NT;
+  u32x4 qv[kQPer];
+  const int64_t row0 = (int64_t)b * p.Q + q0;
+  {
+    const u32x4* qsrc = (const u32x4*)((const __bf16*)p.q + row0 * kHi * kDi);
+#pragma unroll
+    for (int c = 0; c < kQPer; ++c) {
+      const int e = c * NT + threadIdx.x;
+      qv[c] = (e < QB * kHi * kDi / 8 && e / (kHi * kDi / 8) < nq) ? qsrc[e] : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  const float wv0 = threadIdx.x < QB * kHi && (int)threadIdx.x < nq * kHi ? p.w[row0 * kHi + threadIdx.x] : 0.f;
+  constexpr int kPtPer = (kRegMaxPages + NT - 1) / NT;
+  int32_t pv[kPtPer];
+#pragma unroll
+  for (int c = 0; c < kPtPer; ++c)
+    pv[c] = c * NT < npg ? ptab_g[page0 + min(c * NT + (int)threadIdx.x, max(npg - 1, 0))] : 0;
+  u32x4 ring[D][NLD];
+  float ring_sc[D];
+#pragma unroll
+  for (int u = 0; u < D; ++u) {
+    auto pt_pro = [&](int, int c) { return pe[u][c]; };
+    if constexpr (CT) {
+      const int64_t r0 = blk_row(u, pe[u][0]);
+      keys_ct(ring[u], r0);
+      if constexpr (FP8) ring_sc[u] = (p.k_scale + r0)[n];
+    } else {
+      keys_any(ring[u], u, pt_pro);
+      if constexpr (FP8) ring_sc[u] = p.k_scale[slot_of(blk_tok(u) + n, NLD, pt_pro)];
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < kQPer; ++c) {
+    const int e = c * NT + threadIdx.x;
+    if (e < QB * kHi * kDi / 8) {
+      const int r = e / (kHi * kDi / 8), rest = e - r * (kHi * kDi / 8);
+      const int h = rest / (kDi / 8), d8 = rest - h * (kDi / 8);
+      *(u32x4*)&sm.q[r][h][8 * d8] = qv[c];
+    }
+  }
+  if (threadIdx.x < QB * kHi) (&sm.w[0][0])[threadIdx.x] = wv0;
+#pragma unroll
+  for (int c = 0; c < kPtPer; ++c)
+    if (c * NT + (int)threadIdx.x < npg) sm.pt[c * NT + threadIdx.x] = pv[c];
+  __syncthreads();
+
+  // A fragments: M-block mb = (row mb/4, heads 16(mb%4) .. +16), lane: head n, dims 32g + 8s
+  bf16x8 af[MB][4];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) af[mb][s] = *(const bf16x8*)&sm.q[mb >> 2][16 * (mb & 3) + n][32 * g + 8 * s];
+  Smem* __restrict__ rd = &sm;
+  auto pt_lds = [&](int pg, int) { return rd->pt[pg - page0]; };
+  // page-table entry of block jj's page from the staged table (0 past the scored tokens)
+  auto blk_pe = [&](int jj) -> int32_t {
+    const int tb = blk_tok(jj);
+    if (tb >= t_stop) return 0;
+    return rd->pt[(p.p_shift >= 0 ? (tb >> p.p_shift) : tb / P) - page0];
+  };
+  float* out = p.scores + row0 * p.ld;
+  const int pos0 = L - p.Q + q0;                  // position of the group's first row
+  uint8_t* tw = rd->tr[wave];
+  // turnaround layout: row r at r * RBY, piece c at slot c ^ (r % PPR)
+  int wr_off[NLD];
+#pragma unroll
+  for (int c = 0; c < NLD; ++c) {
+    const int r = TPL * c + lane / PPR, pc = lane % PPR;
+    wr_off[c] = r * RBY + 16 * (pc ^ (r % PPR));
+  }
+
+  // Per iteration jj (ring slot u = jj % D): block jj goes through the turnaround, block jj + D
+  // is requested into its ring slot, block jj's MFMAs and head reduction run, then the scale of
+  // block jj + D is requested into the slot block jj's scale has left.  CT: the page entry of
+  // block jj + 2D is read into the slot that held block jj + D's (a D-iteration lead, so the
+  // read is long done when it is used).
+  int32_t pgr[D];
+#pragma unroll
+  for (int u = 0; u < D; ++u) pgr[u] = CT ? blk_pe(u + D) : 0;
+  const int nbw_pad = (nbw + D - 1) / D * D;
+  for (int j0 = 0; j0 < nbw_pad; j0 += D) {
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+      const int jj = j0 + u;
+#pragma unroll
+      for (int c = 0; c < NLD; ++c) *(u32x4*)(tw + wr_off[c]) = ring[u][c];
+      int64_t row_next = 0;
+      if constexpr (CT) {
+        row_next = blk_row(jj + D, pgr[u]);
+        keys_ct(ring[u], row_next);
+        pgr[u] = blk_pe(jj + 2 * D);
+      } else {
+        keys_any(ring[u], jj + D, pt_lds);
+      }
+      // B fragments of token n: dims 32g + 8s .. +8 = bytes [32g, 32g + 32) (fp8: two pieces)
+      // or [64g, 64g + 64) (bf16: four pieces) of its row
+      bf16x8 kb[4];
+      if constexpr (FP8) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const u32x4 raw = *(const u32x4*)(tw + n * RBY + 16 * ((2 * g + h) ^ (n % PPR)));
+          kb[2 * h] = fp8x8_to_bf16x8(raw[0], raw[1]);
+          kb[2 * h + 1] = fp8x8_to_bf16x8(raw[2], raw[3]);
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) kb[s] = *(const bf16x8*)(tw + n * RBY + 16 * ((4 * g + s) ^ (n % PPR)));
+      }
+      f32x4 acc[MB];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+          acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mb][s], kb[s], acc[mb], 0, 0, 0);
+      const float ks = FP8 ? ring_sc[u] : 1.f;
+      const int tb = blk_tok(jj), t = tb + n;
+#pragma unroll
+      for (int qi = 0; qi < QB; ++qi) {
+        float s_ = 0.f;
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb) {
+          const f32x4 wv = *(const f32x4*)&rd->w[qi][16 * hb + 4 * g];
+#pragma unroll
+          for (int jx = 0; jx < 4; ++jx)   // ReLU as one integer max on the bits (negatives -> +0)
+            s_ = fmaf(wv[jx], __int_as_float(max(__float_as_int(acc[4 * qi + hb][jx]), 0)), s_);
+        }
+        s_ = lanes4_sum(s_);
+        if (g == 0 && qi < nq && jj < nbw && t < t_end) (out + (int64_t)qi * p.ld + tb)[n] = t <= pos0 + qi ? s_ * ks : -INFINITY;
+      }
+      // the scale of block jj + D goes into the slot this block's scale has just left
+      if constexpr (FP8) {
+        if constexpr (CT) ring_sc[u] = (p.k_scale + row_next)[n];
+        else ring_sc[u] = p.k_scale[slot_of(blk_tok(jj + D) + n, NLD, pt_lds)];
+      }
+    }
+  }
+  // tokens of the range past the group's last position: -inf (their blocks are not computed)
+  for (int t = t_begin + nb * kRB + (int)threadIdx.x; t < t_end; t += NT)
+#pragma unroll
+    for (int qi = 0; qi < QB; ++qi)
+      if (qi < nq) out[(int64_t)qi * p.ld + t] = -INFINITY;
+}
 }  // namespace
 
 bool indexer_uses_mfma(int Hi, int Di, dsa_dtype_t q_dtype, dsa_dtype_t k_dtype) {
@@ -740,46 +634,40 @@ hipError_t launch_indexer(const IndexerParams& p0, dsa_dtype_t q_dtype, dsa_dtyp
     return hipGetLastError();
   }
   if (indexer_uses_mfma(p.Hi, p.Di, q_dtype, k_dtype)) {
-    // about one round of the 256 workgroups the GPU holds at once (one per CU): a workgroup's
-    // q / page-table staging and first copies take several microseconds, paid once per CU
-    const bool contig = p.P % kSub == 0;
-    const int QB = (p.Q % 2 == 0) ? 2 : 1;
-    // tile size of the kernel's key ranges (one stage for one-row blocks)
-    static_assert(Geo<false, 1>::ST == 128 && Geo<true, 1>::ST == 128, "one-row stage");
-    const int TL = QB == 1 ? 128 : kTile;
-    const int64_t tiles = ((int64_t)p.max_seq_len + TL - 1) / TL;
-    const int64_t work = tiles * p.B * (p.Q / QB);
-    // (the same token spans as kMaxTpw* tiles of kTile tokens: the page-table staging bound)
-    const int max_tpw = (contig ? kMaxTpwContig : kMaxTpwAny) * (kTile / TL);
-    int tpw = (int)(work / 256);
-    tpw = tpw < 1 ? 1 : (tpw > max_tpw ? max_tpw : tpw);
-    p.tiles_per_wg = tpw;
-    p.p_shift = (p.P & (p.P - 1)) == 0 ? __builtin_ctz((unsigned)p.P) : -1;
-    const int64_t groups = (tiles + tpw - 1) / tpw;
+    // Keys straight into registers: QB rows per workgroup (one row group for Q <= 4), about one
+    // round of 256 workgroups (one per compute unit) per row group.
+    const int QB = p.Q <= 2 ? p.Q : (p.Q == 3 ? 3 : 4);
+    const int NW = QB <= 2 ? 8 : 4;
+    const int64_t ng = (p.Q + QB - 1) / QB;
+    const int64_t blocks = ((int64_t)p.max_seq_len + kRB - 1) / kRB;
+    const int64_t tb_max = std::max<int64_t>(1, (int64_t)(kRegMaxPages - 2) * p.P / kRB);
+    const int64_t R = std::max<int64_t>(1, 256 / ng);
+    int64_t tb = (blocks * p.B + R - 1) / R;
+    tb = std::min<int64_t>(std::max<int64_t>(tb, 1), tb_max);
+    int64_t groups = (blocks + tb - 1) / tb;
+    p.tiles_per_wg = (int32_t)tb;
     p.groups = (int32_t)groups;
-    int64_t ranges = (groups * p.B + 7) / 8 * 8;
-    // Several sequences of possibly different lengths: ranges sized from the actual lengths so
-    // that all of them run in one round of one workgroup per compute unit.  With
-    // T = ceil(total / (R - B)) tiles per range there are at most total/T + B <= R ranges,
-    // R = 256 / (row groups); used when B <= R/2 and the largest T the partition can produce,
-    // ceil(B * tiles / (R - B)), still fits the page-table staging.
-    const int64_t R = 256 / (p.Q / QB);
+    p.p_shift = (p.P & (p.P - 1)) == 0 ? __builtin_ctz((unsigned)p.P) : -1;
     p.balanced = 0;
-    if (p.B >= 2 && 2 * p.B <= R && (p.B * tiles + (R - p.B) - 1) / (R - p.B) <= max_tpw) {
+    int64_t ranges = p.B * groups;
+    // several sequences of possibly different lengths: ranges sized from the actual lengths
+    if (p.B >= 2 && 2 * p.B <= R && p.B <= NW * 64 && (p.B * blocks + (R - p.B) - 1) / (R - p.B) <= tb_max) {
       p.balanced = (int32_t)(R - p.B);
-      ranges = (R + 7) / 8 * 8;
+      ranges = R;
     }
-    const dim3 grid((unsigned)(ranges * (p.Q / QB)));
+    const dim3 grid((unsigned)((ranges + 7) / 8 * 8 * ng));
     const bool f8 = k_dtype == DSA_FP8_E4M3FN;
-#define DSA_IDX_MFMA(F8, CT, QBV) hipLaunchKernelGGL((indexer_mfma_kernel<F8, CT, QBV>), grid, dim3(kThreadsI), 0, s, p)
-    if (QB == 2) {
-      if (contig) { if (f8) DSA_IDX_MFMA(true, true, 2); else DSA_IDX_MFMA(false, true, 2); }
-      else { if (f8) DSA_IDX_MFMA(true, false, 2); else DSA_IDX_MFMA(false, false, 2); }
-    } else {
-      if (contig) { if (f8) DSA_IDX_MFMA(true, true, 1); else DSA_IDX_MFMA(false, true, 1); }
-      else { if (f8) DSA_IDX_MFMA(true, false, 1); else DSA_IDX_MFMA(false, false, 1); }
-    }
-#undef DSA_IDX_MFMA
+    const bool ct = p.P % kRB == 0;
+#define DSA_IDX_REG2(F8, QBV, NWV, DV)                                                                          \
+  do {                                                                                                       \
+    if (ct) hipLaunchKernelGGL((indexer_reg_kernel<F8, true, QBV, NWV, DV>), grid, dim3(NWV * 64), 0, s, p);  \
+    else hipLaunchKernelGGL((indexer_reg_kernel<F8, false, QBV, NWV, DV>), grid, dim3(NWV * 64), 0, s, p);    \
+  } while (0)
+    if (QB == 1) { if (f8) DSA_IDX_REG2(true, 1, 8, 4); else DSA_IDX_REG2(false, 1, 8, 3); }
+    else if (QB == 2) { if (f8) DSA_IDX_REG2(true, 2, 8, 3); else DSA_IDX_REG2(false, 2, 8, 2); }
+    else if (QB == 3) { if (f8) DSA_IDX_REG2(true, 3, 4, 4); else DSA_IDX_REG2(false, 3, 4, 3); }
+    else { if (f8) DSA_IDX_REG2(true, 4, 4, 3); else DSA_IDX_REG2(false, 4, 4, 2); }
+#undef DSA_IDX_REG2
     return hipGetLastError();
   }
   dim3 grid((unsigned)((p.max_seq_len + 255) / 256), (unsigned)p.Q, (unsigned)p.B);

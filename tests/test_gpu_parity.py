@@ -42,6 +42,15 @@ INDEXER_CASES = [
     # long contexts: several 128-token tiles per workgroup (work >= 4096 tiles)
     ("c2", [131072, 131072, 60000, 60000, 60001, 59999, 4097, 77], dict()),
     ("c5", [131072, 100000, 70000, 9000], dict()),                    # fp8, Q = 2, two tiles per workgroup
+    # rows of one sequence scored from one key read: 3 and 4 rows per workgroup, row groups
+    ("c2", [1000, 333], dict(q_per_seq=4)),
+    ("c5", [2000, 515], dict(q_per_seq=4)),
+    ("c5", [1500], dict(q_per_seq=3)),
+    ("c2", [700, 450], dict(q_per_seq=6)),
+    ("c5", [300 + 20], dict(q_per_seq=20)),
+    # page sizes that do not hold whole 16-token blocks
+    ("c2", [1000, 37], dict(page_size=24)),
+    ("c5", [500, 61], dict(page_size=1)),
 ]
 
 
