@@ -202,10 +202,11 @@ dsa_status_t dsa_decode_step(const dsa_decode_step_args_t *args,
                              void *workspace, size_t workspace_bytes, void *stream);
 size_t dsa_decode_step_workspace_size(const dsa_decode_step_args_t *args);
 
+
 /*
- * Cache append: the write that precedes the path on every decode step (the README's usage
- * section serves with an fp8_e4m3 KV cache; the Show HN page "Chay GLM 5.2 tren may tinh
- * cham", main-features list, keeps per-row scales and dequantizes on use).  The row of new
+ * Cache append: the write that precedes the path on every decode step (the renning22/glm-5.2-4090
+ * README's usage section serves with an fp8_e4m3 KV cache; one f32 scale per token row is this
+ * library's choice of granularity, which the pages do not fix).  The row of new
  * token i of sequence b goes to slot(b, pos(b,i)), pos(b,i) = L_b - Q + i, so seq_lens must
  * already count the Q new tokens.
  *   kv_new  [B, Q, 576]       f32 or bf16 new latent rows, or NULL to leave the latent cache

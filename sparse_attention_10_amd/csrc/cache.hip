@@ -1,9 +1,8 @@
 // Cache append: the write that precedes the sparse path on every decode step.  Each new token's
 // 576-wide latent row and its indexer key go to the token's paged slot; an fp8 cache receives a
 // per-token scale, max |row| / 448, and the nearest-even e4m3fn codes of row / scale (the
-// renning22/glm-5.2-4090 README, usage section, serves with an fp8_e4m3 KV cache; the Show HN
-// page "Chay GLM 5.2 tren may tinh cham", main-features list, keeps per-row scales and
-// dequantizes on use).
+// renning22/glm-5.2-4090 README, usage section, serves with an fp8_e4m3 KV cache; one f32 scale
+// per token row is this library's choice of granularity, not something the pages specify).
 //
 // One wave per (token, cache): the wave loads the row as 8-value chunks (lane l takes chunks l
 // and l + 64), reduces the row maximum across its 64 lanes, and stores the converted chunks

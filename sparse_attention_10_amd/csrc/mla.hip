@@ -769,8 +769,10 @@ __global__ __launch_bounds__(kNTX) void mla_fp8x_kernel(MlaParams p) {
       for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf((float)raw[i][e]));
     mx = lanes4_max(mx);
     // exponent of mx (mx = f * 2^ex, f in [1, 2)): qs = 7 - ex puts mx in [128, 256)
+    // (qs is capped at 126 so that 2^-qs stays a normal float: a head whose largest |q| is
+    // below 2^-119, subnormals included, keeps fewer significant bits, on logits of ~1e-36)
     const int ex = mx > 0.f ? (int)((__float_as_uint(mx) >> 23) & 255u) - 127 : 7;
-    const int qs = 7 - ex;
+    const int qs = min(7 - ex, 126);
     q_unscale = __uint_as_float((uint32_t)(127 - qs) << 23);
 #pragma unroll
     for (int b = 0; b < kKBlocksX; ++b) {

@@ -272,6 +272,27 @@ def test_sparse_mla_wide_logit_range(name, ns):
         assert abs(lg[0, 0, 3] - rl[0, 0, 3]) <= 1e-4 * abs(rl[0, 0, 3])
 
 
+@pytest.mark.parametrize("name", ["c5", "c2"])
+def test_sparse_mla_tiny_query_heads(name):
+    """Query heads far below the normal range: head 5's values are bf16 subnormals (about
+    2^-130), head 6 is all zeros.  The fp8 kernel scales each head's q by a power of two before
+    splitting it into e4m3 parts; that scale must stay finite for such heads.  Their logits are
+    ~0, so their outputs are the mean of the selected V rows."""
+    cfg, inp, _ = _case(name, [2000], seed=107, top_k=512, q_per_seq=1)
+    q = O.dequantize(inp["q_mla"], "bf16").copy()
+    q[0, 0, 5] *= 2.0 ** -125
+    q[0, 0, 6] = 0.0
+    inp["q_mla"] = dsa_inputs.encode_bf16(q)
+    assert np.abs(O.dequantize(inp["q_mla"], "bf16")[0, 0, 5]).max() < 2.0 ** -119
+    t = dsa_inputs.to_torch(inp, cfg, DEV)
+    rng = np.random.default_rng(13)
+    slots = _random_slots(cfg, rng, 512)
+    for ns in (1, 2):
+        out, lse = gpu_mla(cfg, t, torch.from_numpy(slots).to(DEV), n_split=ns)
+        ro, rl = oracle_mla(cfg, inp, slots)
+        check_attention(out.cpu().numpy(), ro, lse.cpu().numpy(), rl)
+
+
 def test_split_combine_parity_direct():
     rng = np.random.default_rng(9)
     rows, ns, H = 3, 5, 64
