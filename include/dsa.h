@@ -202,6 +202,21 @@ dsa_status_t dsa_decode_step(const dsa_decode_step_args_t *args,
                              void *workspace, size_t workspace_bytes, void *stream);
 size_t dsa_decode_step_workspace_size(const dsa_decode_step_args_t *args);
 
+/*
+ * The fused step for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same launches and results as
+ * dsa_decode_step, with the workspace taken from a scratch buffer of fixed size that the
+ * library holds on every device it runs on (dsa_decode_step_noalloc_max_bytes() = 128 MiB,
+ * held until the process ends).  The call allocates and frees nothing.
+ *   - A step whose workspace (dsa_decode_step_workspace_size) exceeds the scratch size is
+ *     rejected with DSA_ERR_WORKSPACE_TOO_SMALL before anything is enqueued; such steps (a
+ *     4096-row prefill chunk, whose score rows alone take 1 GiB) need dsa_decode_step.
+ *   - Every call on one GPU uses that GPU's single scratch buffer, whose contents carry over
+ *     between calls (no call relies on them).  Calls that may overlap on one GPU (several
+ *     streams or threads) race on it: the caller must order them, e.g. on one stream.
+ */
+dsa_status_t dsa_decode_step_noalloc(const dsa_decode_step_args_t *args, void *stream);
+size_t dsa_decode_step_noalloc_max_bytes(void);
 
 /*
  * Cache append: the write that precedes the path on every decode step (the renning22/glm-5.2-4090

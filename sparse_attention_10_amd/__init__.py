@@ -25,6 +25,7 @@ V_DIM = 512
 EXPORTS = ("dsa_indexer_scores", "dsa_topk", "dsa_topk_workspace_size", "dsa_page_map",
            "dsa_sparse_mla_decode", "dsa_sparse_mla_workspace_size", "dsa_sparse_mla_default_split",
            "dsa_mla_combine", "dsa_decode_step", "dsa_decode_step_workspace_size", "dsa_kv_cache_append",
+           "dsa_decode_step_noalloc", "dsa_decode_step_noalloc_max_bytes",
            "dsa_status_string", "dsa_last_error", "dsa_abi_version")
 
 
@@ -78,6 +79,8 @@ def lib() -> ctypes.CDLL:
             "dsa_mla_combine": (e, [i32, i32, i32, vp, vp, vp, vp, vp, vp]),
             "dsa_decode_step": (e, [ctypes.POINTER(DsaDecodeStepArgs), vp, sz, vp]),
             "dsa_decode_step_workspace_size": (sz, [ctypes.POINTER(DsaDecodeStepArgs)]),
+            "dsa_decode_step_noalloc": (e, [ctypes.POINTER(DsaDecodeStepArgs), vp]),
+            "dsa_decode_step_noalloc_max_bytes": (sz, []),
             "dsa_kv_cache_append": (e, [bp, vp, e, vp, e, vp, vp, e, i32, vp, e, vp, vp]),
             "dsa_status_string": (ctypes.c_char_p, [e]),
             "dsa_last_error": (ctypes.c_char_p, []),
@@ -230,6 +233,15 @@ def decode_step_workspace_bytes(args: DsaDecodeStepArgs) -> int:
 def dsa_decode_step(args: DsaDecodeStepArgs, workspace: Optional[torch.Tensor], stream=None):
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().dsa_decode_step(ctypes.byref(args), _ptr(workspace), nbytes, _stream(stream)))
+
+
+def dsa_decode_step_noalloc(args: DsaDecodeStepArgs, stream=None):
+    """The fused step on the library's fixed per-device scratch buffer (no workspace argument)."""
+    _check(lib().dsa_decode_step_noalloc(ctypes.byref(args), _stream(stream)))
+
+
+def decode_step_noalloc_max_bytes() -> int:
+    return lib().dsa_decode_step_noalloc_max_bytes()
 
 
 def dsa_kv_cache_append(batch: DsaBatch, kv_new: Optional[torch.Tensor], kv_cache: Optional[torch.Tensor],

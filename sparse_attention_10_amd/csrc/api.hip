@@ -378,7 +378,12 @@ size_t dsa_decode_step_workspace_size(const dsa_decode_step_args_t* a) {
   return step_ws(a).total;
 }
 
-dsa_status_t dsa_decode_step(const dsa_decode_step_args_t* a, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks of the fused step (everything but the workspace).
+dsa_status_t check_step(const dsa_decode_step_args_t* a) {
   DSA_REQUIRE(a != nullptr, "decode_step: args is NULL");
   const dsa_batch_t* b = &a->batch;
   DSA_TRY(check_indexer(b, a->q_idx, a->q_idx_dtype, a->w, a->k_cache, a->k_dtype, a->k_scale, a->idx_heads,
@@ -389,13 +394,13 @@ dsa_status_t dsa_decode_step(const dsa_decode_step_args_t* a, void* workspace, s
                     a->n_split));
   DSA_REQUIRE((!a->debug_idx || aligned(a->debug_idx, 4)) && (!a->debug_slots || aligned(a->debug_slots, 4)),
               "decode_step: debug arrays must be 4-byte aligned");
-  const StepWs w = step_ws(a);
-  if (workspace_bytes < w.total || (w.total > 0 && workspace == nullptr))
-    return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "decode_step: workspace needs %zu bytes (got %zu)", w.total,
-                workspace_bytes);
-  DSA_REQUIRE(w.total == 0 || aligned(workspace, 256), "decode_step: workspace must be 256-byte aligned");
-  DSA_TRY(check_device());
-  hipStream_t s = (hipStream_t)stream;
+  return DSA_OK;
+}
+
+// The launches of the fused step into a checked workspace of step_ws(a).total bytes or more.
+dsa_status_t launch_step(const dsa_decode_step_args_t* a, const StepWs& w, void* workspace, size_t workspace_bytes,
+                         hipStream_t s) {
+  const dsa_batch_t* b = &a->batch;
   uint8_t* ws = (uint8_t*)workspace;
   float* scores = a->debug_scores ? a->debug_scores : (float*)(ws + w.scores_off);
   int32_t* idx = a->debug_idx ? a->debug_idx : (int32_t*)(ws + w.idx_off);
@@ -428,6 +433,59 @@ dsa_status_t dsa_decode_step(const dsa_decode_step_args_t* a, void* workspace, s
   const size_t mla_bytes = workspace_bytes - w.mla_off;
   return run_mla(rows, a->q_mla, a->q_mla_dtype, a->kv_cache, a->kv_dtype, a->kv_scale, b->num_slots, slots, a->top_k,
                  a->mla_heads, a->sm_scale, a->out, a->lse, w.ns, ws + w.mla_off, mla_bytes, s);
+}
+
+// Scratch memory of dsa_decode_step_noalloc: one copy per device, zero-initialised when the
+// library is loaded on that device and kept until the process ends.  Host code reaches it
+// only through the device address hipGetSymbolAddress returns for the current device.
+constexpr size_t kScratchBytes = (size_t)128 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+std::atomic<void*> g_scratch[kMaxDevices];
+
+dsa_status_t scratch_of_current_device(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(DSA_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(DSA_ERR_UNSUPPORTED, "device ordinal %d out of range", dev);
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(DSA_ERR_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch[dev].store(p, std::memory_order_release);   // (a racing first call stores the same address)
+  }
+  *ptr = p;
+  return DSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+dsa_status_t dsa_decode_step(const dsa_decode_step_args_t* a, void* workspace, size_t workspace_bytes, void* stream) {
+  DSA_TRY(check_step(a));
+  const StepWs w = step_ws(a);
+  if (workspace_bytes < w.total || (w.total > 0 && workspace == nullptr))
+    return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "decode_step: workspace needs %zu bytes (got %zu)", w.total,
+                workspace_bytes);
+  DSA_REQUIRE(w.total == 0 || aligned(workspace, 256), "decode_step: workspace must be 256-byte aligned");
+  DSA_TRY(check_device());
+  return launch_step(a, w, workspace, workspace_bytes, (hipStream_t)stream);
+}
+
+size_t dsa_decode_step_noalloc_max_bytes(void) { return kScratchBytes; }
+
+dsa_status_t dsa_decode_step_noalloc(const dsa_decode_step_args_t* a, void* stream) {
+  DSA_TRY(check_step(a));
+  const StepWs w = step_ws(a);
+  if (w.total > kScratchBytes)
+    return fail(DSA_ERR_WORKSPACE_TOO_SMALL,
+                "decode_step_noalloc: the step needs %zu bytes of scratch, above the library's fixed %zu "
+                "(use dsa_decode_step with a caller workspace)", w.total, kScratchBytes);
+  DSA_TRY(check_device());
+  void* ptr = nullptr;
+  DSA_TRY(scratch_of_current_device(&ptr));
+  return launch_step(a, w, ptr, kScratchBytes, (hipStream_t)stream);
 }
 
 dsa_status_t dsa_kv_cache_append(const dsa_batch_t* b, const void* kv_new, dsa_dtype_t kv_new_dtype, void* kv_cache,

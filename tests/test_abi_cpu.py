@@ -184,3 +184,20 @@ def _append(L, batch, **kw):
 def test_cache_append_rejects(L, kw, status):
     assert _append(L, _batch(), **kw) == status
     assert len(L.dsa_last_error()) > 0
+
+
+def test_noalloc_step_rejects_oversized_steps_before_the_device(L):
+    """A 4096-row prefill chunk over 69632 tokens needs over 1 GiB of scores: beyond the fixed
+    scratch of the no-allocation step, which refuses it before any device call."""
+    a = dsa.DsaDecodeStepArgs()
+    a.batch = _batch(q_per_seq=4096, max_seq_len=69632, max_pages_per_seq=1088, num_slots=69632)
+    a.q_idx, a.q_idx_dtype, a.w = FAKE, dsa.DSA_BF16, FAKE
+    a.k_cache, a.k_dtype, a.k_scale = FAKE, dsa.DSA_BF16, None
+    a.idx_heads, a.idx_dim, a.top_k = 64, 128, 2048
+    a.q_mla, a.q_mla_dtype, a.kv_cache, a.kv_dtype, a.kv_scale = FAKE, dsa.DSA_BF16, FAKE, dsa.DSA_BF16, None
+    a.mla_heads, a.sm_scale, a.n_split, a.out, a.lse = 64, 1.0 / 24, 0, FAKE, None
+    assert L.dsa_decode_step_workspace_size(ctypes.byref(a)) > L.dsa_decode_step_noalloc_max_bytes()
+    assert L.dsa_decode_step_noalloc_max_bytes() == 128 << 20
+    assert L.dsa_decode_step_noalloc(ctypes.byref(a), None) == dsa.DSA_ERR_WORKSPACE_TOO_SMALL
+    assert b"scratch" in L.dsa_last_error()
+    assert L.dsa_decode_step_noalloc(None, None) == dsa.DSA_ERR_INVALID_ARGUMENT
