@@ -199,6 +199,32 @@ def make_inputs(cfg: DsaConfig, with_mla: bool = True, with_indexer: bool = True
     return out
 
 
+# tensor ids of the projection weights after attention (their own random streams)
+_T_WUV, _T_WO = 20, 21
+
+
+def make_up_projection_weights(n_heads: int, v_dim: int, d_model: int, seed: int):
+    """Synthetic weights of the projection after attention, as bf16 bit patterns:
+    w_uv [H, Dv, 512] ~ N(0,1)/sqrt(512) (per head, the value block of kv_b) and
+    w_o [Dm, H*Dv] ~ N(0,1)/sqrt(H*Dv) (o_proj)."""
+    r = np.random.default_rng([seed, _T_WUV])
+    w_uv = encode_bf16(r.standard_normal((n_heads, v_dim, V_DIM)) / math.sqrt(V_DIM))
+    r = np.random.default_rng([seed, _T_WO])
+    w_o = encode_bf16(r.standard_normal((d_model, n_heads * v_dim)) / math.sqrt(n_heads * v_dim))
+    return w_uv, w_o
+
+
+def make_up_projection_weights_torch(n_heads: int, v_dim: int, d_model: int, seed: int, device):
+    """The same kind of weights drawn in device memory (torch.bfloat16 tensors)."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed + 7919)
+    w_uv = (torch.randn((n_heads, v_dim, V_DIM), generator=g, device=device) / math.sqrt(V_DIM)).to(torch.bfloat16)
+    w_o = (torch.randn((d_model, n_heads * v_dim), generator=g, device=device) /
+           math.sqrt(n_heads * v_dim)).to(torch.bfloat16)
+    return w_uv, w_o
+
+
 def make_inputs_torch(cfg: DsaConfig, device, with_mla: bool = True, with_indexer: bool = True):
     """Draw the same kind of inputs directly in device memory with a seeded
     torch generator (for the full-size workloads, whose caches run to GBs).

@@ -37,8 +37,14 @@ top-k + page-mapping transform, MLA sparse decode):
                       new token's latent row and indexer key go to slot(b, pos(b,i));
                       an fp8 cache stores per-token scale = max|row| / 448 and the
                       nearest-even e4m3fn codes of row / scale (README usage section:
-                      fp8_e4m3 KV cache; Show HN main-features section: per-row
-                      scales, dequantized on use).
+                      fp8_e4m3 KV cache; one scale per token row is this library's
+                      choice of granularity).
+  8. latent_up_projection
+                      the step after the path: with MLA weight absorption the query
+                      has absorbed kv_b and the attention output is still in the
+                      512-wide latent space, so it is projected afterwards, per head
+                      by that head's value block of kv_b (W_UV), then by o_proj (W_O)
+                      (Show HN main-features section, MLA weight absorption bullet).
 
 Every array is decoded from its stored bits here (bf16 and fp8 e4m3fn decoders
 written from the format definitions) and all arithmetic is float64.
@@ -351,3 +357,21 @@ def cache_append(cache, cache_dtype: str, scale, new_rows, new_dtype: str, seq_l
             else:
                 raise ValueError(f"no append from {new_dtype} rows into a {cache_dtype} cache")
     return cache, scale
+
+
+# ---------------------------------------------------------------------------
+# 8. latent up-projection: the projection after attention of the weight-absorbed MLA
+
+def latent_up_projection(o, w_uv, w_o):
+    """o [R, H, 512] float (the attention output in the latent space), w_uv [H, Dv, 512]
+    bf16 bits (per head, the value block of kv_b), w_o [Dm, H*Dv] bf16 bits (o_proj):
+        v[r, h, j] = sum_d w_uv[h, j, d] * o[r, h, d]
+        y[r, m]    = sum_{h, j} w_o[m, h*Dv + j] * v[r, h, j]
+    Returns (y [R, Dm], v [R, H, Dv]) in float64."""
+    od = np.asarray(o, dtype=np.float64)
+    w1 = decode_bf16(w_uv)
+    w2 = decode_bf16(w_o)
+    R, H, _ = od.shape
+    v = np.einsum("rhd,hjd->rhj", od, w1)
+    y = v.reshape(R, -1) @ w2.T
+    return y, v

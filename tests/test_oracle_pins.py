@@ -546,3 +546,99 @@ def test_cache_append_places_rows_and_leaves_the_rest(dtype):
     assert np.array_equal(cache[rest], old[rest])
     if sc is not None:
         assert np.array_equal(sc[rest], old_sc[rest])
+
+
+# ---------------------------------------------------------------------------
+# latent up-projection (the projection after attention of the weight-absorbed MLA)
+
+def _bits(x):
+    return dsa_inputs.encode_bf16(np.asarray(x, dtype=np.float64))
+
+
+def test_up_projection_hand_example(golden):
+    g = golden["up_projection"]
+    o = np.zeros((1, 2, 512))
+    for r, h, d, v in g["o_nonzero"]:
+        o[r, h, d] = v
+    w_uv = np.zeros((2, 2, 512))
+    for h, j, d, v in g["w_uv_nonzero"]:
+        w_uv[h, j, d] = v
+    y, v = O.latent_up_projection(o, _bits(w_uv), _bits(g["w_o"]))
+    assert np.array_equal(v, np.array(g["expected_v"]))
+    assert np.array_equal(y, np.array(g["expected_y"]))
+
+
+def test_up_projection_brute_force_tiny():
+    """Pure-Python loops over (r, h, j, d) and (m, h, j)."""
+    rng = np.random.default_rng(41)
+    R, H, Dv, Dm = 2, 3, 4, 5
+    o = rng.standard_normal((R, H, 512))
+    w_uv = _bits(rng.standard_normal((H, Dv, 512)) / 8)
+    w_o = _bits(rng.standard_normal((Dm, H * Dv)) / 2)
+    y, v = O.latent_up_projection(o, w_uv, w_o)
+    W1, W2 = O.decode_bf16(w_uv), O.decode_bf16(w_o)
+    for r in range(R):
+        vv = [[sum(float(W1[h][j][d]) * float(o[r][h][d]) for d in range(512)) for j in range(Dv)] for h in range(H)]
+        for h in range(H):
+            for j in range(Dv):
+                assert abs(v[r, h, j] - vv[h][j]) <= 1e-12 * (1 + abs(vv[h][j]))
+        for m in range(Dm):
+            ym = sum(float(W2[m][h * Dv + j]) * vv[h][j] for h in range(H) for j in range(Dv))
+            assert abs(y[r, m] - ym) <= 1e-12 * (1 + abs(ym))
+
+
+def test_up_projection_identity_and_permutation():
+    """Identity weights return the latent output itself; permutation weights permute it (head
+    blocks of o_proj are contiguous and in head order)."""
+    rng = np.random.default_rng(42)
+    R, H = 3, 2
+    o = rng.standard_normal((R, H, 512))
+    eye = np.eye(512)
+    y, v = O.latent_up_projection(o, _bits(np.stack([eye] * H)), _bits(np.eye(H * 512)))
+    assert np.array_equal(y, o.reshape(R, H * 512)) and np.array_equal(v, o)
+    p0, p1 = rng.permutation(512), rng.permutation(512)
+    w_uv = np.stack([eye[p0], eye[p1]])                 # row j picks latent p_h[j]
+    pm = rng.permutation(H * 512)
+    y, v = O.latent_up_projection(o, _bits(w_uv), _bits(np.eye(H * 512)[pm]))
+    assert np.array_equal(v[:, 0], o[:, 0, p0]) and np.array_equal(v[:, 1], o[:, 1, p1])
+    assert np.array_equal(y, v.reshape(R, -1)[:, pm])
+
+
+def test_up_projection_after_attention_equals_attention_over_projected_values():
+    """Weight absorption: projecting the latent attention output afterwards equals attending over
+    each token's value reconstructed per head (W_UV c_t[:512]) and projecting those; the softmax
+    weights are recomputed here with scipy from the logits, independently of the oracle."""
+    from scipy.special import softmax
+    rng = np.random.default_rng(43)
+    cfg = dsa_inputs.scaled_config("c2", [300], seed=44, mla_heads=4, top_k=40)
+    inp = dsa_inputs.make_inputs(cfg, with_indexer=False)
+    slots = rng.choice(cfg.num_slots, (1, 1, 40), replace=False).astype(np.int32)
+    o, _ = O.sparse_mla(inp["q_mla"], "bf16", inp["kv_cache"], "bf16", None, slots, cfg.sm_scale)
+    Dv, Dm = 16, 24
+    w_uv = _bits(rng.standard_normal((4, Dv, 512)) / 16)
+    w_o = _bits(rng.standard_normal((Dm, 4 * Dv)) / 8)
+    y_abs, _ = O.latent_up_projection(o[0], w_uv, w_o)
+    q = O.decode_bf16(inp["q_mla"])[0, 0]                     # [H, 576]
+    c = O.decode_bf16(inp["kv_cache"])[slots[0, 0]]          # [40, 576]
+    W1, W2 = O.decode_bf16(w_uv), O.decode_bf16(w_o)
+    v = np.zeros((4, Dv))
+    for h in range(4):
+        p = softmax(cfg.sm_scale * (c @ q[h]))
+        vals = c[:, :512] @ W1[h].T                          # [40, Dv]: each token's value of head h
+        v[h] = p @ vals
+    y_direct = W2 @ v.reshape(-1)
+    assert np.allclose(y_abs[0], y_direct, rtol=1e-11, atol=1e-14)
+
+
+def test_up_projection_is_linear_in_o():
+    rng = np.random.default_rng(45)
+    w_uv = _bits(rng.standard_normal((2, 8, 512)) / 16)
+    w_o = _bits(rng.standard_normal((6, 16)))
+    o1, o2 = rng.standard_normal((2, 3, 2, 512))
+    y1, _ = O.latent_up_projection(o1, w_uv, w_o)
+    y2, _ = O.latent_up_projection(o2, w_uv, w_o)
+    y3, _ = O.latent_up_projection(2.5 * o1 - o2, w_uv, w_o)
+    assert np.allclose(y3, 2.5 * y1 - y2, rtol=1e-12, atol=1e-12)
+    assert not np.allclose(y1, 0)
+    yz, _ = O.latent_up_projection(np.zeros((1, 2, 512)), w_uv, w_o)
+    assert np.array_equal(yz, np.zeros((1, 6)))
