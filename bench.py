@@ -496,8 +496,34 @@ def measure(name, K, W, args, dev, evict, stages=True):
     app = dict(us=round(ms * 1e3, 3), bytes=rows * per_tok + B * 4, kernel="cache_append_kernel",
                timing="hip-graph of launches, replicas cycled")
     app["GBps"] = round(app["bytes"] / (app["us"] * 1e-6) / 1e9, 1)
-    res["outside_step"] = {"kv_cache_append": app}
+    res["outside_step"] = {"kv_cache_append": app, "latent_up_projection": measure_up_projection(rows, H, dev,
+                                                                                                 stream, evict, KS)}
     return res
+
+
+UP_V_DIM, UP_D_MODEL = 128, 6144   # value head width and model width of the projection's workload
+
+
+def measure_up_projection(rows, H, dev, stream, evict, KS):
+    """The projection after attention (per-head W_UV, then o_proj) of one step's attention
+    output: weight sets replicated past the Infinity Cache, a graph of KS launches cycling them."""
+    import torch
+    import dsa_inputs
+    import sparse_attention_10_amd as dsa
+    wbytes = (H * UP_V_DIM * 512 + UP_D_MODEL * H * UP_V_DIM) * 2
+    nrep = max(1, math.ceil(2 * MALL_BYTES / wbytes))
+    sets = [dsa_inputs.make_up_projection_weights_torch(H, UP_V_DIM, UP_D_MODEL, 71 + i, dev) for i in range(nrep)]
+    o = (torch.randn((rows, H, 512), device=dev) / 24).float()
+    y = torch.empty((rows, UP_D_MODEL), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(1, dsa.up_projection_workspace_bytes(rows, H, UP_V_DIM, UP_D_MODEL)), dtype=torch.uint8,
+                     device=dev)
+    ms = time_graph([(lambda j=j: dsa.dsa_latent_up_projection(o, sets[j % nrep][0], sets[j % nrep][1], y, ws,
+                                                              stream=stream)) for j in range(KS)], stream, evict) / KS
+    by = wbytes + rows * H * 512 * 4 + rows * UP_D_MODEL * 4
+    us = ms * 1e3
+    return dict(us=round(us, 3), bytes=by, GBps=round(by / (us * 1e-6) / 1e9, 1), rows=rows, v_dim=UP_V_DIM,
+                d_model=UP_D_MODEL, kernels=["up_v_kernel", "up_y_kernel", "up_reduce_kernel"],
+                timing="hip-graph of launches, weight sets cycled")
 
 
 def main():

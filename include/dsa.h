@@ -246,6 +246,29 @@ dsa_status_t dsa_kv_cache_append(const dsa_batch_t *batch,
                                  void *k_cache, dsa_dtype_t k_dtype, float *k_scale,
                                  void *stream);
 
+/*
+ * Latent up-projection after attention (Show HN page "Chay GLM 5.2 tren may tinh cham",
+ * main-features section, MLA weight absorption: the query absorbs kv_b and the context is
+ * projected after attention).  The attention output of dsa_sparse_mla_decode is still in the
+ * 512-wide latent space; per head it is projected by that head's value block of kv_b, then all
+ * heads by o_proj:
+ *   v[r,h,j] = sum_d w_uv[h,j,d] * attn_out[r,h,d]        (d < 512)
+ *   y[r,m]   = sum_{h,j} w_o[m, h*v_dim + j] * v[r,h,j]
+ *   attn_out  [rows, n_heads, 512] f32 (r = b*Q + i, as dsa_sparse_mla_decode writes it)
+ *   w_uv      [n_heads, v_dim, 512] bf16;  w_o [d_model, n_heads*v_dim] bf16
+ *   y         [rows, d_model] f32
+ * The f32 activations enter the bf16 matrix cores as two bf16 parts (hi + lo, 2^-18 relative),
+ * so y is an fp32-accurate product.  The workspace (dsa_latent_up_projection_workspace_size
+ * bytes, 256-byte aligned, no initial contents) holds v and, when the K dimension is split over
+ * workgroups, the partial sums, which are added in a fixed order (deterministic results).
+ * Supported: n_heads <= 128, v_dim a multiple of 32 (<= 1024), d_model a multiple of 16
+ * (<= 65536), rows <= 1000000.
+ */
+dsa_status_t dsa_latent_up_projection(int32_t rows, int32_t n_heads, int32_t v_dim, int32_t d_model,
+                                      const float *attn_out, const void *w_uv, const void *w_o, float *y,
+                                      void *workspace, size_t workspace_bytes, void *stream);
+size_t dsa_latent_up_projection_workspace_size(int32_t rows, int32_t n_heads, int32_t v_dim, int32_t d_model);
+
 const char *dsa_status_string(dsa_status_t status);
 const char *dsa_last_error(void);   /* thread-local detail for the last non-OK status */
 int32_t dsa_abi_version(void);

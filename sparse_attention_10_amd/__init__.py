@@ -26,6 +26,7 @@ EXPORTS = ("dsa_indexer_scores", "dsa_topk", "dsa_topk_workspace_size", "dsa_pag
            "dsa_sparse_mla_decode", "dsa_sparse_mla_workspace_size", "dsa_sparse_mla_default_split",
            "dsa_mla_combine", "dsa_decode_step", "dsa_decode_step_workspace_size", "dsa_kv_cache_append",
            "dsa_decode_step_noalloc", "dsa_decode_step_noalloc_max_bytes",
+           "dsa_latent_up_projection", "dsa_latent_up_projection_workspace_size",
            "dsa_status_string", "dsa_last_error", "dsa_abi_version")
 
 
@@ -80,6 +81,8 @@ def lib() -> ctypes.CDLL:
             "dsa_decode_step": (e, [ctypes.POINTER(DsaDecodeStepArgs), vp, sz, vp]),
             "dsa_decode_step_workspace_size": (sz, [ctypes.POINTER(DsaDecodeStepArgs)]),
             "dsa_decode_step_noalloc": (e, [ctypes.POINTER(DsaDecodeStepArgs), vp]),
+            "dsa_latent_up_projection": (e, [i32, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]),
+            "dsa_latent_up_projection_workspace_size": (sz, [i32, i32, i32, i32]),
             "dsa_decode_step_noalloc_max_bytes": (sz, []),
             "dsa_kv_cache_append": (e, [bp, vp, e, vp, e, vp, vp, e, i32, vp, e, vp, vp]),
             "dsa_status_string": (ctypes.c_char_p, [e]),
@@ -242,6 +245,24 @@ def dsa_decode_step_noalloc(args: DsaDecodeStepArgs, stream=None):
 
 def decode_step_noalloc_max_bytes() -> int:
     return lib().dsa_decode_step_noalloc_max_bytes()
+
+
+def up_projection_workspace_bytes(rows: int, n_heads: int, v_dim: int, d_model: int) -> int:
+    return lib().dsa_latent_up_projection_workspace_size(rows, n_heads, v_dim, d_model)
+
+
+def dsa_latent_up_projection(attn_out: torch.Tensor, w_uv: torch.Tensor, w_o: torch.Tensor, y: torch.Tensor,
+                             workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """attn_out [..., H, 512] f32 (rows flattened), w_uv [H, Dv, 512] bf16, w_o [Dm, H*Dv] bf16
+    -> y [rows, Dm] f32 (see dsa.h)."""
+    H, Dv, Dm = w_uv.shape[0], w_uv.shape[1], w_o.shape[0]
+    rows = attn_out.numel() // (H * 512)
+    need = up_projection_workspace_bytes(rows, H, Dv, Dm)
+    if workspace is None:
+        workspace = torch.empty(max(1, need), dtype=torch.uint8, device=attn_out.device)
+    _check(lib().dsa_latent_up_projection(rows, H, Dv, Dm, _ptr(attn_out), _ptr(w_uv), _ptr(w_o), _ptr(y),
+                                          _ptr(workspace), workspace.numel(), _stream(stream)))
+    return y
 
 
 def dsa_kv_cache_append(batch: DsaBatch, kv_new: Optional[torch.Tensor], kv_cache: Optional[torch.Tensor],

@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdsa.so")
-SOURCES = ["api.hip", "indexer.hip", "topk.hip", "mla.hip", "cache.hip"]
+SOURCES = ["api.hip", "indexer.hip", "topk.hip", "mla.hip", "cache.hip", "up_proj.hip"]
 ARCH = "gfx950"
 
 

@@ -488,6 +488,63 @@ dsa_status_t dsa_decode_step_noalloc(const dsa_decode_step_args_t* a, void* stre
   return launch_step(a, w, ptr, kScratchBytes, (hipStream_t)stream);
 }
 
+namespace {
+
+struct UpWs {
+  size_t v_bytes, part_bytes, total;
+  int32_t ksplit;
+};
+
+UpWs up_ws(int32_t R, int32_t H, int32_t Dv, int32_t Dm) {
+  UpWs w{};
+  w.ksplit = up_proj_ksplit(R, Dm, H * Dv);
+  w.v_bytes = align_up((size_t)R * H * Dv * sizeof(float), 256);
+  w.part_bytes = w.ksplit > 1 ? align_up((size_t)w.ksplit * R * Dm * sizeof(float), 256) : 0;
+  w.total = w.v_bytes + w.part_bytes;
+  return w;
+}
+
+}  // namespace
+
+size_t dsa_latent_up_projection_workspace_size(int32_t rows, int32_t n_heads, int32_t v_dim, int32_t d_model) {
+  if (rows < 1 || n_heads < 1 || v_dim < 1 || d_model < 1) return 0;
+  return up_ws(rows, n_heads, v_dim, d_model).total;
+}
+
+dsa_status_t dsa_latent_up_projection(int32_t rows, int32_t n_heads, int32_t v_dim, int32_t d_model,
+                                      const float* attn_out, const void* w_uv, const void* w_o, float* y,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  DSA_REQUIRE(rows >= 1 && n_heads >= 1 && v_dim >= 1 && d_model >= 1,
+              "up_projection: rows, n_heads, v_dim and d_model must be >= 1");
+  DSA_REQUIRE(attn_out && w_uv && w_o && y, "up_projection: attn_out, w_uv, w_o and y must be non-NULL");
+  DSA_SUPPORT(n_heads <= 128 && v_dim % 32 == 0 && v_dim <= 1024 && d_model % 16 == 0 && d_model <= 65536 &&
+                  rows <= 1000000,
+              "up_projection: n_heads=%d v_dim=%d d_model=%d rows=%d outside the supported set (n_heads <= 128, "
+              "v_dim a multiple of 32 up to 1024, d_model a multiple of 16 up to 65536, rows <= 1000000)",
+              n_heads, v_dim, d_model, rows);
+  DSA_REQUIRE(aligned(attn_out, 16) && aligned(w_uv, 16) && aligned(w_o, 16) && aligned(y, 4),
+              "up_projection: attn_out, w_uv and w_o must be 16-byte aligned, y 4-byte aligned");
+  const UpWs w = up_ws(rows, n_heads, v_dim, d_model);
+  if (workspace_bytes < w.total || workspace == nullptr)
+    return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "up_projection: workspace needs %zu bytes (got %zu)", w.total,
+                workspace_bytes);
+  DSA_REQUIRE(aligned(workspace, 256), "up_projection: workspace must be 256-byte aligned");
+  DSA_TRY(check_device());
+  UpProjParams p{};
+  p.o = attn_out;
+  p.w_uv = w_uv;
+  p.w_o = w_o;
+  p.v = (float*)workspace;
+  p.part = w.ksplit > 1 ? (float*)((uint8_t*)workspace + w.v_bytes) : nullptr;
+  p.y = y;
+  p.R = rows;
+  p.H = n_heads;
+  p.Dv = v_dim;
+  p.Dm = d_model;
+  p.ksplit = w.ksplit;
+  return launched(launch_up_proj(p, (hipStream_t)stream), "up-projection");
+}
+
 dsa_status_t dsa_kv_cache_append(const dsa_batch_t* b, const void* kv_new, dsa_dtype_t kv_new_dtype, void* kv_cache,
                                  dsa_dtype_t kv_dtype, float* kv_scale, const void* k_new, dsa_dtype_t k_new_dtype,
                                  int32_t head_dim, void* k_cache, dsa_dtype_t k_dtype, float* k_scale,

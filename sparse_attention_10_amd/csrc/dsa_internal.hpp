@@ -204,6 +204,19 @@ struct AppendParams {
   int32_t kv_src_dtype, kv_dst_dtype, k_src_dtype, k_dst_dtype;
 };
 
+// Latent up-projection after attention: o [R, H, 512] f32 -> v [R, H, Dv] f32 (workspace) ->
+// y [R, Dm] f32, with K = H * Dv split into ksplit chunks whose partial sums (part, [ksplit, R,
+// Dm], workspace) are added in order when ksplit > 1.
+struct UpProjParams {
+  const float* o;
+  const void* w_uv;   // [H, Dv, 512] bf16
+  const void* w_o;    // [Dm, H*Dv] bf16
+  float* v;
+  float* part;
+  float* y;
+  int32_t R, H, Dv, Dm, ksplit, k_chunk;
+};
+
 // launchers (return hipGetLastError() of the launch)
 hipError_t launch_indexer(const IndexerParams& p, dsa_dtype_t q_dtype, dsa_dtype_t k_dtype,
                           hipStream_t s);
@@ -219,5 +232,7 @@ hipError_t launch_mla(const MlaParams& p, dsa_dtype_t q_dtype, dsa_dtype_t kv_dt
 hipError_t launch_combine(const CombineParams& p, hipStream_t s);
 int mla_default_split(int rows, int H, int k, dsa_dtype_t kv_dtype);
 hipError_t launch_cache_append(const AppendParams& p, hipStream_t s);
+int up_proj_ksplit(int R, int Dm, int K);
+hipError_t launch_up_proj(const UpProjParams& p, hipStream_t s);
 
 }  // namespace dsa

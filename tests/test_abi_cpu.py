@@ -201,3 +201,24 @@ def test_noalloc_step_rejects_oversized_steps_before_the_device(L):
     assert L.dsa_decode_step_noalloc(ctypes.byref(a), None) == dsa.DSA_ERR_WORKSPACE_TOO_SMALL
     assert b"scratch" in L.dsa_last_error()
     assert L.dsa_decode_step_noalloc(None, None) == dsa.DSA_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("R,H,Dv,Dm,ptrs,ws,status", [
+    (0, 64, 128, 256, True, 1 << 30, 1),
+    (4, 64, 100, 256, True, 1 << 30, 2),       # value dim not a multiple of 32
+    (4, 64, 128, 250, True, 1 << 30, 2),       # model width not a multiple of 16
+    (4, 200, 128, 256, True, 1 << 30, 2),
+    (4, 64, 128, 256, False, 1 << 30, 1),      # NULL arrays
+    (4, 64, 128, 256, True, 16, 3),            # workspace too small
+])
+def test_up_projection_rejects(L, R, H, Dv, Dm, ptrs, ws, status):
+    p = FAKE if ptrs else None
+    assert L.dsa_latent_up_projection(R, H, Dv, Dm, p, p, p, p, FAKE, ws, None) == status
+    assert len(L.dsa_last_error()) > 0
+
+
+def test_up_projection_workspace_size(L):
+    # v [R, H, Dv] f32, plus K-split partials [ksplit, R, Dm] f32 when the rows leave the GPU idle
+    assert L.dsa_latent_up_projection_workspace_size(128, 64, 128, 6144) >= 128 * 64 * 128 * 4
+    assert L.dsa_latent_up_projection_workspace_size(1, 64, 128, 6144) > 64 * 128 * 4
+    assert L.dsa_latent_up_projection_workspace_size(0, 64, 128, 6144) == 0
