@@ -44,6 +44,7 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 MALL_BYTES = 256 << 20
 FLUSH_BYTES = 1 << 30
+MODEL_LAYERS = 78        # main layers of the model whose per-token forward the graph replays
 
 WORKLOAD_NAMES = {"c1": "tiny fp32 decode, 4K ctx", "c2": "single-stream decode layer, 32K ctx",
                   "c2_128k": "single-stream decode layer, 128K ctx",
@@ -75,7 +76,96 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 10 plain 1 GiB device copies (reference for the FETCH_SIZE / WRITE_SIZE counters)")
     ap.add_argument("--cpu-one-core-child", action="store_true", help=argparse.SUPPRESS)
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="print a markdown table of the kernel statistics of a rocprofv3 --kernel-trace --stats run")
+    ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="print the per-launch HBM traffic JSON of rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs of a "
+                         "workload and of --copy-calibration")
+    ap.add_argument("--summarize-mfma", metavar="DIR",
+                    help="print the per-kernel matrix-core use of a rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES "
+                         "GRBM_GUI_ACTIVE SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F8 run")
     return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------------------------
+# rocprofv3 output summaries (CSV written by --output-format csv)
+
+def _csv_rows(d, suffix):
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True)):
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    if not rows:
+        raise SystemExit(f"no *{suffix} under {d}")
+    return rows
+
+
+def _short(name):
+    for pre in ("void ", "dsa::(anonymous namespace)::"):
+        name = name.replace(pre, "")
+    return name.split("(")[0].strip()
+
+
+def summarize_trace(d):
+    rows = _csv_rows(d, "kernel_stats.csv")
+    print("| kernel | calls | avg µs | min µs | max µs |\n|---|---|---|---|---|")
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        print(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+              f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+
+
+def _per_dispatch(d, counter):
+    """{kernel: mean over its dispatches of the counter summed over the dispatch's rows}"""
+    import collections
+    per = collections.defaultdict(float)
+    names = {}
+    for r in _csv_rows(d, "counter_collection.csv"):
+        if r["Counter_Name"] != counter:
+            continue
+        key = int(r["Dispatch_Id"])
+        per[key] += float(r["Counter_Value"])
+        names[key] = _short(r["Kernel_Name"])
+    by = collections.defaultdict(list)
+    for key, v in per.items():
+        by[names[key]].append(v)
+    return {k: sum(v) / len(v) for k, v in by.items()}
+
+
+def summarize_counters(fetch_d, write_d, cfetch_d, cwrite_d):
+    copy_kib = (1 << 30) / 1024
+    fc = _per_dispatch(cfetch_d, "FETCH_SIZE")
+    wc = _per_dispatch(cwrite_d, "WRITE_SIZE")
+    ff = copy_kib / max(v for k, v in fc.items() if "opy" in k or "elementwise" in k or "Copy" in k)
+    wf = copy_kib / max(v for k, v in wc.items() if "opy" in k or "elementwise" in k or "Copy" in k)
+    f = _per_dispatch(fetch_d, "FETCH_SIZE")
+    w = _per_dispatch(write_d, "WRITE_SIZE")
+    out = {"kernel_source_hash": kernel_hash(),
+           "calibration": {"fetch_factor": round(ff, 4), "write_factor": round(wf, 4),
+                           "copy": "1 GiB device copy via bench.py --copy-calibration"},
+           "kernels": {}}
+    for k in sorted(set(f) | set(w)):
+        if k.startswith("__amd") or k.startswith("at::"):   # the harness's own copies and fills
+            continue
+        fk, wk = f.get(k, 0.0), w.get(k, 0.0)
+        out["kernels"][k] = dict(fetch_kib=round(fk, 1), write_kib=round(wk, 1),
+                                 bytes_per_launch=int(round((fk * ff + wk * wf) * 1024)))
+    print(json.dumps(out, indent=1))
+
+
+def summarize_mfma(d):
+    busy = _per_dispatch(d, "SQ_VALU_MFMA_BUSY_CYCLES")
+    gui = _per_dispatch(d, "GRBM_GUI_ACTIVE")
+    bf16 = _per_dispatch(d, "SQ_INSTS_VALU_MFMA_MOPS_BF16")
+    f8 = _per_dispatch(d, "SQ_INSTS_VALU_MFMA_MOPS_F8")
+    xcds, simds = 8, 1024      # GRBM_GUI_ACTIVE is summed over the 8 XCDs; 256 CUs x 4 SIMDs
+    print("| kernel | MFMA busy / (active cycles x SIMDs) | bf16 MFMA flops | fp8 MFMA flops |\n|---|---|---|---|")
+    for k in sorted(busy, key=lambda k: -busy[k]):
+        if busy[k] <= 0:
+            continue
+        util = busy[k] / (gui[k] / xcds * simds) if gui.get(k) else float("nan")
+        print(f"| `{k}` | {100 * util:.1f}% | {bf16.get(k, 0) * 512:.3e} | {f8.get(k, 0) * 512:.3e} |")
 
 
 # ---------------------------------------------------------------------------------------------
@@ -298,7 +388,7 @@ def kernel_names(cfg, ns):
     return dict(indexer=idx, mla=mla, topk="topk_kernel", combine=comb)
 
 
-def measure(name, K, W, args, dev, evict, stages=True):
+def measure(name, K, W, args, dev, evict, stages=True, multi_layer=False):
     """Time K decode steps of workload `name` (graph replay unless --eager) and, optionally, each
     stage alone.  Returns the result dict of that workload."""
     import torch
@@ -381,6 +471,27 @@ def measure(name, K, W, args, dev, evict, stages=True):
         eager_ms = f0.elapsed_time(f1) / ke
 
     gbs = by["total"] / (ms_step * 1e-3) / 1e9
+    multi = None
+    if multi_layer and not args.eager:
+        # one token through a 78-layer stack: 78 consecutive steps, each over its own layer's
+        # caches (replica j mod R), as one graph and as eager launches
+        nl = MODEL_LAYERS
+        g_ms = time_graph([(lambda j=j: step(j)) for j in range(nl)], stream, evict)
+        evict(stream)
+        torch.cuda.synchronize()
+        f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            f0.record(stream)
+            for j in range(nl):
+                step(j)
+            f1.record(stream)
+        torch.cuda.synchronize()
+        e_ms = f0.elapsed_time(f1)
+        multi = dict(layers=nl, graph_us_per_token=round(g_ms * 1e3, 1), eager_us_per_token=round(e_ms * 1e3, 1),
+                     graph_speedup=round(e_ms / g_ms, 3),
+                     attention_tokens_per_s=round(1e3 / g_ms, 1),
+                     note="attention stage of every layer only (indexer, top-k, sparse MLA, merge); "
+                          "layer caches cycle over %d replicas" % R)
     kvd = dsa.dtype_code(reps[0]["kv_cache"])
     ns = args.n_split or dsa.lib().dsa_sparse_mla_default_split(B, Q, H, k, kvd)
     ns = min(ns, (k + 31) // 32)
@@ -396,6 +507,8 @@ def measure(name, K, W, args, dev, evict, stages=True):
     }
     if union is not None:
         res["union_rows"] = union
+    if multi is not None:
+        res["multi_layer"] = multi
     if not stages:
         return res
 
@@ -528,6 +641,15 @@ def measure_up_projection(rows, H, dev, stream, evict, KS):
 
 def main():
     args = parse()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
+        return
+    if args.summarize_mfma:
+        summarize_mfma(args.summarize_mfma)
+        return
     if args.cpu_one_core_child:
         print(json.dumps(cpu_sample(args.config, args.cpu_seconds)))
         return
@@ -550,7 +672,8 @@ def main():
     torch.cuda.set_device(0)
     dsa.lib()
     evict = Evictor(dev)
-    head = measure(args.config, args.steps, args.warmup, args, dev, evict, stages=not args.no_stages)
+    head = measure(args.config, args.steps, args.warmup, args, dev, evict, stages=not args.no_stages,
+                   multi_layer=True)
     workloads = {}
     for n in extras:
         torch.cuda.empty_cache()
@@ -574,7 +697,7 @@ def main():
         "algorithmic_bytes_per_step": head["algorithmic_bytes_per_step"],
         "timing": head["timing"],
     }
-    for key in ("stages", "rooflines", "roofline", "outside_step"):
+    for key in ("stages", "rooflines", "roofline", "outside_step", "multi_layer"):
         if key in head:
             res[key] = head[key]
     if workloads:

@@ -444,6 +444,64 @@ def test_decode_step_hip_graph_replay():
         assert torch.equal(lse, eager_l), f"replay {rep}"
 
 
+def test_multi_layer_graph_replay_matches_oracle():
+    """Several layers' decode steps (each with its own caches, one shared workspace) captured in
+    one HIP graph, the way a model's per-token forward replays them.  The first replay is checked
+    layer by layer against the oracle with the staged protocol; every later replay, with eager
+    work between replays, must reproduce it bit for bit."""
+    layers = [("c2", [3000], dict()), ("c5", [2500, 1800], dict()), ("c2", [900], dict(q_per_seq=3)),
+              ("c5", [4100], dict())]
+    cases, args, bufs = [], [], []
+    for n, (name, lens, kw) in enumerate(layers):
+        cfg, inp, t = _case(name, lens, seed=120 + n, **kw)
+        B, Q, H, k = cfg.batch, cfg.q_per_seq, cfg.mla_heads, cfg.top_k
+        b = dict(out=torch.zeros((B, Q, H, 512), device=DEV), lse=torch.zeros((B, Q, H), device=DEV),
+                 scores=torch.zeros((B, Q, cfg.max_seq_len), device=DEV),
+                 idx=torch.zeros((B, Q, k), dtype=torch.int32, device=DEV),
+                 slots=torch.zeros((B, Q, k), dtype=torch.int32, device=DEV))
+        args.append(dsa.decode_step_args(batch_of(cfg, t), t["q_idx"], t["w"], t["k_cache"], t["k_scale"], k,
+                                         t["q_mla"], t["kv_cache"], t["kv_scale"], cfg.sm_scale, b["out"],
+                                         b["lse"], 0, b["scores"], b["idx"], b["slots"]))
+        cases.append((cfg, inp, t))
+        bufs.append(b)
+    ws = torch.zeros(max(dsa.decode_step_workspace_bytes(a) for a in args), dtype=torch.uint8, device=DEV)
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for a in args:
+            dsa.dsa_decode_step(a, ws, stream=s)
+    first = None
+    for rep in range(3):
+        for b in bufs:                      # eager work between replays
+            for v in b.values():
+                v.fill_(-3)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s):
+            g.replay()
+        torch.cuda.synchronize()
+        got = [{k: v.cpu() for k, v in b.items()} for b in bufs]
+        if first is None:
+            first = got
+            for (cfg, inp, _), r in zip(cases, got):
+                s_g = r["scores"].numpy()
+                s_ref = O.indexer_scores(inp["q_idx"], cfg.q_idx_dtype, inp["w"], inp["k_cache"], cfg.key_dtype,
+                                         inp["k_scale"], inp["seq_lens"], inp["page_table"], cfg.q_per_seq,
+                                         cfg.page_size)
+                check_indexer(cfg, s_g, s_ref, inp["seq_lens"])
+                idx_g, slots_g = r["idx"].numpy(), r["slots"].numpy()
+                assert np.array_equal(idx_g, O.topk(np.where(np.isnan(s_g), -np.inf, s_g).astype(np.float64),
+                                                    inp["seq_lens"], cfg.q_per_seq, cfg.top_k))
+                assert np.array_equal(slots_g, O.page_map(idx_g, inp["page_table"], cfg.page_size))
+                ro, rl = oracle_mla(cfg, inp, slots_g)
+                check_attention(r["out"].numpy(), ro, r["lse"].numpy(), rl)
+        else:
+            for n, (r0, r) in enumerate(zip(first, got)):
+                for key in r:
+                    assert torch.equal(r0[key].view(torch.int32) if r0[key].dtype == torch.float32 else r0[key],
+                                       r[key].view(torch.int32) if r[key].dtype == torch.float32 else r[key]), \
+                        f"replay {rep}, layer {n}, {key}"
+
+
 def test_abi_errors_leave_outputs_untouched():
     cfg, inp, t = _case("c2", [600], seed=110)
     out = torch.full((1, 1, 64, 512), 3.0, device=DEV)
