@@ -379,7 +379,7 @@ def kernel_names(cfg, ns):
     k = cfg.top_k
     chunk = -(-(-(-k // ns)) // 32) * 32
     if cfg.kv_dtype == "fp8":
-        mla = "mla_fp8x_kernel" if chunk <= 1024 else "mla_fp8_kernel"
+        mla = "mla_fp8d_kernel" if chunk <= 2048 else "mla_fp8_kernel"
     else:
         mla = "mla_bf16d_kernel" if chunk <= 2048 else "mla_mfma_kernel"
     idx = ("indexer_prefill_kernel" if cfg.q_per_seq >= 16 and cfg.key_dtype == "bf16" and cfg.page_size % 32 == 0

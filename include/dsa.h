@@ -145,7 +145,7 @@ dsa_status_t dsa_sparse_mla_decode(int32_t batch, int32_t q_per_seq,
                                    void *workspace, size_t workspace_bytes, void *stream);
 size_t dsa_sparse_mla_workspace_size(int32_t batch, int32_t q_per_seq, int32_t n_heads, int32_t k,
                                      int32_t n_split, dsa_dtype_t q_dtype, dsa_dtype_t kv_dtype);
-/* The n_split that dsa_sparse_mla_decode uses when passed 0 (fp8 rows: at most 1024 selected
+/* The n_split that dsa_sparse_mla_decode uses when passed 0 (fp8 rows: at most 2048 selected
  * rows per chunk). */
 int32_t dsa_sparse_mla_default_split(int32_t batch, int32_t q_per_seq, int32_t n_heads, int32_t k,
                                      dsa_dtype_t kv_dtype);

@@ -7,8 +7,9 @@
 //   mla_bf16d_kernel  bf16 rows, chunks <= 2048: 8 waves, 32-token tiles copied HBM -> LDS into
 //                     a 4-deep ring, S^T per (head group, 16-token block), P.V per 64 output
 //                     values over all heads, softmax against a fixed per-head reference.
-//   mla_fp8x_kernel   fp8 rows, chunks <= 1024: 4 waves, 64-token tiles, S^T on the e4m3 matrix
-//                     core with q split into two e4m3 parts, the same fixed-reference softmax.
+//   mla_fp8d_kernel   fp8 rows, chunks <= 2048: 8 waves, 32-token e4m3 tiles staged HBM ->
+//                     registers -> LDS with coalesced loads, rows widened exactly to bf16 at
+//                     each operand read, the same fixed-reference softmax.
 //   mla_fp8_kernel    fp8 rows, longer chunks: 8 waves, online softmax with lazy rescaling.
 //   mla_mfma_kernel   bf16 rows, longer chunks: 8 waves, rows staged through registers.
 // Common to all: S^T = rows . q^T and O^T += V^T . P^T on the bf16 (or e4m3) MFMAs in fp32,
@@ -38,16 +39,6 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRefMargin = 64.f;   // log2 of the largest P relative to the softmax reference R
 
-// Four f32 values as e4m3 pairs (round to nearest even): hw = e4m3(f), lw = e4m3(f - hw), byte
-// j of each word for value j.
-__device__ __forceinline__ void split_e4m3_x4(float f0, float f1, float f2, float f3, int& hw, int& lw) {
-  hw = __builtin_amdgcn_cvt_pk_fp8_f32(f0, f1, 0, false);
-  hw = __builtin_amdgcn_cvt_pk_fp8_f32(f2, f3, hw, true);
-  const float h0 = __builtin_amdgcn_cvt_f32_fp8(hw, 0), h1 = __builtin_amdgcn_cvt_f32_fp8(hw, 1);
-  const float h2 = __builtin_amdgcn_cvt_f32_fp8(hw, 2), h3 = __builtin_amdgcn_cvt_f32_fp8(hw, 3);
-  lw = __builtin_amdgcn_cvt_pk_fp8_f32(f0 - h0, f1 - h1, 0, false);
-  lw = __builtin_amdgcn_cvt_pk_fp8_f32(f2 - h2, f3 - h3, lw, true);
-}
 constexpr float kLn2 = 0.6931471805599453f;
 
 // ---------------------------------------------------------------------------------------------
@@ -657,355 +648,336 @@ __global__ __launch_bounds__(kNT) void mla_fp8_kernel(MlaParams p) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// fp8 rows, wide-tile variant (chunks of at most kChunkX selected rows): 4 waves, one per SIMD,
-// each with up to 512 registers, 64-token tiles.
-//   * Tiles are copied HBM -> LDS directly (36 copies of 1 KiB per tile, 9 per wave, whole rows
-//     per copy, through a buffer resource) into a ring of kRingX slots, kRingX-1 tiles in flight;
-//     layout as in mla_fp8_kernel (row t at t*576, piece p in slot p ^ fp8_swz(t)).
-//   * S^T and the softmax: wave w owns the 16 heads 16w .. 16w+15 over all 64 tokens and the
-//     full K (q in registers); it publishes P (bf16, in the P.V operand layout) through LDS.
-//     P = exp2(z - R) with a fixed reference per head, the largest logit of the head's first
-//     tile with a live token, so that the accumulators are only ever touched by the matrix core
-//     (no rescaling, no copies out of the accumulator registers).  P and the sums stay finite
-//     while every logit is below R + 64 (log2 units); if some head's logit exceeds that, the
-//     chunk is computed again with R = that head's largest logit over the chunk.
-//   * P.V: wave w owns the output values 128w .. 128w+127 for all 64 heads, so each V^T operand
-//     is read from LDS and widened once and feeds the four head groups' MFMAs.
-//   * Two barriers per tile (tile landed; P published).  Loop-body LDS accesses go through
-//     restrict pointers (see the loop), copies through a buffer resource, so the compiler's
-//     waits for LDS reads stay partial and never cover the copies in flight.
+// fp8 rows, chunks of at most kChunkF selected rows: 8 waves (two per SIMD, at most 256
+// registers each), 32-token tiles kept as e4m3 in LDS.
+//   * Tiles are loaded HBM -> registers (per wave two loads of 1 KiB of whole rows, one of 256
+//     bytes and the scales) three steps ahead and stored into one of three LDS slots: while tile
+//     v is computed, the loads of tiles v+1 .. v+3 are in flight, and the compiler's wait before
+//     each store counts only the later tiles' loads.  A skipped token
+//     (slot -1) reads row 0 and is zeroed on the way into LDS.  Layout: row t at t*576, 16-byte
+//     piece p in slot p ^ fp8_swz(t) (conflict-free for both operand reads below).
+//   * S^T: wave w owns head group hg = w % 4 (heads 16hg .. 16hg+15, q in registers as bf16)
+//     and token block tb = w / 4 (tokens 16tb .. 16tb+15) over the full K.  Each 16-byte LDS
+//     read gives a lane 16 e4m3 values of its token, widened exactly to bf16 for two K steps of
+//     v_mfma_f32_16x16x32_bf16, so every product is exact in the fp32 accumulator.  Lane group
+//     g of the result holds tokens 16tb + 4g .. +3 of its head: the half of the P^T operand that
+//     the token ordering tau below assigns to it, written to LDS for the other waves.
+//   * P.V: wave w owns the output values 64w .. 64w+63 for all 64 heads; the V^T operand
+//     (ds_read_b64_tr_b8, tokens in the order tau(g, e) = 4g + e for e < 4, 16 + 4g + e - 4
+//     otherwise, then widened) is read once and feeds the four head groups' MFMAs.
+//   * Softmax against a fixed per-head reference R (the largest logit of the chunk's first
+//     tile over both token blocks, 0 if it has no live token); P = exp2(z - R) stays finite and
+//     accurate while the head's logits lie within R +- 64 (log2 units), otherwise the chunk is
+//     computed again with R = the head's largest logit.  The accumulators are only touched by
+//     the matrix core.
+//   * Two barriers per tile (next tile stored; P published).
+constexpr int kTF = 32;                                   // tokens per tile
+constexpr int kTFBytes = kTF * kRowDim;                   // 18432
+constexpr int kNTF = 512;                                 // 8 waves
+constexpr int kChunkF = 2048;                             // selected rows staged per workgroup
+constexpr int kStepsF = kRowDim / 32;                     // 18 K steps of 32
+constexpr int kDBlocksF = kVDim / 16 / 8;                 // 4 output blocks of 16 per wave
 
-constexpr int kTX = 64;                                  // tokens per tile
-constexpr int kTXBytes = kTX * kRowDim;                  // 36864
-constexpr int kTXCopies = kTXBytes / 1024;               // 36
-constexpr int kRingX = 4;
-constexpr int kNTX = 256;                                // 4 waves
-constexpr int kChunkX = 1024;                            // selected rows staged per workgroup
-constexpr int kStepsX = kRowDim / 32;                    // 18 K steps of 32 (bf16 q loads)
-constexpr int kKBlocksX = (kRowDim + 127) / 128;         // 5 e4m3 K blocks of 128 (the last half empty)
-constexpr int kDBlocksW = kVDim / 16 / 4;                // 8 output blocks of 16 per wave
-
-// Shared memory of mla_fp8x_kernel.
-struct FXSmem {
-  uint8_t ring[kRingX][kTXBytes + kTX * 4];   // tile, then its 64 per-token scales
-  int32_t sl[kChunkX + kTX];                  // the chunk's slots, -1 padded
-  bf16x8 pex[4][2][64];                       // P^T operands: head group, K half, lane
-  float fin_m[64], fin_l[64];                 // per-head reference and sum, after the last tile
-  int32_t redo;                               // some head exceeded its reference by the margin
+struct FDSmem {
+  uint8_t ring[3][kTFBytes + kTF * 4];        // tile, then its 32 per-token scales
+  int32_t sl[kChunkF + kTF];                  // the chunk's slots, -1 padded
+  bf16x8 pex[4][64];                          // P^T operands: head group, lane
+  float m0[2][64];                            // largest logit of the first tile, by token block
+  float fin_m[2][64], fin_l[2][64];           // per head and token block, after the last tile
+  int32_t redo;
 };
 
-__global__ __launch_bounds__(kNTX) void mla_fp8x_kernel(MlaParams p) {
-  __shared__ __attribute__((aligned(16))) FXSmem sm;
+__global__ __launch_bounds__(kNTF) void mla_fp8d_kernel(MlaParams p) {
+  __shared__ __attribute__((aligned(16))) FDSmem sm;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int r = blockIdx.y, split = blockIdx.x;
+  const int hg = wave & 3, tb = wave >> 2;
+  // Blocks go to the 8 XCDs round-robin.  With 8 rows or more the chunks of row r run on XCD
+  // r % 8, so the row's q is read from HBM into one L2; with fewer rows they spread.
+  int r, split;
+  if (p.rows >= 8) {
+    const int xcd = blockIdx.x & 7, jx = blockIdx.x >> 3;
+    r = 8 * (jx / p.n_split) + xcd;
+    split = jx - (jx / p.n_split) * p.n_split;
+    if (r >= p.rows) return;
+  } else {
+    r = blockIdx.x / p.n_split;
+    split = blockIdx.x - r * p.n_split;
+  }
   const int j0 = split * p.chunk;
   const int j1 = min(p.k, j0 + p.chunk);
-  const int ntiles = j1 > j0 ? (j1 - j0 + kTX - 1) / kTX : 0;
+  const int ntiles = j1 > j0 ? (j1 - j0 + kTF - 1) / kTF : 0;
   const int32_t* sl = p.slots + (int64_t)r * p.k;
   const int ngroups = min(4, p.H / 16);           // live head groups (H is a multiple of 16)
-  const bool s_active = wave < ngroups;           // this wave's S^T head group exists
+  const bool s_active = hg < ngroups;             // this wave's S^T head group exists
   const int m16 = lane & 15, grp = lane >> 4;
 
   {
-    const int span = ntiles * kTX;
-    for (int e0 = 0; e0 < span; e0 += 4 * kNTX) {
+    const int span = ntiles * kTF;
+    for (int e0 = 0; e0 < span; e0 += 4 * kNTF) {
       int32_t v[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = sl[min(j0 + e0 + u * kNTX + (int)threadIdx.x, p.k - 1)];
+      for (int u = 0; u < 4; ++u) v[u] = sl[min(j0 + e0 + u * kNTF + (int)threadIdx.x, p.k - 1)];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int e = e0 + u * kNTX + threadIdx.x;
+        const int e = e0 + u * kNTF + threadIdx.x;
         if (e < span) sm.sl[e] = j0 + e < j1 ? v[u] : -1;
       }
     }
   }
+  if (threadIdx.x == 0) sm.redo = 0;
+  if (!s_active && tb == 0) sm.pex[hg][lane] = bf16x8{};   // head groups past the head count: P = 0
   __syncthreads();
 
-  // Copies of tile v into ring slot `dst`: lane i of copy cc fills tile slot q = 64cc + i (token
-  // q/36, slot q%36); wave 0 also copies the 64 scales behind the tile.
-  const __amdgpu_buffer_rsrc_t kv_rs = rows_rsrc(p.kv, kRowDim, p.num_slots);
-  const __amdgpu_buffer_rsrc_t sc_rs = rows_rsrc(p.kv_scale, 4, p.num_slots);
-  auto issue = [&](const FXSmem* __restrict__ rd, uint8_t* __restrict__ dst, int v) {
+  // q of this wave's head group (B operand of S^T): head 16hg + m16 (a group past the head count
+  // loads the last head and never uses it); K step 2u + h holds dims 64u + 16grp + 8h .. +8,
+  // the order in which a lane's 16-byte row piece 4u + grp is widened
+  bf16x8 qf[kStepsF];
+  {
+    const int qhead = min(hg * 16 + m16, p.H - 1);
+    const bf16x8* qrow = (const bf16x8*)((const __bf16*)p.q + ((int64_t)r * p.H + qhead) * kRowDim);
 #pragma unroll
-    for (int c = 0; c < kTXCopies / 4; ++c) {
-      const int cc = wave * (kTXCopies / 4) + c;
-      const int q = cc * 64 + lane;
-      const int t = q / kFp8Pieces, sp = q - t * kFp8Pieces;
-      const int32_t sv = rd->sl[v * kTX + t];
-      lds_dma16_row(kv_rs, sv < 0 ? 0 : sv, (sp ^ fp8_swz(t)) << 4, dst + cc * 1024);
+    for (int u = 0; u < kStepsF / 2; ++u)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) qf[2 * u + h] = qrow[8 * u + 2 * grp + h];
+  }
+
+  // ---- staging of tile v: every wave issues the same four loads per tile.  Loads 0 and 1 of
+  // wave w read the tile's 16-byte pieces q = 64(w + 8c) + lane (1 KiB of whole rows each), load
+  // 2 the 4 bytes at tile offset 16384 + 256w + 4 lane, load 3 the scale of token 4w + lane % 4.
+  // Tile offset o holds token o / 576 at LDS slot (o % 576) / 16, i.e. the row's logical piece
+  // slot ^ fp8_swz(token).  Tiles past the chunk re-read row 0 and are never used, so every
+  // step issues the same loads.
+  struct Stage {
+    u32x4 d[2];
+    uint32_t e;
+    float sc;
+    uint32_t dead;   // bit c: load c belongs to a skipped token
+  };
+  const int e_off = kTFBytes - 2048 + 256 * wave + 4 * lane;   // tile offset of load 2
+  auto row_src = [&](int o, int32_t sv) {                       // global address of tile offset o
+    const int t = o / kRowDim, w = o - t * kRowDim;
+    return (const uint8_t*)p.kv + (int64_t)(sv < 0 ? 0 : sv) * kRowDim + ((((w >> 4) ^ fp8_swz(t)) << 4) | (w & 15));
+  };
+  auto load_tile = [&](const FDSmem* __restrict__ rd, Stage& st, int v) {
+    const bool real = v < ntiles;
+    const int vb = (real ? v : 0) * kTF;          // (a tile past the chunk reads entries it ignores)
+    uint32_t dead = 0u;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int o = ((wave + 8 * c) * 64 + lane) * 16;
+      const int32_t sl_t = rd->sl[vb + o / kRowDim];
+      const int32_t sv = real ? sl_t : 0;
+      dead |= (sv < 0 ? 1u : 0u) << c;
+      st.d[c] = *(const u32x4*)row_src(o, sv);
     }
-    if (wave == 0) {
-      const int32_t ss = rd->sl[v * kTX + lane];
-      lds_dma4_row(sc_rs, ss < 0 ? 0 : ss, dst + kTXBytes);
+    {
+      const int32_t sl_t = rd->sl[vb + e_off / kRowDim];
+      const int32_t sv = real ? sl_t : 0;
+      dead |= (sv < 0 ? 4u : 0u);
+      st.e = *(const uint32_t*)row_src(e_off, sv);
     }
+    const int32_t sl_s = rd->sl[vb + 4 * wave + (lane & 3)];
+    const int32_t ss = real ? sl_s : 0;
+    st.sc = p.kv_scale[ss < 0 ? 0 : ss];
+    st.dead = dead;
+  };
+  auto store_tile = [&](const Stage& st, uint8_t* __restrict__ dst) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int o = ((wave + 8 * c) * 64 + lane) * 16;
+      *(u32x4*)(dst + o) = (st.dead >> c) & 1u ? u32x4{0u, 0u, 0u, 0u} : st.d[c];
+    }
+    *(uint32_t*)(dst + e_off) = st.dead & 4u ? 0u : st.e;
+    if (lane < 4) *(float*)(dst + kTFBytes + 4 * (4 * wave + lane)) = st.sc;
   };
 
-  // the first kRingX-1 tiles are requested before q is loaded and split, so their copies are
-  // in flight meanwhile
-#pragma unroll
-  for (int v = 0; v < kRingX - 1; ++v)
-    if (v < ntiles) issue(&sm, sm.ring[v], v);
-  // q of this wave's S^T head group (head 16w + m16) as two e4m3 parts: scaled by 2^qs so that
-  // its largest magnitude lies in [128, 256), hi = e4m3(q 2^qs) and lo = e4m3(q 2^qs - hi), so
-  // hi + lo = q 2^qs exactly for every element down to 2^-18 of the largest (e4m3 holds 4
-  // significant bits, bf16 8).  S^T then runs on the e4m3 matrix core with no widening of the
-  // rows.  K block b (of 5) gives lane group grp, in bytes 0-15 / 16-31, the dims
-  // 64u + 16grp .. +16 of u = 2b / 2b + 1 (u = 9: zeros), the rows' operand following suit.
-  i32x8 qh[kKBlocksX], ql[kKBlocksX];
-  float q_unscale = 1.f;                          // 2^-qs
-  if (s_active) {
-    const bf16x8* qrow = (const bf16x8*)((const __bf16*)p.q + ((int64_t)r * p.H + wave * 16 + m16) * kRowDim);
-    bf16x8 raw[kStepsX];
-#pragma unroll
-    for (int u = 0; u < kStepsX / 2; ++u)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) raw[2 * u + h] = qrow[8 * u + 2 * grp + h];
-    float mx = 0.f;
-#pragma unroll
-    for (int i = 0; i < kStepsX; ++i)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf((float)raw[i][e]));
-    mx = lanes4_max(mx);
-    // exponent of mx (mx = f * 2^ex, f in [1, 2)): qs = 7 - ex puts mx in [128, 256)
-    // (qs is capped at 126 so that 2^-qs stays a normal float: a head whose largest |q| is
-    // below 2^-119, subnormals included, keeps fewer significant bits, on logits of ~1e-36)
-    const int ex = mx > 0.f ? (int)((__float_as_uint(mx) >> 23) & 255u) - 127 : 7;
-    const int qs = min(7 - ex, 126);
-    q_unscale = __uint_as_float((uint32_t)(127 - qs) << 23);
-#pragma unroll
-    for (int b = 0; b < kKBlocksX; ++b) {
-      qh[b] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
-      ql[b] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int i = 0; i < kStepsX; ++i)   // raw[i] = dims 64(i/2) + 16grp + 8(i%2) .. +8
-#pragma unroll
-      for (int w2 = 0; w2 < 2; ++w2) {   // 4 values per register
-        int hw, lw;
-        split_e4m3_x4(ldexpf((float)raw[i][4 * w2], qs), ldexpf((float)raw[i][4 * w2 + 1], qs),
-                      ldexpf((float)raw[i][4 * w2 + 2], qs), ldexpf((float)raw[i][4 * w2 + 3], qs), hw, lw);
-        // step i = 2u + h: block b = u / 2, bytes 16(u % 2) + 8h + 4w2
-        const int u = i >> 1, hh = i & 1, b = u >> 1;
-        const int word = 4 * (u & 1) + 2 * hh + w2;
-        qh[b][word] = hw;
-        ql[b][word] = lw;
-      }
-  }
-  if (!s_active) {   // head groups past the head count: P = 0 for every tile
-    sm.pex[wave][0][lane] = bf16x8{};
-    sm.pex[wave][1][lane] = bf16x8{};
-  }
-  if (threadIdx.x == 0) sm.redo = 0;
+  Stage X, Y, Z;
+  load_tile(&sm, X, 0);
+  load_tile(&sm, Y, 1);
+  load_tile(&sm, Z, 2);
 
-  // P.V accumulators: head group g, output block 8w + db; lane holds O^T[d][head g*16 + m16]
-  f32x4 o[4][kDBlocksW];
-#pragma unroll
-  for (int g = 0; g < 4; ++g)
-#pragma unroll
-    for (int db = 0; db < kDBlocksW; ++db) o[g][db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_ref = -INFINITY;   // S^T head group: the head's reference R (z * log2(e) units)
-  float m_seen = -INFINITY;  // the head's largest logit so far
+  // P.V accumulators: head group g, output block db; lane holds O^T[64w + 16db + 4grp + j][16g + m16]
+  f32x4 o[4][kDBlocksF];
+  const float scale2 = p.sm_scale * kLog2e;
+  float ref = 0.f;           // R of this lane's head
+  float m_seen = -INFINITY;  // the head's largest logit in this wave's token block
   float l_run = 0.f;         // this lane group's share of sum exp2(z - R)
-  bool over = false;         // a logit of this lane's head exceeded R + kRefMargin
-  const float scale2 = p.sm_scale * kLog2e * q_unscale;   // (q_unscale: exact power of two)
 
-  // S^T operand of block beta (tokens 16beta + m16), steps 2u and 2u+1: logical piece
-  // 4u + grp, read whole; pieces 4 apart lie 64 bytes apart
-  int a_base[4];
-#pragma unroll
-  for (int beta = 0; beta < 4; ++beta) a_base[beta] = fp8_pos(16 * beta + m16, grp);
-  // V^T operand of output block 8w + db, K half kq: row e = m16/2 of the group's 8x16 block is
-  // token 32kq + tau(grp, e); pieces 4 apart lie 64 bytes apart
+  // S^T operand: token 16tb + m16, logical piece 4u + grp at a_off + 64u
+  const int a_off = fp8_pos(16 * tb + m16, grp);
+  // V^T operand of output block db: row e = m16/2 of the group's 8x16 block is token tau(grp, e);
+  // value block 4w + db is logical piece db of the 64-byte group at 64w
   const int e_row = m16 >> 1;
   const int tau = e_row < 4 ? 4 * grp + e_row : 16 + 4 * grp + (e_row - 4);
-  int v_base[2][4];
+  int v_base[kDBlocksF];
 #pragma unroll
-  for (int kq = 0; kq < 2; ++kq)
-#pragma unroll
-    for (int d4 = 0; d4 < 4; ++d4) v_base[kq][d4] = fp8_pos(32 * kq + tau, d4) + 8 * (m16 & 1) + 128 * wave;
+  for (int db = 0; db < kDBlocksF; ++db) v_base[db] = fp8_pos(tau, db) + 8 * (m16 & 1) + 64 * wave;
 
-  // one tile: rd = shared memory as this iteration reads (and, for skipped rows, zeroes) it;
-  // dst = the ring slot that receives tile v + kRingX - 1
-  auto tile = [&](FXSmem* __restrict__ rd, uint8_t* __restrict__ dst, int v) {
-    if (v + kRingX - 1 < ntiles) issue(rd, dst, v + kRingX - 1);
-    uint8_t* T = rd->ring[v % kRingX];
-    const float* sc_t = (const float*)(T + kTXBytes);
-    const int toff = v * kTX;
-    // skipped tokens (past the chunk, or slot -1) read row 0: zero their rows (every wave reads
-    // the same slot list, so the choice is uniform over the workgroup)
-    if (__ballot(rd->sl[toff + lane] < 0)) {
-      for (int e = threadIdx.x; e < kTX * kFp8Pieces; e += kNTX) {
-        const int t = e / kFp8Pieces, pc = e - t * kFp8Pieces;
-        if (rd->sl[toff + t] < 0) *(u32x4*)(T + t * kRowDim + pc * 16) = u32x4{0u, 0u, 0u, 0u};
-      }
-      lds_barrier();
+  auto s_tile = [&](const uint8_t* __restrict__ T) -> f32x4 {
+    f32x4 acc0 = f32x4{0.f, 0.f, 0.f, 0.f}, acc1 = f32x4{0.f, 0.f, 0.f, 0.f};
+    constexpr int kAhead = 2;
+    u32x4 a[kAhead];
+#pragma unroll
+    for (int u = 0; u < kAhead; ++u) a[u] = *(const u32x4*)(T + a_off + 64 * u);
+#pragma unroll
+    for (int u = 0; u < kStepsF / 2; ++u) {
+      const u32x4 x = a[u % kAhead];
+      if (u + kAhead < kStepsF / 2) a[u % kAhead] = *(const u32x4*)(T + a_off + 64 * (u + kAhead));
+      const bf16x8 lo = fp8x8_to_bf16x8(x[0], x[1]);
+      const bf16x8 hi = fp8x8_to_bf16x8(x[2], x[3]);
+      // two accumulators so that consecutive MFMAs do not wait on each other
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, qf[2 * u], acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, qf[2 * u + 1], acc1, 0, 0, 0);
     }
-
-    if (s_active) {
-      // ---- S^T for the 64 tokens (four blocks) x 16 heads, full K, operands read one step ahead
-      f32x4 sacc[4];
+    return acc0 + acc1;
+  };
+  // lane holds head 16hg + m16, tokens 16tb + 4grp + j: logits (scale folded), -inf if skipped
+  auto logits = [&](const FDSmem* __restrict__ rd, const uint8_t* __restrict__ T, int v, const f32x4& sacc,
+                    float (&z)[4], float (&sc)[4]) {
+    const int t0 = 16 * tb + 4 * grp;
+    const int32_t* slt = rd->sl + v * kTF + t0;
+    const f32x4 sc4 = *(const f32x4*)(T + kTFBytes + 4 * t0);
+    float tmax = -INFINITY;
 #pragma unroll
-      for (int beta = 0; beta < 4; ++beta) sacc[beta] = f32x4{0.f, 0.f, 0.f, 0.f};
-      {
-        // e4m3 x e4m3 on v_mfma_scale_f32_16x16x128_f8f6f4 (unit scales), q hi then lo into the
-        // same accumulator; operands of K block b+1 are requested before block b is computed
-        constexpr int kU = kStepsX / 2;             // 9 double steps of 64 dims
-        u32x4 a[2][2][4];
-#pragma unroll
-        for (int beta = 0; beta < 4; ++beta) {
-          a[0][0][beta] = *(const u32x4*)(T + a_base[beta]);
-          a[0][1][beta] = *(const u32x4*)(T + a_base[beta] + 64);
-        }
-#pragma unroll
-        for (int b = 0; b < kKBlocksX; ++b) {
-          if (b + 1 < kKBlocksX) {
-#pragma unroll
-            for (int beta = 0; beta < 4; ++beta) {
-              a[(b + 1) & 1][0][beta] = *(const u32x4*)(T + a_base[beta] + 64 * (2 * b + 2));
-              if (2 * b + 3 < kU) a[(b + 1) & 1][1][beta] = *(const u32x4*)(T + a_base[beta] + 64 * (2 * b + 3));
-            }
-          }
-#pragma unroll
-          for (int beta = 0; beta < 4; ++beta) {
-            const u32x4 lo4 = a[b & 1][0][beta];
-            const u32x4 hi4 = 2 * b + 1 < kU ? a[b & 1][1][beta] : u32x4{0u, 0u, 0u, 0u};
-            const i32x8 av = {(int)lo4[0], (int)lo4[1], (int)lo4[2], (int)lo4[3],
-                              (int)hi4[0], (int)hi4[1], (int)hi4[2], (int)hi4[3]};
-            sacc[beta] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, qh[b], sacc[beta], 0, 0, 0, 127, 0, 127);
-            sacc[beta] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, ql[b], sacc[beta], 0, 0, 0, 127, 0, 127);
-          }
-        }
-      }
-      // ---- online softmax; lane holds head 16w + m16, tokens 16beta + 4grp + j
-      float z[16], sc[16];
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int beta = 0; beta < 4; ++beta) {
-        const int t0 = 16 * beta + 4 * grp;
-        const f32x4 sc4 = *(const f32x4*)(sc_t + t0);
-        const int32_t* slt = rd->sl + toff + t0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          sc[4 * beta + j] = sc4[j];
-          const float zz = slt[j] >= 0 ? sacc[beta][j] * sc4[j] * scale2 : -INFINITY;
-          z[4 * beta + j] = zz;
-          tmax = fmaxf(tmax, zz);
-        }
-      }
-      tmax = lanes4_max(tmax);
-      m_ref = m_ref == -INFINITY ? tmax : m_ref;   // the first tile with a live token sets R
-      m_seen = fmaxf(m_seen, tmax);
-      over |= tmax > m_ref + kRefMargin;
-      // P^T operand of K half kq: tokens 32kq + tau(grp, e) = blocks 2kq, 2kq+1, rows 4grp + j
-#pragma unroll
-      for (int kq = 0; kq < 2; ++kq) {
-        bf16x8 pb;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float ze = z[8 * kq + e];
-          const float pe = ze == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ze - m_ref);
-          l_run += pe;
-          pb[e] = (__bf16)(pe * sc[8 * kq + e]);
-        }
-        rd->pex[wave][kq][lane] = pb;
-      }
+    for (int j = 0; j < 4; ++j) {
+      sc[j] = sc4[j];
+      z[j] = slt[j] >= 0 ? sacc[j] * sc4[j] * scale2 : -INFINITY;
+      tmax = fmaxf(tmax, z[j]);
     }
-    lds_barrier();   // P and the rescale factors of every head group are published
-
-    // ---- O^T += V^T . P^T over this wave's 128 output values, all four head groups (a group
-    // past the head count has P = 0 and is never written out).  All V^T operands of the tile
-    // are requested first, so their latency overlaps the rescale check and the P reads.
-    u32x2 raw[kDBlocksW][2];
+    return lanes4_max(tmax);   // over the block's 16 tokens
+  };
+  auto publish = [&](FDSmem* __restrict__ rd, const float (&z)[4], const float (&sc)[4]) {
+    bf16x4 pb;
 #pragma unroll
-    for (int db = 0; db < kDBlocksW; ++db)
+    for (int j = 0; j < 4; ++j) {
+      const float pe = z[j] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(z[j] - ref);
+      l_run += pe;
+      pb[j] = (__bf16)(pe * sc[j]);
+    }
+    *(bf16x4*)((uint8_t*)&rd->pex[hg][lane] + 8 * tb) = pb;
+  };
+  auto pv_tile = [&](const FDSmem* __restrict__ rd, const uint8_t* __restrict__ T) {
+    u32x2 raw[kDBlocksF];
 #pragma unroll
-      for (int kq = 0; kq < 2; ++kq)
-        raw[db][kq] = __builtin_bit_cast(
-            u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                       (__attribute__((address_space(3))) i32x2*)(T + v_base[kq][db & 3] + 64 * (db >> 2))));
-    bf16x8 pg[4][2];
+    for (int db = 0; db < kDBlocksF; ++db)
+      raw[db] = __builtin_bit_cast(
+          u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)(T + v_base[db])));
+    bf16x8 av[kDBlocksF];
+#pragma unroll
+    for (int db = 0; db < kDBlocksF; ++db) av[db] = fp8x8_to_bf16x8(raw[db][0], raw[db][1]);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      pg[g][0] = rd->pex[g][0][lane];
-      pg[g][1] = rd->pex[g][1][lane];
-    }
+      const bf16x8 pg = rd->pex[g][lane];
 #pragma unroll
-    for (int db = 0; db < kDBlocksW; ++db) {
-#pragma unroll
-      for (int kq = 0; kq < 2; ++kq) {
-        const bf16x8 av = fp8x8_to_bf16x8(raw[db][kq][0], raw[db][kq][1]);
-#pragma unroll
-        for (int g = 0; g < 4; ++g) o[g][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pg[g][kq], o[g][db], 0, 0, 0);
-      }
+      for (int db = 0; db < kDBlocksF; ++db) o[g][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[db], pg, o[g][db], 0, 0, 0);
     }
   };
-
-  // pass 0 with R from the first live tile; pass 1 (rare) with R = the chunk's largest logit
-  for (int pass = 0; pass < 2; ++pass) {
-    if (pass == 1) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-#pragma unroll
-        for (int db = 0; db < kDBlocksW; ++db) o[g][db] = f32x4{0.f, 0.f, 0.f, 0.f};
-      l_run = 0.f;
-      m_ref = m_seen;
-      over = false;
-#pragma unroll
-      for (int v = 0; v < kRingX - 1; ++v)
-        if (v < ntiles) issue(&sm, sm.ring[v], v);
-    }
-    for (int v = 0; v < ntiles; ++v) {
-      const int later = min(kRingX - 2, ntiles - 1 - v);
-      if (wave == 0) {
-        if (later >= 2) wait_vmcnt<2 * (kTXCopies / 4 + 1)>();
-        else if (later == 1) wait_vmcnt<kTXCopies / 4 + 1>();
-        else wait_vmcnt<0>();
-      } else {
-        if (later >= 2) wait_vmcnt<2 * (kTXCopies / 4)>();
-        else if (later == 1) wait_vmcnt<kTXCopies / 4>();
-        else wait_vmcnt<0>();
+  // one tile (v, in ring slot T): S^T, the first tile's reference, P, then P.V
+  auto tile = [&](FDSmem* __restrict__ rd, const uint8_t* __restrict__ T, int v, bool first) {
+    float z[4], sc[4];
+    float tmax = -INFINITY;
+    if (s_active) tmax = logits(rd, T, v, s_tile(T), z, sc);
+    if (first) {
+      // the reference: the first tile's largest logit over both token blocks (0 without one)
+      if (s_active && grp == 0) rd->m0[tb][hg * 16 + m16] = tmax;
+      lds_barrier();
+      if (s_active) {
+        const float m0 = fmaxf(rd->m0[0][hg * 16 + m16], rd->m0[1][hg * 16 + m16]);
+        ref = m0 == -INFINITY ? 0.f : m0;
       }
-      lds_barrier();   // tile v landed for every wave; ring slot (v-1) % kRingX and P are no longer read
-      tile(&sm, sm.ring[(v + kRingX - 1) % kRingX], v);
     }
-    if (s_active && __any(over)) sm.redo = 1;
-    __syncthreads();   // (also: the last tile is no longer read before pass 1 refills the ring)
-    if (pass == 1 || sm.redo == 0) break;
+    if (s_active) {
+      m_seen = fmaxf(m_seen, tmax);
+      publish(rd, z, sc);
+    }
+    lds_barrier();   // P of the tile is published
+    pv_tile(rd, T);
+  };
+
+  // Pipeline: while tile v is computed from ring slot v % 3, the loads of tiles v+2 and v+3 are
+  // in flight, and tile v+1 (requested two steps earlier) is stored into slot (v+1) % 3
+  // afterwards.  Three steps per loop trip, so X, Y and Z keep their registers.  Pass 0 takes R
+  // from the first tile; pass 1 (rare) recomputes the chunk with R = the largest logit.  Each
+  // pass has its own copy of the loop (the lambda is expanded twice), so that the compiler sees
+  // one fixed set of loads in flight at each loop entry and its waits before the stores stay
+  // partial.
+  auto run_pass = [&](bool first) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int db = 0; db < kDBlocksF; ++db) o[g][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    l_run = 0.f;
+    store_tile(X, sm.ring[0]);
+    lds_barrier();   // tile 0 landed
+    for (int v = 0; v < ntiles; v += 3) {
+      load_tile(&sm, X, v + 3);
+      tile(&sm, sm.ring[0], v, first && v == 0);
+      store_tile(Y, sm.ring[1]);
+      lds_barrier();   // tile v + 1 landed; tile v and its P are no longer read
+      load_tile(&sm, Y, v + 4);
+      if (v + 1 < ntiles) tile(&sm, sm.ring[1], v + 1, false);
+      store_tile(Z, sm.ring[2]);
+      lds_barrier();   // tile v + 2 landed
+      load_tile(&sm, Z, v + 5);
+      if (v + 2 < ntiles) tile(&sm, sm.ring[2], v + 2, false);
+      store_tile(X, sm.ring[0]);
+      lds_barrier();   // tile v + 3 landed
+    }
+    // does some head's largest logit lie outside R +- 64?
+    if (s_active) {
+      const float l_blk = lanes4_sum(l_run);   // (all lanes of the wave take part)
+      if (grp == 0) {
+        sm.fin_m[tb][hg * 16 + m16] = m_seen;
+        sm.fin_l[tb][hg * 16 + m16] = l_blk;
+      }
+    }
+    __syncthreads();
+  };
+  run_pass(true);
+  {
+    float mx = -INFINITY;
+    if (s_active) {
+      mx = fmaxf(sm.fin_m[0][hg * 16 + m16], sm.fin_m[1][hg * 16 + m16]);
+      if (mx > -INFINITY && (mx > ref + kRefMargin || mx < ref - kRefMargin)) sm.redo = 1;
+    }
+    __syncthreads();
+    if (sm.redo) {
+      ref = mx > -INFINITY ? mx : 0.f;
+      load_tile(&sm, X, 0);
+      load_tile(&sm, Y, 1);
+      load_tile(&sm, Z, 2);
+      run_pass(false);
+    }
   }
 
-  // ---- final reference and sum per head, then each wave writes its 128 output values
-  if (s_active) {
-    const float l_tot = lanes4_sum(l_run);
-    if (grp == 0) {
-      sm.fin_m[wave * 16 + m16] = m_ref;
-      sm.fin_l[wave * 16 + m16] = l_tot;
-    }
-  }
-  __syncthreads();
+  // ---- output: each wave writes its 64 values of every head
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     if (g >= ngroups) break;
     const int head = g * 16 + m16;
-    const float mh = sm.fin_m[head], lh = sm.fin_l[head];
+    const float mh = fmaxf(sm.fin_m[0][head], sm.fin_m[1][head]);
+    const float lh = sm.fin_l[0][head] + sm.fin_l[1][head];
+    // R of this head as its S^T waves used it (recomputed from what they published)
+    const float m0 = fmaxf(sm.m0[0][head], sm.m0[1][head]);
+    const float rh = sm.redo ? (mh > -INFINITY ? mh : 0.f) : (m0 == -INFINITY ? 0.f : m0);
     const float inv = lh > 0.f ? 1.f / lh : 0.f;
-    // lane holds O^T[d = 128w + db*16 + grp*4 + j][head]
     float* dst;
     if (p.n_split == 1) {
-      dst = p.out + ((int64_t)r * p.H + head) * kVDim + wave * 128 + grp * 4;
+      dst = p.out + ((int64_t)r * p.H + head) * kVDim + wave * 64 + grp * 4;
       if (p.lse && wave == 0 && grp == 0)
-        p.lse[(int64_t)r * p.H + head] = lh > 0.f ? (mh + log2f(lh)) * kLn2 : -INFINITY;
+        p.lse[(int64_t)r * p.H + head] = lh > 0.f ? (rh + log2f(lh)) * kLn2 : -INFINITY;
     } else {
       const int64_t prow = ((int64_t)r * p.n_split + split) * p.H + head;
-      dst = p.part_o + prow * kVDim + wave * 128 + grp * 4;
+      dst = p.part_o + prow * kVDim + wave * 64 + grp * 4;
       if (wave == 0 && grp == 0) {
-        p.part_m[prow] = lh > 0.f ? mh * kLn2 : -INFINITY;
+        p.part_m[prow] = lh > 0.f ? rh * kLn2 : -INFINITY;
         p.part_l[prow] = lh;
       }
     }
 #pragma unroll
-    for (int db = 0; db < kDBlocksW; ++db) *(f32x4*)(dst + db * 16) = o[g][db] * inv;
+    for (int db = 0; db < kDBlocksF; ++db) *(f32x4*)(dst + db * 16) = o[g][db] * inv;
   }
 }
 
@@ -1417,11 +1389,11 @@ __global__ __launch_bounds__(256) void mla_combine_few_kernel(CombineParams p) {
 int mla_default_split(int rows, int H, int k, dsa_dtype_t kv_dtype) {
   (void)H;
   // about one workgroup per compute unit, at least 64 selected rows per chunk, and for fp8 rows
-  // at most kChunkX (the wide fp8 kernel's staging limit)
+  // at most kChunkF (the fp8 ring kernel's staging limit)
   int ns = 256 / (rows > 0 ? rows : 1);
   const int max_ns = (k + 63) / 64;
   if (ns > max_ns) ns = max_ns;
-  const int min_ns = kv_dtype == DSA_FP8_E4M3FN ? (k + kChunkX - 1) / kChunkX : 1;
+  const int min_ns = kv_dtype == DSA_FP8_E4M3FN ? (k + kChunkF - 1) / kChunkF : 1;
   if (ns < min_ns) ns = min_ns;
   if (ns < 1) ns = 1;
   return ns;
@@ -1443,7 +1415,9 @@ hipError_t launch_mla(const MlaParams& p0, dsa_dtype_t q_dtype, dsa_dtype_t kv_d
   p.chunk = chunk;
   const dim3 grid((unsigned)p.n_split, (unsigned)p.rows);
   if (kv_dtype == DSA_FP8_E4M3FN) {
-    if (chunk <= kChunkX) hipLaunchKernelGGL(mla_fp8x_kernel, grid, dim3(kNTX), 0, s, p);
+    if (chunk <= kChunkF)
+      hipLaunchKernelGGL(mla_fp8d_kernel, dim3((unsigned)((p.rows >= 8 ? (p.rows + 7) / 8 * 8 : p.rows) * p.n_split)),
+                         dim3(kNTF), 0, s, p);
     else hipLaunchKernelGGL(mla_fp8_kernel, grid, dim3(kNT), 0, s, p);
   }
   else if (chunk <= kChunkD)

@@ -133,9 +133,10 @@ def test_mla_workspace_sizes(L):
     need = L.dsa_sparse_mla_workspace_size(1, 1, 64, 2048, 4, dsa.DSA_BF16, dsa.DSA_BF16)
     assert need >= 4 * 64 * 512 * 4 + 2 * 4 * 64 * 4
     assert L.dsa_sparse_mla_workspace_size(1, 1, 16, 2048, 4, dsa.DSA_F32, dsa.DSA_BF16) == 0   # vector path: no split
-    # many rows fill the GPU with one chunk each; fp8 rows keep chunks of at most 1024 rows
+    # many rows fill the GPU with one chunk each; fp8 rows keep chunks of at most 2048 rows
     assert L.dsa_sparse_mla_default_split(4096, 1, 64, 2048, dsa.DSA_BF16) == 1
-    assert L.dsa_sparse_mla_default_split(4096, 1, 64, 2048, dsa.DSA_FP8_E4M3FN) == 2
+    assert L.dsa_sparse_mla_default_split(4096, 1, 64, 2048, dsa.DSA_FP8_E4M3FN) == 1
+    assert L.dsa_sparse_mla_default_split(4096, 1, 64, 4096, dsa.DSA_FP8_E4M3FN) == 2
     assert L.dsa_sparse_mla_default_split(64, 2, 64, 2048, dsa.DSA_FP8_E4M3FN) == 2
 
 

@@ -230,9 +230,11 @@ def test_sparse_mla_wide_logit_range(name, ns):
     Head 3 meets one selected row, late in the chunk, whose logit lies more than 64 (log2
     units) above the rest; head 7 sees every logit near -200 and, in the second chunk, a first
     tile with no live slot.  Both need the second pass of the kernels; the expected values are
-    the oracle's.  fp8 rows: the e4m3 matrix core accumulates S^T with an error of about
-    1e-4 * sum |q_d k_d|, which the boosted row's large norm makes visible in every head, so the
-    bound there is relative to each head's output scale and looser."""
+    the oracle's.  fp8 rows: the logits are exact products accumulated in fp32 (the e4m3
+    codes are widened to bf16), but each token's scale is folded into its bf16 P weight, so a
+    dominant row's contribution carries a relative rounding of up to 2^-9; the boosted row's
+    large norm makes that visible in every head, so the output bound there is relative to each
+    head's output scale (2^-8), while the direction (cosine) and lse keep the strict bar."""
     cfg, inp, _ = _case(name, [3000], seed=106, top_k=512, q_per_seq=1)
     rng = np.random.default_rng(12)
     slots = _random_slots(cfg, rng, 512)
@@ -258,13 +260,13 @@ def test_sparse_mla_wide_logit_range(name, ns):
     if fp8:
         scale = np.maximum(1.0, np.abs(ro).max(axis=-1, keepdims=True))
         err = (np.abs(og - ro) / scale).max()
-        # (logit error of 1e-4 * sum |q_d k_d| ~ 0.005 log2 units for the boosted row, plus
-        # the bf16 rounding of P * scale, 2^-9: about 0.5% of a head's output scale)
-        assert err <= 1e-2, f"scaled max-abs error {err:.3e}"
+        # (the bf16 rounding of P * scale scales a token's whole contribution by at most
+        # 1 +- 2^-9, so the output moves by at most 2^-9 of its scale and keeps its direction)
+        assert err <= 2.0 ** -8, f"scaled max-abs error {err:.3e}"
         g, r = og.reshape(-1, 512), ro.reshape(-1, 512)
         cos = (g * r).sum(1) / (np.linalg.norm(g, axis=1) * np.linalg.norm(r, axis=1))
-        assert cos.min() >= 0.9999, f"min cosine {cos.min():.8f}"
-        assert np.abs(lg - rl).max() <= 1e-2
+        assert cos.min() >= 0.99999, f"min cosine {cos.min():.8f}"
+        assert (np.abs(lg - rl) / np.maximum(1.0, np.abs(rl))).max() <= 1e-4
     else:
         check_attention(og[:, :, keep], ro[:, :, keep], lg[:, :, keep], rl[:, :, keep])
         # head 3 is that one row's V (values of about 100): relative error
