@@ -214,7 +214,7 @@ struct UpProjParams {
   float* v;
   float* part;
   float* y;
-  int32_t R, H, Dv, Dm, ksplit, k_chunk;
+  int32_t R, H, Dv, Dm, ksplit;
 };
 
 // launchers (return hipGetLastError() of the launch)

@@ -7,111 +7,162 @@
 //   v[r, h, j] = sum_d W_UV[h, j, d] * o[r, h, d]          (d over the 512 latent values)
 //   y[r, m]    = sum_{h, j} W_O[m, h*Dv + j] * v[r, h, j]
 //
-// Both products run on v_mfma_f32_16x16x32_bf16 (16 rows of r as M, 16 output columns as N).
-// The weights are bf16; the activations (o, and v in between) are f32, fed as two bf16 parts
-// hi = bf16(a), lo = bf16(a - hi), so a = hi + lo to 2^-18 relative and each product is exact
-// in the fp32 accumulator: the result is an fp32-accurate projection.  In decode the rows are few
-// (1-128) and the kernels stream the weights once (8 MB of W_UV and 100 MB of W_O at 64 heads,
-// Dv = 128, Dm = 6144), so they are bounded by HBM; up_y_kernel splits K over workgroups when the
-// rows alone would not fill the GPU, and up_reduce_kernel adds the partial sums in a fixed order.
-#include <type_traits>
-
+// Both are products C[r, n] = sum_k A[r, k] * B[n, k] with f32 activations A and bf16 weights B
+// (B row n contiguous along k), run by one tiled kernel, up_gemm_kernel, on
+// v_mfma_f32_16x16x32_bf16.  The activations enter the matrix core as two bf16 parts,
+// hi = bf16(a) and lo = bf16(a - hi), so a = hi + lo to 2^-18 relative and each product is exact
+// in the fp32 accumulator: the result is an fp32-accurate projection.
+//   * A workgroup (4 waves) owns a tile of up to 128 rows x 128 columns (x 256 when there are
+//     many rows) and a range of k.  Each 128-wide (64-wide) chunk of k of the tile's activations
+//     is loaded once, split into its two bf16 parts and stored in LDS (rows padded by 16 bytes,
+//     so the operand reads are free of bank conflicts); wave w reads the weights of its 32 (64)
+//     columns straight into registers.
+//     Weights are therefore read once per row tile (once in decode, where the rows are few), and
+//     the next chunk's loads are in flight while the current one is multiplied.
+//   * v: one group of tiles per head (A = o[:, h, :], B = W_UV[h], K = 512).  y: K = H * Dv is
+//     split over workgroups when the tiles alone would not fill the GPU; up_reduce_kernel adds
+//     the partial sums in split order, so the result is deterministic.
 #include "dsa_internal.hpp"
 
 namespace dsa {
 
 namespace {
 
-constexpr int kUT = 256;   // threads per workgroup (4 waves, 16 output columns each)
+constexpr int kGT = 256;              // threads per workgroup (4 waves)
 
-// 8 f32 values -> bf16 hi and lo parts (round to nearest even both times)
-__device__ __forceinline__ void split8(const f32x4& a0, const f32x4& a1, bf16x8& hi, bf16x8& lo) {
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float x = e < 4 ? a0[e] : a1[e - 4];
-    const __bf16 h = (__bf16)x;
-    hi[e] = h;
-    lo[e] = (__bf16)(x - (float)h);
-  }
-}
+// C[g][split][r][n] = sum over k in the split's range of A[g][r][k] * B[g][n][k]
+struct GemmArgs {
+  const float* A;
+  int64_t lda, a_gs;                  // row r of group g: A + g*a_gs + r*lda
+  const __bf16* B;
+  int64_t ldb, b_gs;                  // column n of group g: B + g*b_gs + n*ldb
+  float* C;
+  int64_t ldc, c_gs, c_ks;            // C + g*c_gs + split*c_ks + r*ldc + n
+  int32_t R, N, K, k_chunk, ksplit;
+};
 
-// One wave: C[16 rows x 16 cols] += A[rows, k0:k1] . B[cols, k0:k1]^T with A f32 rows of stride
-// lda (rows >= nrows read as zero) and B bf16 rows of stride ldb.  Lane (n = l % 16, g = l / 16)
-// supplies, for each 32-wide k step, A row n and B row n at k + 8g .. +8.
-__device__ __forceinline__ f32x4 mma_rows(const float* __restrict__ A, int64_t lda, int nrows,
-                                          const __bf16* __restrict__ Bm, int64_t ldb, int k0, int k1) {
+// RB blocks of 16 rows per tile (1, 2, 4 or 8), CB blocks of 16 columns per wave (2 or 4), KC
+// contraction values per staged chunk (64 or 128)
+template <int RB, int CB, int KC>
+__global__ __launch_bounds__(kGT) void up_gemm_kernel(GemmArgs g) {
+  constexpr int kGN = 4 * 16 * CB;    // columns per tile
+  constexpr int kPitch = KC + 8;      // bf16 per staged row (144 or 272 bytes: conflict-free reads)
+  constexpr int kS = KC / 32;         // k steps per chunk
+  constexpr int kF4 = KC / 4;         // float4 per staged row
+  __shared__ __attribute__((aligned(16))) __bf16 as[2][2][RB * 16][kPitch];   // [buffer][hi, lo][row][k]
+
   const int lane = threadIdx.x & 63;
-  const int n = lane & 15, g = lane >> 4;
-  const bool live = n < nrows;
-  const float* a = A + (int64_t)n * lda + 8 * g;
-  const __bf16* bp = Bm + (int64_t)n * ldb + 8 * g;
-  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  // U steps per round: every load of the round is issued before its first MFMA
-  auto round = [&](int k, auto U) {
-    constexpr int NU = decltype(U)::value;
-    f32x4 a0[NU], a1[NU];
-    bf16x8 b[NU];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n16 = lane & 15, grp = lane >> 4;
+  const int col0 = blockIdx.x * kGN;
+  const int row0 = blockIdx.y * (RB * 16);
+  const int gz = blockIdx.z / g.ksplit, split = blockIdx.z - gz * g.ksplit;
+  const int k0 = split * g.k_chunk, k1 = min(g.K, k0 + g.k_chunk);   // k1 > k0 (host), both multiples of 32
+  const int nrows = min(RB * 16, g.R - row0);
+  const int nch = (k1 - k0 + KC - 1) / KC;
+  const float* A = g.A + gz * g.a_gs + (int64_t)row0 * g.lda;
+  const __bf16* B = g.B + gz * g.b_gs;
+
+  // activations of chunk c: float4 e = j*256 + thread is row e / kF4, values 4(e % kF4) .. +4;
+  // rows past the tile and values past the range read a valid address and are replaced by 0
+  constexpr int kAL = RB * 16 * kF4 / kGT;
+  f32x4 ar[kAL];
+  auto load_a = [&](int c) {
+    const int kb = k0 + c * KC;
 #pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      a0[u] = live ? *(const f32x4*)(a + k + 32 * u) : f32x4{0.f, 0.f, 0.f, 0.f};
-      a1[u] = live ? *(const f32x4*)(a + k + 32 * u + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
-      b[u] = *(const bf16x8*)(bp + k + 32 * u);
-    }
-#pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      bf16x8 hi, lo;
-      split8(a0[u], a1[u], hi, lo);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, b[u], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, b[u], acc, 0, 0, 0);
+    for (int j = 0; j < kAL; ++j) {
+      const int e = j * kGT + threadIdx.x;
+      const int r = e / kF4, k = kb + 4 * (e % kF4);
+      const f32x4 x = *(const f32x4*)(A + (int64_t)min(r, nrows - 1) * g.lda + min(k, k1 - 4));
+      ar[j] = (r < nrows && k < k1) ? x : f32x4{0.f, 0.f, 0.f, 0.f};
     }
   };
-  int k = k0;
-  for (; k + 256 <= k1; k += 256) round(k, std::integral_constant<int, 8>{});
-  for (; k < k1; k += 32) round(k, std::integral_constant<int, 1>{});
-  return acc;
-}
-
-// v = per-head W_UV . o.  Workgroup (head h, 16-row block, 64-column block of Dv); wave w takes
-// value columns 64 cb + 16 w .. +16.
-__global__ __launch_bounds__(kUT) void up_v_kernel(UpProjParams p) {
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  const int h = blockIdx.x, r0 = blockIdx.y * 16;
-  const int c0 = blockIdx.z * 64 + wave * 16;
-  if (c0 >= p.Dv) return;                          // (uniform per wave)
-  const int nrows = min(16, p.R - r0);
-  const float* A = p.o + ((int64_t)r0 * p.H + h) * kVDim;          // rows of stride H*512
-  const __bf16* Bm = (const __bf16*)p.w_uv + ((int64_t)h * p.Dv + c0) * kVDim;
-  const f32x4 acc = mma_rows(A, (int64_t)p.H * kVDim, nrows, Bm, kVDim, 0, kVDim);
-  // lane holds C[row 4g + jx][col n]
-  const int n = lane & 15, g = lane >> 4;
+  auto store_a = [&](int buf) {
 #pragma unroll
-  for (int jx = 0; jx < 4; ++jx) {
-    const int r = 4 * g + jx;
-    if (r < nrows) p.v[((int64_t)(r0 + r) * p.H + h) * p.Dv + c0 + n] = acc[jx];
+    for (int j = 0; j < kAL; ++j) {
+      const int e = j * kGT + threadIdx.x;
+      const int r = e / kF4, kk = 4 * (e % kF4);
+      bf16x4 hi, lo;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const __bf16 h = (__bf16)ar[j][i];
+        hi[i] = h;
+        lo[i] = (__bf16)(ar[j][i] - (float)h);
+      }
+      *(bf16x4*)&as[buf][0][r][kk] = hi;
+      *(bf16x4*)&as[buf][1][r][kk] = lo;
+    }
+  };
+  // weights of chunk c for this wave's CB column blocks: lane (n16, grp) of block cb, k step s
+  // reads column col0 + 16(CB w + cb) + n16, values kb + 32s + 8grp .. +8 (0 past the range)
+  auto load_b = [&](bf16x8 (&bb)[CB][kS], int c) {
+    const int kb = k0 + c * KC;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      const int n = min(col0 + 16 * (CB * wave + cb) + n16, g.N - 1);
+#pragma unroll
+      for (int s = 0; s < kS; ++s) {
+        const int k = kb + 32 * s + 8 * grp;
+        const bf16x8 x = *(const bf16x8*)(B + (int64_t)n * g.ldb + min(k, k1 - 8));
+        bb[cb][s] = k < k1 ? x : bf16x8{};
+      }
+    }
+  };
+
+  f32x4 acc[RB][CB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // lane (n16, grp) supplies row 16rb + n16, values 32s + 8grp .. +8 of both parts
+  auto compute = [&](int buf, const bf16x8 (&bb)[CB][kS]) {
+#pragma unroll
+    for (int s = 0; s < kS; ++s)
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const bf16x8 ah = *(const bf16x8*)&as[buf][0][16 * rb + n16][32 * s + 8 * grp];
+        const bf16x8 al = *(const bf16x8*)&as[buf][1][16 * rb + n16][32 * s + 8 * grp];
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+          acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bb[cb][s], acc[rb][cb], 0, 0, 0);
+          acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bb[cb][s], acc[rb][cb], 0, 0, 0);
+        }
+      }
+  };
+
+  // two chunks per loop trip, so that the two weight buffers keep their registers; every step
+  // issues the same loads (the chunk index is clamped past the end)
+  bf16x8 bx[CB][kS], by[CB][kS];
+  load_a(0);
+  load_b(bx, 0);
+  store_a(0);
+  lds_barrier();
+  for (int c = 0; c < nch; c += 2) {
+    load_a(min(c + 1, nch - 1));
+    load_b(by, min(c + 1, nch - 1));
+    compute(0, bx);
+    store_a(1);
+    lds_barrier();   // chunk c + 1 staged; buffer 0 is no longer read
+    load_a(min(c + 2, nch - 1));
+    load_b(bx, min(c + 2, nch - 1));
+    if (c + 1 < nch) compute(1, by);
+    store_a(0);
+    lds_barrier();   // chunk c + 2 staged; buffer 1 is no longer read
   }
-}
 
-// y (or its K-split partial sums) = v . W_O^T.  Workgroup (64-column block, 16-row block,
-// K split ks); wave w takes output columns 64 cb + 16 w .. +16 over its K range.
-__global__ __launch_bounds__(kUT) void up_y_kernel(UpProjParams p) {
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  const int c0 = blockIdx.x * 64 + wave * 16;
-  const int r0 = blockIdx.y * 16, ks = blockIdx.z;
-  if (c0 >= p.Dm) return;                          // (uniform per wave)
-  const int K = p.H * p.Dv;
-  const int k0 = ks * p.k_chunk, k1 = min(K, k0 + p.k_chunk);
-  const int nrows = min(16, p.R - r0);
-  const float* A = p.v + (int64_t)r0 * K;
-  const __bf16* Bm = (const __bf16*)p.w_o + (int64_t)c0 * K;
-  const f32x4 acc = k0 < k1 ? mma_rows(A, K, nrows, Bm, K, k0, k1) : f32x4{0.f, 0.f, 0.f, 0.f};
-  const int n = lane & 15, g = lane >> 4;
-  float* dst = p.ksplit == 1 ? p.y : p.part + (int64_t)ks * p.R * p.Dm;
+  // lane (n16, grp) holds C[16rb + 4grp + j][16(CB w + cb) + n16]
+  float* C = g.C + gz * g.c_gs + split * g.c_ks;
 #pragma unroll
-  for (int jx = 0; jx < 4; ++jx) {
-    const int r = 4 * g + jx;
-    if (r < nrows) dst[(int64_t)(r0 + r) * p.Dm + c0 + n] = acc[jx];
+  for (int cb = 0; cb < CB; ++cb) {
+    const int n = col0 + 16 * (CB * wave + cb) + n16;
+    if (n >= g.N) continue;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = 16 * rb + 4 * grp + j;
+        if (r < nrows) C[(int64_t)(row0 + r) * g.ldc + n] = acc[rb][cb][j];
+      }
   }
 }
 
@@ -125,30 +176,95 @@ __global__ __launch_bounds__(256) void up_reduce_kernel(UpProjParams p) {
   p.y[e] = s;
 }
 
+int rows_per_tile_blocks(int R) { return R <= 16 ? 1 : R <= 32 ? 2 : R <= 64 ? 4 : 8; }
+// column blocks per wave: with at least two rounds of 128 x 256 tiles (many rows), 64 columns
+// per wave, so that each activation operand read from LDS feeds twice the matrix work;
+// otherwise 32, which keeps more workgroups in flight
+int col_blocks_per_wave(int R, int N) {
+  return (int64_t)((N + 255) / 256) * ((R + 127) / 128) >= 512 ? 4 : 2;
+}
+
+template <int RB, int CB, int KC>
+hipError_t launch_gemm_t(const GemmArgs& a, int groups, hipStream_t s) {
+  const dim3 grid((unsigned)((a.N + 64 * CB - 1) / (64 * CB)), (unsigned)((a.R + RB * 16 - 1) / (RB * 16)),
+                  (unsigned)(groups * a.ksplit));
+  hipLaunchKernelGGL((up_gemm_kernel<RB, CB, KC>), grid, dim3(kGT), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm(const GemmArgs& a, int groups, hipStream_t s) {
+  switch (rows_per_tile_blocks(a.R)) {
+    case 1: return launch_gemm_t<1, 2, 128>(a, groups, s);
+    case 2: return launch_gemm_t<2, 2, 128>(a, groups, s);
+    case 4: return launch_gemm_t<4, 2, 128>(a, groups, s);
+    default:
+      if (col_blocks_per_wave(a.R, a.N) == 4)
+        return launch_gemm_t<8, 4, 64>(a, groups, s);   // (chunks of 64 keep 128 x 64 per wave in registers)
+      return launch_gemm_t<8, 2, 128>(a, groups, s);
+  }
+}
+
+// K values per split of a product (a multiple of 32)
+int up_proj_kchunk(int K, int ks) { return ((K + ks - 1) / ks + 31) / 32 * 32; }
+
 }  // namespace
 
 int up_proj_ksplit(int R, int Dm, int K) {
-  // enough workgroups for the 256 compute units (about two rounds), chunks of at least 512
-  const int64_t wg = (int64_t)((Dm + 63) / 64) * ((R + 15) / 16);
-  int ks = (int)((512 + wg - 1) / wg);
-  const int max_ks = K / 512 > 1 ? K / 512 : 1;
-  if (ks > max_ks) ks = max_ks;
+  // enough workgroups for one full round (tiles of up to 32 rows fit two workgroups per compute
+  // unit), splits of at least 512 values, partial sums of at most a quarter of the weight bytes
+  // (2 * ks * R * Dm floats against Dm * K bf16), at most 16 splits; every split non-empty
+  const int rb = rows_per_tile_blocks(R);
+  const int64_t occupancy = rb <= 2 ? 2 : 1;
+  const int cols = rb == 8 ? 64 * col_blocks_per_wave(R, Dm) : 128;
+  const int64_t tiles = (int64_t)((Dm + cols - 1) / cols) * ((R + 16 * rb - 1) / (16 * rb));
+  int64_t ks = 256 * occupancy / tiles;
+  if (ks > K / 512) ks = K / 512;
+  if (ks > K / (16 * (int64_t)R)) ks = K / (16 * (int64_t)R);
+  if (ks > 16) ks = 16;
   if (ks < 1) ks = 1;
-  return ks;
+  const int kc = up_proj_kchunk(K, (int)ks);
+  return (K + kc - 1) / kc;
 }
 
-hipError_t launch_up_proj(const UpProjParams& p0, hipStream_t s) {
-  UpProjParams p = p0;
+hipError_t launch_up_proj(const UpProjParams& p, hipStream_t s) {
   const int K = p.H * p.Dv;
-  hipLaunchKernelGGL(up_v_kernel, dim3((unsigned)p.H, (unsigned)((p.R + 15) / 16), (unsigned)((p.Dv + 63) / 64)),
-                     dim3(kUT), 0, s, p);
-  hipError_t e = hipGetLastError();
+  // v[r, h, :] = W_UV[h] . o[r, h, :]: one group of tiles per head
+  GemmArgs v{};
+  v.A = p.o;
+  v.lda = (int64_t)p.H * kVDim;
+  v.a_gs = kVDim;
+  v.B = (const __bf16*)p.w_uv;
+  v.ldb = kVDim;
+  v.b_gs = (int64_t)p.Dv * kVDim;
+  v.C = p.v;
+  v.ldc = K;
+  v.c_gs = p.Dv;
+  v.c_ks = 0;
+  v.R = p.R;
+  v.N = p.Dv;
+  v.K = kVDim;
+  v.k_chunk = kVDim;
+  v.ksplit = 1;
+  hipError_t e = launch_gemm(v, p.H, s);
   if (e != hipSuccess) return e;
-  // K chunks of whole 32-wide steps
-  p.k_chunk = ((K + p.ksplit - 1) / p.ksplit + 31) / 32 * 32;
-  hipLaunchKernelGGL(up_y_kernel, dim3((unsigned)((p.Dm + 63) / 64), (unsigned)((p.R + 15) / 16), (unsigned)p.ksplit),
-                     dim3(kUT), 0, s, p);
-  e = hipGetLastError();
+  // y (or its K-split partial sums) = v . W_O^T
+  GemmArgs y{};
+  y.A = p.v;
+  y.lda = K;
+  y.a_gs = 0;
+  y.B = (const __bf16*)p.w_o;
+  y.ldb = K;
+  y.b_gs = 0;
+  y.C = p.ksplit == 1 ? p.y : p.part;
+  y.ldc = p.Dm;
+  y.c_gs = 0;
+  y.c_ks = (int64_t)p.R * p.Dm;
+  y.R = p.R;
+  y.N = p.Dm;
+  y.K = K;
+  y.k_chunk = up_proj_kchunk(K, p.ksplit);
+  y.ksplit = p.ksplit;
+  e = launch_gemm(y, 1, s);
   if (e != hipSuccess || p.ksplit == 1) return e;
   const int64_t total = (int64_t)p.R * p.Dm;
   hipLaunchKernelGGL(up_reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, p);

@@ -41,8 +41,11 @@ CASES = [  # rows, heads, value dim, model width
     (128, 64, 128, 6144),    # the fp8 verify workload's 64 x 2 rows
     (3, 16, 32, 48),
     (37, 64, 64, 96),        # a partial 16-row block
-    (20, 8, 96, 160),        # a value dim that leaves a wave of the 64-column block idle
+    (20, 8, 96, 160),        # a value dim that leaves a wave of the 128-column tile idle
     (1, 1, 32, 16),
+    (1, 20, 96, 160),        # K = 1920 over three splits whose last 128-chunk is partial
+    (50, 4, 32, 144),        # 64-row tiles, a ragged second column tile
+    (300, 8, 64, 272),       # three 128-row tiles with a ragged tail, three column tiles
 ]
 
 
