@@ -19,9 +19,11 @@
  *   - Arguments are validated before anything is enqueued: a status other than DSA_OK means
  *     nothing was launched.  dsa_last_error() then describes the problem.  A launch failure
  *     returns DSA_ERR_HIP.  A device that is not gfx950 returns DSA_ERR_UNSUPPORTED.
- *   - Data preconditions that would need a device read to check are the caller's duty and
- *     are not checked: page ids < num_slots / page_size, 1 <= seq_lens[b] <= max_seq_len,
- *     q_per_seq <= seq_lens[b], slot ids < num_slots, no NaN scores.
+ *   - Data preconditions that would need a device read to check are the caller's duty:
+ *     page ids < num_slots / page_size, q_per_seq <= seq_lens[b] <= max_seq_len, slot ids in
+ *     [-1, num_slots), no NaN scores, top-k indices in [-1, seq_lens[b]).  libdsa.so does not
+ *     check them.  libdsa_debug.so, the same sources built with DSA_DEBUG defined, checks them
+ *     on the device (dsa_debug_check below).
  *
  * Notation: B = batch, Q = query tokens per sequence, L_b = seq_lens[b] = cached tokens of
  * sequence b INCLUDING its Q new tokens, pos(b,i) = L_b - Q + i is the position of query i
@@ -268,6 +270,27 @@ dsa_status_t dsa_latent_up_projection(int32_t rows, int32_t n_heads, int32_t v_d
                                       const float *attn_out, const void *w_uv, const void *w_o, float *y,
                                       void *workspace, size_t workspace_bytes, void *stream);
 size_t dsa_latent_up_projection_workspace_size(int32_t rows, int32_t n_heads, int32_t v_dim, int32_t d_model);
+
+/*
+ * Opt-in checks of the data preconditions (the library built with DSA_DEBUG: libdsa_debug.so).
+ * Its kernels test every sequence length, page-table entry, MLA slot, top-k score and page-map
+ * index they read against the preconditions above.  A violation sets its bit in an error word
+ * that the library keeps on each device, and the kernel clamps the value into range (a slot or
+ * index out of range is skipped like -1; the cache append writes nothing for that token), so no
+ * access leaves its buffer; the results are then unspecified but the GPU keeps running.
+ * dsa_debug_check synchronises `stream`, stores the word in *flags (if flags is not NULL),
+ * clears it, and returns DSA_OK when it was 0, otherwise DSA_ERR_INVALID_ARGUMENT with the
+ * violated preconditions in dsa_last_error().  It is not capturable (it reads device memory).
+ * libdsa.so returns DSA_ERR_UNSUPPORTED with *flags = 0.  The word is shared by every call on
+ * one device, so calls that overlap there report together.
+ */
+#define DSA_DEBUG_SEQ_LEN     1u    /* seq_lens[b] outside [q_per_seq, max_seq_len] */
+#define DSA_DEBUG_PAGE_ID     2u    /* a page-table entry outside [0, num_slots / page_size) */
+#define DSA_DEBUG_SLOT        4u    /* a slot of dsa_sparse_mla_decode outside [-1, num_slots) */
+#define DSA_DEBUG_NAN_SCORE   8u    /* a NaN among the scores a top-k ranks */
+#define DSA_DEBUG_TOPK_INDEX 16u    /* an index of dsa_page_map outside [-1, seq_lens[b]) */
+dsa_status_t dsa_debug_check(uint32_t *flags, void *stream);
+int32_t dsa_debug_enabled(void);    /* 1 for libdsa_debug.so, 0 for libdsa.so */
 
 const char *dsa_status_string(dsa_status_t status);
 const char *dsa_last_error(void);   /* thread-local detail for the last non-OK status */

@@ -1,6 +1,8 @@
-"""Compile the gfx950 HIP sources into sparse_attention_10_amd/libdsa.so (in-tree).
+"""Compile the gfx950 HIP sources into sparse_attention_10_amd/libdsa.so (in-tree), and the same
+sources with DSA_DEBUG defined into libdsa_debug.so (opt-in device-side checks of the data
+preconditions, see include/dsa.h).
 
-    python -m sparse_attention_10_amd.build
+    python -m sparse_attention_10_amd.build [--debug-only | --release-only]
 
 Each .hip file is compiled to an object in parallel, then linked with hipcc -shared.
 """
@@ -16,6 +18,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdsa.so")
+BUILD_DEBUG = os.path.join(HERE, "_build_debug")
+LIB_DEBUG = os.path.join(HERE, "libdsa_debug.so")
 SOURCES = ["api.hip", "indexer.hip", "topk.hip", "mla.hip", "cache.hip", "up_proj.hip"]
 ARCH = "gfx950"
 
@@ -34,9 +38,9 @@ def flags():
             f"-I{os.path.join(HERE, '..', 'include')}"]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, debug: bool = False) -> str:
+    obj = os.path.join(BUILD_DEBUG if debug else BUILD, os.path.splitext(src)[0] + ".o")
+    cmd = [hipcc()] + flags() + (["-DDSA_DEBUG"] if debug else []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compiling {src} failed:\n{r.stdout}\n{r.stderr}")
@@ -46,20 +50,25 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, debug: bool = False) -> str:
+    """Build libdsa.so (or, with debug=True, libdsa_debug.so) and return its path."""
+    out = LIB_DEBUG if debug else LIB
+    os.makedirs(BUILD_DEBUG if debug else BUILD, exist_ok=True)
     with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda src: _compile(src, debug), SOURCES))
+    tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"linking libdsa.so failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+        raise RuntimeError(f"linking {os.path.basename(out)} failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {out}")
+    return out
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    if "--debug-only" not in sys.argv:
+        build(verbose=True)
+    if "--release-only" not in sys.argv:
+        build(verbose=True, debug=True)

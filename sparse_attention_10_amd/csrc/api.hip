@@ -55,6 +55,35 @@ dsa_status_t check_device() {
   return DSA_OK;
 }
 
+// The error word of the opt-in device-side checks (DSA_DEBUG builds): one per device, zero when
+// the library is loaded, reached by host code only through the address hipGetSymbolAddress
+// returns for the current device.  Other builds pass no word (nullptr).
+#ifdef DSA_DEBUG
+static __device__ uint32_t g_dbg_word;
+std::atomic<uint32_t*> g_dbg_ptr[kMaxDevices];
+#endif
+
+dsa_status_t debug_word(uint32_t** out) {
+  *out = nullptr;
+#ifdef DSA_DEBUG
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(DSA_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(DSA_ERR_UNSUPPORTED, "device ordinal %d out of range", dev);
+  uint32_t* p = g_dbg_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    void* v = nullptr;
+    e = hipGetSymbolAddress(&v, HIP_SYMBOL(g_dbg_word));
+    if (e != hipSuccess || v == nullptr)
+      return fail(DSA_ERR_HIP, "hipGetSymbolAddress(debug word) failed on device %d: %s", dev, hipGetErrorString(e));
+    p = (uint32_t*)v;
+    g_dbg_ptr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+#endif
+  return DSA_OK;
+}
+
 dsa_status_t launched(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(DSA_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
   return DSA_OK;
@@ -177,7 +206,7 @@ int32_t effective_split(int64_t rows, int32_t H, int32_t k, int32_t n_split, dsa
 
 dsa_status_t run_mla(int64_t rows, const void* q, dsa_dtype_t q_dtype, const void* kv, dsa_dtype_t kv_dtype,
                      const float* kv_scale, int64_t num_slots, const int32_t* slots, int32_t k, int32_t H, float sm_scale, float* out,
-                     float* lse, int32_t ns, void* ws, size_t ws_bytes, hipStream_t s) {
+                     float* lse, int32_t ns, void* ws, size_t ws_bytes, uint32_t* dbg, hipStream_t s) {
   MlaWs w = mla_ws(rows, H, ns);
   if (ws_bytes < w.total || (w.total > 0 && ws == nullptr))
     return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "mla: workspace needs %zu bytes (got %zu)", w.total, ws_bytes);
@@ -195,6 +224,7 @@ dsa_status_t run_mla(int64_t rows, const void* q, dsa_dtype_t q_dtype, const voi
   p.k = k;
   p.n_split = ns;
   p.sm_scale = sm_scale;
+  p.dbg = dbg;
   if (ns > 1) {
     uint8_t* base = (uint8_t*)ws;
     p.part_o = (float*)base;
@@ -245,7 +275,10 @@ dsa_status_t dsa_indexer_scores(const dsa_batch_t* b, const void* q, dsa_dtype_t
                                 int32_t head_dim, float* scores, int64_t scores_ld, void* stream) {
   DSA_TRY(check_indexer(b, q, q_dtype, w, k_cache, k_dtype, k_scale, n_heads, head_dim, scores, scores_ld));
   DSA_TRY(check_device());
+  uint32_t* dbg = nullptr;
+  DSA_TRY(debug_word(&dbg));
   IndexerParams p{};
+  p.dbg = dbg;
   p.seq_lens = b->seq_lens;
   p.page_table = b->page_table;
   p.q = q;
@@ -279,8 +312,11 @@ dsa_status_t dsa_topk(const dsa_batch_t* b, const float* scores, int64_t scores_
     return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "topk: workspace needs %zu bytes (got %zu)", need, workspace_bytes);
   DSA_REQUIRE(need == 0 || aligned(workspace, 256), "topk: workspace must be 256-byte aligned");
   DSA_TRY(check_device());
+  uint32_t* dbg = nullptr;
+  DSA_TRY(debug_word(&dbg));
   TopkParams p{scores, scores_ld, b->seq_lens, b->page_table, topk_idx, topk_slots,
-               b->q_per_seq, k, b->page_size, b->max_pages_per_seq, 0, 0, nullptr, nullptr, 0};
+               b->q_per_seq, k, b->page_size, b->max_pages_per_seq, 0, 0, nullptr, nullptr, 0,
+               b->num_slots, b->max_seq_len, dbg};
   return launched(launch_topk(p, b->batch * b->q_per_seq, b->max_seq_len, workspace, (hipStream_t)stream),
                   "top-k");
 }
@@ -291,9 +327,11 @@ dsa_status_t dsa_page_map(const dsa_batch_t* b, const int32_t* topk_idx, int32_t
   DSA_REQUIRE(k >= 1, "page_map: k must be >= 1");
   DSA_REQUIRE(aligned(topk_idx, 4) && aligned(slots, 4), "page_map: arrays must be 4-byte aligned");
   DSA_TRY(check_device());
+  uint32_t* dbg = nullptr;
+  DSA_TRY(debug_word(&dbg));
   const int64_t total = (int64_t)b->batch * b->q_per_seq * k;
   return launched(launch_page_map(topk_idx, total, k, b->q_per_seq, b->page_table, b->max_pages_per_seq,
-                                  b->page_size, slots, (hipStream_t)stream),
+                                  b->page_size, slots, b->seq_lens, b->num_slots, dbg, (hipStream_t)stream),
                   "page map");
 }
 
@@ -323,8 +361,10 @@ dsa_status_t dsa_sparse_mla_decode(int32_t batch, int32_t q_per_seq, const void*
   if (workspace_bytes < w.total || (w.total > 0 && workspace == nullptr))
     return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "mla: workspace needs %zu bytes (got %zu)", w.total, workspace_bytes);
   DSA_TRY(check_device());
+  uint32_t* dbg = nullptr;
+  DSA_TRY(debug_word(&dbg));
   return run_mla(rows, q, q_dtype, kv_cache, kv_dtype, kv_scale, num_slots, slots, k, n_heads, sm_scale, out, lse, ns,
-                 workspace, workspace_bytes, (hipStream_t)stream);
+                 workspace, workspace_bytes, dbg, (hipStream_t)stream);
 }
 
 dsa_status_t dsa_mla_combine(int32_t rows, int32_t n_heads, int32_t n_split, const float* part_o, const float* part_m,
@@ -406,7 +446,10 @@ dsa_status_t launch_step(const dsa_decode_step_args_t* a, const StepWs& w, void*
   int32_t* idx = a->debug_idx ? a->debug_idx : (int32_t*)(ws + w.idx_off);
   int32_t* slots = a->debug_slots ? a->debug_slots : (int32_t*)(ws + w.slots_off);
 
+  uint32_t* dbg = nullptr;
+  DSA_TRY(debug_word(&dbg));
   IndexerParams ip{};
+  ip.dbg = dbg;
   ip.seq_lens = b->seq_lens;
   ip.page_table = b->page_table;
   ip.q = a->q_idx;
@@ -426,13 +469,14 @@ dsa_status_t launch_step(const dsa_decode_step_args_t* a, const StepWs& w, void*
   DSA_TRY(launched(launch_indexer(ip, a->q_idx_dtype, a->k_dtype, s), "indexer"));
 
   TopkParams tp{scores, w.ld, b->seq_lens, b->page_table, idx, slots,
-                b->q_per_seq, a->top_k, b->page_size, b->max_pages_per_seq, 0, 0, nullptr, nullptr, 0};
+                b->q_per_seq, a->top_k, b->page_size, b->max_pages_per_seq, 0, 0, nullptr, nullptr, 0,
+                b->num_slots, b->max_seq_len, dbg};
   DSA_TRY(launched(launch_topk(tp, b->batch * b->q_per_seq, b->max_seq_len, ws + w.topk_off, s), "top-k"));
 
   const int64_t rows = (int64_t)b->batch * b->q_per_seq;
   const size_t mla_bytes = workspace_bytes - w.mla_off;
   return run_mla(rows, a->q_mla, a->q_mla_dtype, a->kv_cache, a->kv_dtype, a->kv_scale, b->num_slots, slots, a->top_k,
-                 a->mla_heads, a->sm_scale, a->out, a->lse, w.ns, ws + w.mla_off, mla_bytes, s);
+                 a->mla_heads, a->sm_scale, a->out, a->lse, w.ns, ws + w.mla_off, mla_bytes, dbg, s);
 }
 
 // Scratch memory of dsa_decode_step_noalloc: one copy per device, zero-initialised when the
@@ -573,7 +617,45 @@ dsa_status_t dsa_kv_cache_append(const dsa_batch_t* b, const void* kv_new, dsa_d
   p.kv_dst_dtype = kv_dtype;
   p.k_src_dtype = k_new_dtype;
   p.k_dst_dtype = k_dtype;
+  p.num_slots = b->num_slots;
+  p.max_seq_len = b->max_seq_len;
+  DSA_TRY(debug_word(&p.dbg));
   return launched(launch_cache_append(p, (hipStream_t)stream), "cache append");
+}
+
+dsa_status_t dsa_debug_check(uint32_t* flags, void* stream) {
+  if (flags) *flags = 0u;
+#ifdef DSA_DEBUG
+  DSA_TRY(check_device());
+  uint32_t* dbg = nullptr;
+  DSA_TRY(debug_word(&dbg));
+  hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+  if (e != hipSuccess) return fail(DSA_ERR_HIP, "debug_check: stream synchronisation failed: %s", hipGetErrorString(e));
+  uint32_t word = 0u;
+  const uint32_t zero = 0u;
+  e = hipMemcpy(&word, dbg, sizeof(word), hipMemcpyDeviceToHost);
+  if (e == hipSuccess) e = hipMemcpy(dbg, &zero, sizeof(zero), hipMemcpyHostToDevice);
+  if (e != hipSuccess) return fail(DSA_ERR_HIP, "debug_check: reading the error word failed: %s", hipGetErrorString(e));
+  if (flags) *flags = word;
+  if (word == 0u) return DSA_OK;
+  return fail(DSA_ERR_INVALID_ARGUMENT, "debug_check: violated data preconditions (flags 0x%x):%s%s%s%s%s", word,
+              word & kDbgSeqLen ? " seq_lens outside [q_per_seq, max_seq_len];" : "",
+              word & kDbgPageId ? " page-table entry outside [0, num_slots / page_size);" : "",
+              word & kDbgSlot ? " slot outside [-1, num_slots);" : "",
+              word & kDbgNanScore ? " NaN score;" : "",
+              word & kDbgTopkIndex ? " top-k index outside [-1, seq_lens[b]);" : "");
+#else
+  (void)stream;
+  return fail(DSA_ERR_UNSUPPORTED, "debug_check: this library was built without DSA_DEBUG (load libdsa_debug.so)");
+#endif
+}
+
+int32_t dsa_debug_enabled(void) {
+#ifdef DSA_DEBUG
+  return 1;
+#else
+  return 0;
+#endif
 }
 
 }  // extern "C"

@@ -70,8 +70,23 @@ __global__ __launch_bounds__(256) void cache_append_kernel(AppendParams p) {
   const int ddt = key ? p.k_dst_dtype : p.kv_dst_dtype;
   if (dst == nullptr) return;
   const int b = (int)(row / p.Q), i = (int)(row - (int64_t)b * p.Q);
-  const int pos = p.seq_lens[b] - p.Q + i;
-  const int64_t slot = (int64_t)p.page_table[(int64_t)b * p.maxP + pos / p.P] * p.P + pos % p.P;
+  const int Lb = p.seq_lens[b];
+#ifdef DSA_DEBUG
+  // a length or page id out of range (flagged) writes nothing for this token
+  if (Lb < p.Q || Lb > p.max_seq_len) {
+    if (lane == 0) dbg_flag(p.dbg, kDbgSeqLen);
+    return;
+  }
+#endif
+  const int pos = Lb - p.Q + i;
+  const int pe = p.page_table[(int64_t)b * p.maxP + pos / p.P];
+#ifdef DSA_DEBUG
+  if (pe < 0 || (int64_t)pe >= p.num_slots / p.P) {
+    if (lane == 0) dbg_flag(p.dbg, kDbgPageId);
+    return;
+  }
+#endif
+  const int64_t slot = (int64_t)pe * p.P + pos % p.P;
   const int nchunk = width >> 3;
   float v[2][8];
   float amax = 0.0f;

@@ -123,6 +123,75 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // ---------------------------------------------------------------------------------------------
+// Opt-in device-side checks of the data preconditions (builds with DSA_DEBUG defined, the
+// library libdsa_debug.so).  A kernel that meets a violation sets its bit in the error word the
+// launch passes (dbg) and clamps the offending value into range, so that no access leaves its
+// buffer; the host reads and clears the word with dsa_debug_check.  Without DSA_DEBUG these
+// compile to nothing and dbg is unused.
+enum : uint32_t {
+  kDbgSeqLen = 1u,      // seq_lens[b] outside [q_per_seq, max_seq_len]
+  kDbgPageId = 2u,      // a page-table entry outside [0, num_slots / page_size)
+  kDbgSlot = 4u,        // a slot of dsa_sparse_mla_decode outside [-1, num_slots)
+  kDbgNanScore = 8u,    // a NaN among the scores a top-k ranks
+  kDbgTopkIndex = 16u,  // an index of dsa_page_map outside [-1, seq_lens[b])
+};
+
+__device__ __forceinline__ void dbg_flag(uint32_t* dbg, uint32_t bit) {
+#ifdef DSA_DEBUG
+  __hip_atomic_fetch_or(dbg, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#else
+  (void)dbg;
+  (void)bit;
+#endif
+}
+// v if it lies in [lo, hi]; otherwise (DSA_DEBUG builds) flags `bit` and returns v clamped
+__device__ __forceinline__ int dbg_clamp(uint32_t* dbg, int v, int lo, int hi, uint32_t bit) {
+#ifdef DSA_DEBUG
+  if (v < lo || v > hi) {
+    dbg_flag(dbg, bit);
+    return v < lo ? lo : hi;
+  }
+#else
+  (void)dbg;
+  (void)lo;
+  (void)hi;
+  (void)bit;
+#endif
+  return v;
+}
+// a page-table entry, checked against the pool's page count
+__device__ __forceinline__ int dbg_page(uint32_t* dbg, int pe, int64_t num_slots, int P) {
+  return dbg_clamp(dbg, pe, 0, (int)(num_slots / P) - 1, kDbgPageId);
+}
+// a slot of the sparse MLA's selection: one outside [-1, num_slots) is flagged (when `flag`) and
+// skipped like -1
+__device__ __forceinline__ int32_t dbg_slot(uint32_t* dbg, int32_t sv, int64_t num_slots, bool flag = true) {
+#ifdef DSA_DEBUG
+  if (sv < -1 || sv >= num_slots) {
+    if (flag) dbg_flag(dbg, kDbgSlot);
+    return -1;
+  }
+#else
+  (void)dbg;
+  (void)num_slots;
+  (void)flag;
+#endif
+  return sv;
+}
+// a sequence length, checked against [Q, max_seq_len] (flag only: every kernel already keeps its
+// accesses inside the rows that max_seq_len sizes)
+__device__ __forceinline__ void dbg_seq_len(uint32_t* dbg, int L, int Q, int max_seq_len) {
+#ifdef DSA_DEBUG
+  if (L < Q || L > max_seq_len) dbg_flag(dbg, kDbgSeqLen);
+#else
+  (void)dbg;
+  (void)L;
+  (void)Q;
+  (void)max_seq_len;
+#endif
+}
+
+// ---------------------------------------------------------------------------------------------
 // launch parameter blocks (plain structs passed by value to the kernels)
 
 struct IndexerParams {
@@ -144,6 +213,7 @@ struct IndexerParams {
   // 0 = ranges of tiles_per_wg tiles over max_seq_len for every sequence; else the number of
   // ranges to aim for (each workgroup derives the partition from seq_lens, see the kernel)
   int32_t balanced;
+  uint32_t* dbg;          // DSA_DEBUG error word
 };
 
 struct TopkParams {
@@ -161,6 +231,9 @@ struct TopkParams {
   float* cand_score;      // [rows, cand_ld]
   int32_t* cand_col;      // [rows, cand_ld]
   int64_t cand_ld;
+  int64_t num_slots;      // cache rows (DSA_DEBUG page-id checks)
+  int32_t max_seq_len;
+  uint32_t* dbg;          // DSA_DEBUG error word
 };
 
 struct MlaParams {
@@ -176,6 +249,7 @@ struct MlaParams {
   float* part_l;     // [rows, n_split, H]
   int32_t rows, H, k, n_split, chunk;
   float sm_scale;
+  uint32_t* dbg;     // DSA_DEBUG error word
 };
 
 struct CombineParams {
@@ -202,6 +276,9 @@ struct AppendParams {
   int32_t Q, P, maxP;
   int32_t kv_width, k_width;
   int32_t kv_src_dtype, kv_dst_dtype, k_src_dtype, k_dst_dtype;
+  int64_t num_slots;      // cache rows (DSA_DEBUG page-id checks)
+  int32_t max_seq_len;
+  uint32_t* dbg;          // DSA_DEBUG error word
 };
 
 // Latent up-projection after attention: o [R, H, 512] f32 -> v [R, H, Dv] f32 (workspace) ->
@@ -227,7 +304,8 @@ bool indexer_uses_mfma(int Hi, int Di, dsa_dtype_t q_dtype, dsa_dtype_t k_dtype)
 size_t topk_workspace_bytes(int64_t rows, int max_seq_len, int k);
 hipError_t launch_topk(const TopkParams& p, int rows, int max_seq_len, void* ws, hipStream_t s);
 hipError_t launch_page_map(const int32_t* idx, int64_t total, int k, int Q, const int32_t* pt,
-                           int maxP, int P, int32_t* slots, hipStream_t s);
+                           int maxP, int P, int32_t* slots, const int32_t* seq_lens, int64_t num_slots,
+                           uint32_t* dbg, hipStream_t s);
 hipError_t launch_mla(const MlaParams& p, dsa_dtype_t q_dtype, dsa_dtype_t kv_dtype, hipStream_t s);
 hipError_t launch_combine(const CombineParams& p, hipStream_t s);
 int mla_default_split(int rows, int H, int k, dsa_dtype_t kv_dtype);

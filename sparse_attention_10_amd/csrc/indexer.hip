@@ -45,7 +45,9 @@ template <typename QT, typename KT>
 __global__ __launch_bounds__(256) void indexer_valu_kernel(IndexerParams p) {
   extern __shared__ float sm[];   // q [Hi*Di] as f32, then w [Hi]
   const int b = blockIdx.z, i = blockIdx.y;
-  const int L = min(p.seq_lens[b], p.max_seq_len);   // never write past the scores row
+  const int Lb = p.seq_lens[b];
+  if (threadIdx.x == 0 && blockIdx.x == 0 && i == 0) dbg_seq_len(p.dbg, Lb, p.Q, p.max_seq_len);
+  const int L = min(Lb, p.max_seq_len);              // never write past the scores row
   const int pos = L - p.Q + i;
   const int t0 = blockIdx.x * 256;
   if (t0 >= L) return;   // whole block past the sequence (uniform)
@@ -61,7 +63,8 @@ __global__ __launch_bounds__(256) void indexer_valu_kernel(IndexerParams p) {
     out[t] = -INFINITY;
     return;
   }
-  const int64_t slot = (int64_t)p.page_table[(int64_t)b * p.maxP + t / p.P] * p.P + t % p.P;
+  const int pe = dbg_page(p.dbg, p.page_table[(int64_t)b * p.maxP + t / p.P], p.num_slots, p.P);
+  const int64_t slot = (int64_t)pe * p.P + t % p.P;
   const int64_t kbase = slot * p.Di;
   float acc = 0.f;
   for (int h = 0; h < p.Hi; ++h) {
@@ -134,7 +137,9 @@ __global__ __launch_bounds__(kPfThreads) void indexer_prefill_kernel(IndexerPara
   const int qb = (int)blockIdx.x % nqb;
   const int rest = (int)blockIdx.x / nqb;
   const int kr = rest % p.groups, b = rest / p.groups;
-  const int L = min(p.seq_lens[b], p.max_seq_len);
+  const int Lb = p.seq_lens[b];
+  if (threadIdx.x == 0 && kr == 0 && qb == 0) dbg_seq_len(p.dbg, Lb, p.Q, p.max_seq_len);
+  const int L = min(Lb, p.max_seq_len);
   const int q0 = qb * kPfQB;
   const int nq = min(kPfQB, p.Q - q0);             // rows of this block
   const int t_begin = kr * p.tiles_per_wg * kPfST;
@@ -189,7 +194,7 @@ __global__ __launch_bounds__(kPfThreads) void indexer_prefill_kernel(IndexerPara
     }
     lk_t0 += kPfST;
   };
-  auto pt_global = [&](int pg) { return ptab_g[pg]; };
+  auto pt_global = [&](int pg) { return dbg_page(p.dbg, ptab_g[pg], p.num_slots, P); };
 #pragma unroll
   for (int v = 0; v < kPfNB - kPfSPB; ++v)
     if (v < nstage) issue(sm.ring[v], pt_global);
@@ -211,7 +216,7 @@ __global__ __launch_bounds__(kPfThreads) void indexer_prefill_kernel(IndexerPara
     const int row = min(q0 + e / kHi, p.Q - 1);
     (&sm.w[0][0])[e] = p.w[((int64_t)b * p.Q + row) * kHi + e % kHi];
   }
-  for (int e = threadIdx.x; e < npg; e += kPfThreads) sm.pt[e] = ptab_g[page0 + e];
+  for (int e = threadIdx.x; e < npg; e += kPfThreads) sm.pt[e] = dbg_page(p.dbg, ptab_g[page0 + e], p.num_slots, P);
   __syncthreads();
 
   float* out_b = p.scores + ((int64_t)b * p.Q + q0) * p.ld;
@@ -400,7 +405,9 @@ __global__ __launch_bounds__(NW * 64) void indexer_reg_kernel(IndexerParams p) {
     blk0 = (kr - sm.part[17]) * T;
     nblk = T;
   }
-  const int L = min(p.seq_lens[b], p.max_seq_len);
+  const int Lb = p.seq_lens[b];
+  if (threadIdx.x == 0 && blk0 == 0 && q0 == 0) dbg_seq_len(p.dbg, Lb, p.Q, p.max_seq_len);
+  const int L = min(Lb, p.max_seq_len);
   const int t_begin = blk0 * kRB;
   if (t_begin >= L) return;                       // uniform early exit
   const int t_end = min(L, (blk0 + nblk) * kRB);
@@ -464,7 +471,7 @@ __global__ __launch_bounds__(NW * 64) void indexer_reg_kernel(IndexerParams p) {
     for (int c = 0; c < NPE; ++c) {
       const int t = blk_tok(u) + (c < NLD ? TPL * c + lane / PPR : n);
       int pg = p.p_shift >= 0 ? (t >> p.p_shift) : t / P;
-      pe[u][c] = t < t_stop ? ptab_g[pg] : 0;
+      pe[u][c] = t < t_stop ? dbg_page(p.dbg, ptab_g[pg], p.num_slots, P) : 0;
     }
   constexpr int kQPer = (QB * kHi * kDi / 8 + NT - 1) / NT;
   u32x4 qv[kQPer];
@@ -509,7 +516,7 @@ __global__ __launch_bounds__(NW * 64) void indexer_reg_kernel(IndexerParams p) {
   if (threadIdx.x < QB * kHi) (&sm.w[0][0])[threadIdx.x] = wv0;
 #pragma unroll
   for (int c = 0; c < kPtPer; ++c)
-    if (c * NT + (int)threadIdx.x < npg) sm.pt[c * NT + threadIdx.x] = pv[c];
+    if (c * NT + (int)threadIdx.x < npg) sm.pt[c * NT + threadIdx.x] = dbg_page(p.dbg, pv[c], p.num_slots, P);
   __syncthreads();
 
   // A fragments: M-block mb = (row mb/4, heads 16(mb%4) .. +16), lane: head n, dims 32g + 8s

@@ -88,7 +88,7 @@ __global__ __launch_bounds__(256) void mla_valu_kernel(MlaParams p) {
   const int32_t* sl = p.slots + (int64_t)r * p.k;
   float m = -INFINITY;
   for (int j = threadIdx.x; j < p.k; j += 256) {
-    const int64_t s = sl[j];
+    const int64_t s = dbg_slot(p.dbg, sl[j], p.num_slots);
     float z = -INFINITY;
     if (s >= 0) {
       float dot = 0.f;
@@ -117,7 +117,7 @@ __global__ __launch_bounds__(256) void mla_valu_kernel(MlaParams p) {
   for (int d = threadIdx.x; d < kVDim; d += 256) {
     float acc = 0.f;
     for (int j = 0; j < p.k; ++j) {
-      const int64_t s = sl[j];
+      const int64_t s = dbg_slot(p.dbg, sl[j], p.num_slots, false);
       if (s < 0) continue;
       float v = RowElt<KT>::get(p.kv, s * kRowDim + d);
       if (p.kv_scale) v *= p.kv_scale[s];
@@ -251,7 +251,7 @@ __global__ __launch_bounds__(kNT) void mla_mfma_kernel(MlaParams p) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int e = e0 + u * kNT + threadIdx.x;
-        if (e < span) sl_lds[e] = j0 + e < j1 ? v[u] : -1;
+        if (e < span) sl_lds[e] = j0 + e < j1 ? dbg_slot(p.dbg, v[u], p.num_slots) : -1;
       }
     }
   }
@@ -460,7 +460,7 @@ __global__ __launch_bounds__(kNT) void mla_fp8_kernel(MlaParams p) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int e = e0 + u * kNT + threadIdx.x;
-        if (e < span) sl_lds[e] = j0 + e < j1 ? v[u] : -1;
+        if (e < span) sl_lds[e] = j0 + e < j1 ? dbg_slot(p.dbg, v[u], p.num_slots) : -1;
       }
     }
   }
@@ -722,7 +722,7 @@ __global__ __launch_bounds__(kNTF) void mla_fp8d_kernel(MlaParams p) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int e = e0 + u * kNTF + threadIdx.x;
-        if (e < span) sm.sl[e] = j0 + e < j1 ? v[u] : -1;
+        if (e < span) sm.sl[e] = j0 + e < j1 ? dbg_slot(p.dbg, v[u], p.num_slots) : -1;
       }
     }
   }
@@ -1061,7 +1061,7 @@ __global__ __launch_bounds__(kNT) void mla_bf16d_kernel(MlaParams p) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int e = e0 + u * kNT + threadIdx.x;
-        if (e < span) sm.sl[e] = j0 + e < j1 ? v[u] : -1;
+        if (e < span) sm.sl[e] = j0 + e < j1 ? dbg_slot(p.dbg, v[u], p.num_slots) : -1;
       }
     }
   }

@@ -227,7 +227,12 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkParams p) {
   const int row = MODE == 1 ? (int)blockIdx.x / p.nchunks : (int)blockIdx.x;
   const int chunk = MODE == 1 ? (int)blockIdx.x - row * p.nchunks : 0;
   const int b = row / p.Q, i = row - b * p.Q;
-  int n_row = p.seq_lens[b] - p.Q + i + 1;         // visible tokens of this row
+  const int Lb = p.seq_lens[b];
+  if (tid == 0 && i == 0 && chunk == 0) dbg_seq_len(p.dbg, Lb, p.Q, p.max_seq_len);
+  int n_row = Lb - p.Q + i + 1;                    // visible tokens of this row
+#ifdef DSA_DEBUG
+  n_row = min(n_row, p.max_seq_len - p.Q + i + 1); // (a length past max_seq_len, flagged, is cut there)
+#endif
   n_row = n_row < 0 ? 0 : n_row;
   n_row = (int64_t)n_row > p.ld ? (int)p.ld : n_row;   // guards against lengths past the scores row
   n_row = n_row > kMaxTopkSeq ? kMaxTopkSeq : n_row;
@@ -248,6 +253,13 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkParams p) {
     srow = p.cand_score + (int64_t)row * p.cand_ld;
   }
   const int32_t* ccol = MODE == 2 ? p.cand_col + (int64_t)row * p.cand_ld : nullptr;
+#ifdef DSA_DEBUG
+  if constexpr (MODE != 2) {   // (the candidates of the second pass come from checked chunks)
+    bool nan_seen = false;
+    for (int j = tid; j < n; j += kThreads) nan_seen |= srow[j] != srow[j];
+    if (nan_seen) dbg_flag(p.dbg, kDbgNanScore);
+  }
+#endif
   // MODE 1 writes its winners after those of the chunks before it (each keeps kc)
   float* cs_out = MODE == 1 ? p.cand_score + (int64_t)row * p.cand_ld + (int64_t)chunk * kc : nullptr;
   int32_t* cc_out = MODE == 1 ? p.cand_col + (int64_t)row * p.cand_ld + (int64_t)chunk * kc : nullptr;
@@ -281,7 +293,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkParams p) {
       for (int j = tid; j < k; j += kThreads) {
         const int t = j < n ? (MODE == 2 ? ccol[j] : j) : -1;
         idx_out[j] = t;
-        if (slot_out) slot_out[j] = t >= 0 ? ptab[t / p.P] * p.P + t % p.P : -1;
+        if (slot_out) slot_out[j] = t >= 0 ? dbg_page(p.dbg, ptab[t / p.P], p.num_slots, p.P) * p.P + t % p.P : -1;
       }
       return;
     }
@@ -317,7 +329,8 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkParams p) {
   int32_t pv[kPtabCache / kThreads];
   if (cache_pages) {
 #pragma unroll
-    for (int u = 0; u < kPtabCache / kThreads; ++u) pv[u] = ptab[min(u * kThreads + tid, npages - 1)];
+    for (int u = 0; u < kPtabCache / kThreads; ++u)
+      pv[u] = dbg_page(p.dbg, ptab[min(u * kThreads + tid, npages - 1)], p.num_slots, p.P);
   }
 
   // The streamed key rows (from kRegRows on), in segments of kTailRows rows per wave.
@@ -813,20 +826,29 @@ threshold_done:
     if (slot_out) {
       int pg = p_pow2 ? t >> p_shift : t / P;
       pg = min(max(pg, 0), npages - 1);            // (t is always in [0, n_row); the clamp only guards the lookup)
-      const int pe = cache_pages ? big[kOffPtab + pg] : ptab[pg];
+      const int pe = cache_pages ? big[kOffPtab + pg] : dbg_page(p.dbg, ptab[pg], p.num_slots, P);
       slot_out[j] = pe * P + (t - pg * P);
     }
   }
 }
 
 __global__ __launch_bounds__(256) void page_map_kernel(const int32_t* idx, int64_t total, int k, int Q,
-                                                       const int32_t* pt, int maxP, int P, int32_t* slots) {
+                                                       const int32_t* pt, int maxP, int P, int32_t* slots,
+                                                       const int32_t* seq_lens, int64_t num_slots, uint32_t* dbg) {
   const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (g >= total) return;
   const int64_t row = g / k;
   const int b = (int)(row / Q);
-  const int t = idx[g];
-  slots[g] = t < 0 ? -1 : pt[(int64_t)b * maxP + t / P] * P + t % P;
+  int t = idx[g];
+#ifdef DSA_DEBUG
+  if (t < -1 || t >= min(seq_lens[b], maxP * P)) {   // (flagged; mapped to -1)
+    dbg_flag(dbg, kDbgTopkIndex);
+    t = -1;
+  }
+#else
+  (void)seq_lens;
+#endif
+  slots[g] = t < 0 ? -1 : dbg_page(dbg, pt[(int64_t)b * maxP + t / P], num_slots, P) * P + t % P;
 }
 
 }  // namespace
@@ -895,10 +917,12 @@ hipError_t launch_topk(const TopkParams& p0, int rows, int max_seq_len, void* ws
 }
 
 hipError_t launch_page_map(const int32_t* idx, int64_t total, int k, int Q, const int32_t* pt, int maxP,
-                           int P, int32_t* slots, hipStream_t s) {
+                           int P, int32_t* slots, const int32_t* seq_lens, int64_t num_slots, uint32_t* dbg,
+                           hipStream_t s) {
   if (total == 0) return hipSuccess;
   const unsigned blocks = (unsigned)((total + 255) / 256);
-  hipLaunchKernelGGL(page_map_kernel, dim3(blocks), dim3(256), 0, s, idx, total, k, Q, pt, maxP, P, slots);
+  hipLaunchKernelGGL(page_map_kernel, dim3(blocks), dim3(256), 0, s, idx, total, k, Q, pt, maxP, P, slots,
+                     seq_lens, num_slots, dbg);
   return hipGetLastError();
 }
 

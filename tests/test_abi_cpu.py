@@ -41,6 +41,21 @@ def test_library_exports_every_declared_symbol(L):
     assert L.dsa_status_string(3) == b"DSA_ERR_WORKSPACE_TOO_SMALL"
 
 
+def test_debug_build_exports_every_symbol_and_release_reports_unsupported(L):
+    if not os.path.exists(dsa.DEBUG_LIB_PATH):
+        from sparse_attention_10_amd import build
+        build.build(debug=True)
+    D = dsa.load_library(dsa.DEBUG_LIB_PATH)
+    for n in _declared():
+        assert hasattr(D, n), n
+    assert D.dsa_debug_enabled() == 1 and L.dsa_debug_enabled() == 0
+    # the release build has no error word: dsa_debug_check says so without touching a device
+    flags = ctypes.c_uint32(7)
+    assert L.dsa_debug_check(ctypes.byref(flags), None) == dsa.DSA_ERR_UNSUPPORTED
+    assert flags.value == 0
+    assert b"DSA_DEBUG" in L.dsa_last_error()
+
+
 def _batch(**kw):
     b = dict(batch=1, q_per_seq=1, max_seq_len=4096, page_size=64, max_pages_per_seq=64, num_slots=4096,
              seq_lens=256, page_table=512)

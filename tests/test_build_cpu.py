@@ -10,13 +10,16 @@ from sparse_attention_10_amd import build
 CSRC = os.path.join(os.path.dirname(build.__file__), "csrc")
 
 
+@pytest.mark.parametrize("debug", [False, True], ids=["release", "debug"])
 @pytest.mark.parametrize("src", build.SOURCES)
-def test_no_kernel_needs_scratch(src, tmp_path):
-    """Every kernel fits its registers: no private (scratch) segment, no dynamic stack."""
+def test_no_kernel_needs_scratch(src, debug, tmp_path):
+    """Every kernel fits its registers: no private (scratch) segment, no dynamic stack; the same
+    for the DSA_DEBUG build, whose checks add only compares and atomic flag writes."""
     if src == "api.hip":
         pytest.skip("host-side validation only")
     out = tmp_path / "k.s"
-    cmd = [build.hipcc()] + build.flags() + ["--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", str(out)]
+    cmd = ([build.hipcc()] + build.flags() + (["-DDSA_DEBUG"] if debug else []) +
+           ["--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", str(out)])
     subprocess.run(cmd, check=True, capture_output=True)
     text = out.read_text()
     kernels = re.findall(r"\.amdhsa_kernel (\S+)", text)
