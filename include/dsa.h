@@ -170,7 +170,10 @@ dsa_status_t dsa_mla_combine(int32_t rows, int32_t n_heads, int32_t n_split,
 
 /*
  * The whole decode step on one stream: indexer -> top-k with the fused page map -> sparse MLA
- * (-> split-k merge), with no host synchronisation.
+ * (-> split-k merge), with no host synchronisation.  With many query rows per sequence (a
+ * chunked-prefill step: bf16 keys, q_per_seq >= 16) the rows are scored and ranked in blocks
+ * that reuse one score buffer small enough to stay in the 256 MB Infinity Cache, instead of
+ * writing the whole [B,Q,max_seq_len] score array at once.
  * Optional debug outputs: when debug_scores / debug_idx / debug_slots are not NULL, the step
  * keeps its intermediate [B,Q,max_seq_len] scores (ld = max_seq_len), [B,Q,top_k] indices and
  * slots there instead of in the workspace, so a caller can inspect exactly what was used.
@@ -198,6 +201,10 @@ typedef struct {
   float *debug_scores;                              /* [B,Q,max_seq_len] */
   int32_t *debug_idx;                               /* [B,Q,top_k] */
   int32_t *debug_slots;                             /* [B,Q,top_k] */
+  /* chunked prefill: rows per sequence whose scores are formed and ranked together (rounded
+   * down to a multiple of 16, at least 16; 0 = automatic, about 72 MiB of scores per block;
+   * ignored with debug_scores or when the many-rows indexer does not apply) */
+  int32_t prefill_rows_per_block;
 } dsa_decode_step_args_t;
 
 dsa_status_t dsa_decode_step(const dsa_decode_step_args_t *args,

@@ -61,7 +61,7 @@ class DsaDecodeStepArgs(ctypes.Structure):
                 ("mla_heads", ctypes.c_int32), ("sm_scale", ctypes.c_float), ("n_split", ctypes.c_int32),
                 ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p),
                 ("debug_scores", ctypes.c_void_p), ("debug_idx", ctypes.c_void_p),
-                ("debug_slots", ctypes.c_void_p)]
+                ("debug_slots", ctypes.c_void_p), ("prefill_rows_per_block", ctypes.c_int32)]
 
 
 _lib = None
@@ -246,7 +246,7 @@ def dsa_mla_combine(part_o: torch.Tensor, part_m: torch.Tensor, part_l: torch.Te
 
 def decode_step_args(batch: DsaBatch, q_idx, w, k_cache, k_scale, top_k: int, q_mla, kv_cache, kv_scale,
                      sm_scale: float, out, lse=None, n_split: int = 0, debug_scores=None, debug_idx=None,
-                     debug_slots=None) -> DsaDecodeStepArgs:
+                     debug_slots=None, prefill_rows_per_block: int = 0) -> DsaDecodeStepArgs:
     a = DsaDecodeStepArgs()
     a.batch = batch
     a.q_idx, a.q_idx_dtype, a.w = _ptr(q_idx), dtype_code(q_idx), _ptr(w)
@@ -258,6 +258,7 @@ def decode_step_args(batch: DsaBatch, q_idx, w, k_cache, k_scale, top_k: int, q_
     a.mla_heads, a.sm_scale, a.n_split = q_mla.shape[2], float(sm_scale), n_split
     a.out, a.lse = _ptr(out), _ptr(lse)
     a.debug_scores, a.debug_idx, a.debug_slots = _ptr(debug_scores), _ptr(debug_idx), _ptr(debug_slots)
+    a.prefill_rows_per_block = prefill_rows_per_block
     a._keep = (batch, q_idx, w, k_cache, k_scale, q_mla, kv_cache, kv_scale, out, lse, debug_scores, debug_idx,
                debug_slots)
     return a

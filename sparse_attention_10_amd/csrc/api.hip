@@ -316,7 +316,7 @@ dsa_status_t dsa_topk(const dsa_batch_t* b, const float* scores, int64_t scores_
   DSA_TRY(debug_word(&dbg));
   TopkParams p{scores, scores_ld, b->seq_lens, b->page_table, topk_idx, topk_slots,
                b->q_per_seq, k, b->page_size, b->max_pages_per_seq, 0, 0, nullptr, nullptr, 0,
-               b->num_slots, b->max_seq_len, dbg};
+               b->num_slots, b->max_seq_len, 0, 0, dbg};
   return launched(launch_topk(p, b->batch * b->q_per_seq, b->max_seq_len, workspace, (hipStream_t)stream),
                   "top-k");
 }
@@ -386,18 +386,40 @@ struct StepWs {
   int64_t ld;
   size_t topk_off, scores_off, idx_off, slots_off, mla_off, total;
   int32_t ns;
+  int32_t q_block;   // query rows per sequence scored and ranked together (q_per_seq: one block)
 };
+
+constexpr size_t kPrefillBlockBytes = (size_t)72 << 20;   // scores per block (stays in the 256 MB cache)
 
 StepWs step_ws(const dsa_decode_step_args_t* a) {
   StepWs w{};
   const dsa_batch_t& b = a->batch;
   const int64_t rows = (int64_t)b.batch * b.q_per_seq;
   w.ld = b.max_seq_len;
+  // chunked prefill: blocks of rows whose scores fit kPrefillBlockBytes (or the caller's size)
+  w.q_block = b.q_per_seq;
+  if (!a->debug_scores && indexer_uses_prefill(a->idx_heads, a->idx_dim, b.q_per_seq, b.page_size, a->q_idx_dtype,
+                                               a->k_dtype)) {
+    int64_t qb = a->prefill_rows_per_block;
+    if (qb <= 0) qb = (int64_t)(kPrefillBlockBytes / ((size_t)b.batch * w.ld * sizeof(float)));
+    if (qb < b.q_per_seq) {
+      qb = qb / 16 * 16;
+      if (qb < 16) qb = 16;
+      if (qb < b.q_per_seq) w.q_block = (int32_t)qb;
+    }
+  }
+  const int64_t block_rows = (int64_t)b.batch * w.q_block;
+  const int32_t last_q = b.q_per_seq % w.q_block;
   size_t off = 0;
-  w.topk_off = off;   // top-k candidates of long rows
-  off += align_up(topk_workspace_bytes(rows, b.max_seq_len, a->top_k), 256);
+  w.topk_off = off;   // top-k candidates of long rows (for the largest need of a block)
+  size_t topk_bytes = topk_workspace_bytes(block_rows, b.max_seq_len, a->top_k);
+  if (last_q) {
+    const size_t last_bytes = topk_workspace_bytes((int64_t)b.batch * last_q, b.max_seq_len, a->top_k);
+    if (last_bytes > topk_bytes) topk_bytes = last_bytes;
+  }
+  off += align_up(topk_bytes, 256);
   w.scores_off = off;
-  if (!a->debug_scores) off += align_up((size_t)rows * w.ld * sizeof(float), 256);
+  if (!a->debug_scores) off += align_up((size_t)block_rows * w.ld * sizeof(float), 256);
   w.idx_off = off;
   if (!a->debug_idx) off += align_up((size_t)rows * a->top_k * sizeof(int32_t), 256);
   w.slots_off = off;
@@ -432,6 +454,8 @@ dsa_status_t check_step(const dsa_decode_step_args_t* a) {
   DSA_TRY(check_mla(b->batch, b->q_per_seq, a->q_mla, a->q_mla_dtype, a->kv_cache, a->kv_dtype, a->kv_scale,
                     b->num_slots, (const int32_t*)16, a->top_k, a->mla_heads, a->sm_scale, a->out, a->lse,
                     a->n_split));
+  DSA_REQUIRE(a->prefill_rows_per_block >= 0, "decode_step: prefill_rows_per_block must be >= 0 (got %d)",
+              a->prefill_rows_per_block);
   DSA_REQUIRE((!a->debug_idx || aligned(a->debug_idx, 4)) && (!a->debug_slots || aligned(a->debug_slots, 4)),
               "decode_step: debug arrays must be 4-byte aligned");
   return DSA_OK;
@@ -466,12 +490,17 @@ dsa_status_t launch_step(const dsa_decode_step_args_t* a, const StepWs& w, void*
   ip.maxP = b->max_pages_per_seq;
   ip.Hi = a->idx_heads;
   ip.Di = a->idx_dim;
-  DSA_TRY(launched(launch_indexer(ip, a->q_idx_dtype, a->k_dtype, s), "indexer"));
-
   TopkParams tp{scores, w.ld, b->seq_lens, b->page_table, idx, slots,
                 b->q_per_seq, a->top_k, b->page_size, b->max_pages_per_seq, 0, 0, nullptr, nullptr, 0,
-                b->num_slots, b->max_seq_len, dbg};
-  DSA_TRY(launched(launch_topk(tp, b->batch * b->q_per_seq, b->max_seq_len, ws + w.topk_off, s), "top-k"));
+                b->num_slots, b->max_seq_len, 0, 0, dbg};
+  // rows in blocks of q_block per sequence, each block's scores in the same buffer
+  for (int32_t q0 = 0; q0 < b->q_per_seq; q0 += w.q_block) {
+    const int32_t qn = b->q_per_seq - q0 < w.q_block ? b->q_per_seq - q0 : w.q_block;
+    ip.q_begin = tp.q_begin = q0;
+    ip.q_count = tp.q_count = qn;
+    DSA_TRY(launched(launch_indexer(ip, a->q_idx_dtype, a->k_dtype, s), "indexer"));
+    DSA_TRY(launched(launch_topk(tp, b->batch * qn, b->max_seq_len, ws + w.topk_off, s), "top-k"));
+  }
 
   const int64_t rows = (int64_t)b->batch * b->q_per_seq;
   const size_t mla_bytes = workspace_bytes - w.mla_off;

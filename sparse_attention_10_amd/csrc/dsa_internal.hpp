@@ -213,6 +213,10 @@ struct IndexerParams {
   // 0 = ranges of tiles_per_wg tiles over max_seq_len for every sequence; else the number of
   // ranges to aim for (each workgroup derives the partition from seq_lens, see the kernel)
   int32_t balanced;
+  // rows i in [q_begin, q_begin + q_count) of every sequence (chunked prefill in row blocks;
+  // the many-rows kernel only): scores row (b, i) at scores + (b*q_count + i - q_begin)*ld.
+  // q_count = 0: all Q rows
+  int32_t q_begin, q_count;
   uint32_t* dbg;          // DSA_DEBUG error word
 };
 
@@ -233,6 +237,10 @@ struct TopkParams {
   int64_t cand_ld;
   int64_t num_slots;      // cache rows (DSA_DEBUG page-id checks)
   int32_t max_seq_len;
+  // rows i in [q_begin, q_begin + q_count) of every sequence: scores (and candidates) of row
+  // (b, i) at local row b*q_count + i - q_begin, idx and slots at row b*Q + i.  q_count = 0:
+  // all Q rows
+  int32_t q_begin, q_count;
   uint32_t* dbg;          // DSA_DEBUG error word
 };
 
@@ -298,6 +306,8 @@ struct UpProjParams {
 hipError_t launch_indexer(const IndexerParams& p, dsa_dtype_t q_dtype, dsa_dtype_t k_dtype,
                           hipStream_t s);
 bool indexer_uses_mfma(int Hi, int Di, dsa_dtype_t q_dtype, dsa_dtype_t k_dtype);
+// the many-rows (chunked prefill) kernel, the one that takes row windows (q_begin, q_count)
+bool indexer_uses_prefill(int Hi, int Di, int Q, int P, dsa_dtype_t q_dtype, dsa_dtype_t k_dtype);
 // Top-k: `ws` is topk_workspace_bytes(rows, max_seq_len, k) bytes of device memory (the
 // candidates of the two-pass plan for long rows; no initial contents), or unused when that
 // size is 0.

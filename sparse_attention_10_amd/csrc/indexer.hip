@@ -132,16 +132,18 @@ __global__ __launch_bounds__(kPfThreads) void indexer_prefill_kernel(IndexerPara
   __shared__ __attribute__((aligned(16))) PfSmem sm;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // id = (b * ranges + range) * query blocks + query block
-  const int nqb = (p.Q + kPfQB - 1) / kPfQB;
+  // id = (b * ranges + range) * query blocks + query block; the blocks cover the rows
+  // q_begin .. q_begin + q_count - 1 of each sequence
+  const int nqb = (p.q_count + kPfQB - 1) / kPfQB;
   const int qb = (int)blockIdx.x % nqb;
   const int rest = (int)blockIdx.x / nqb;
   const int kr = rest % p.groups, b = rest / p.groups;
   const int Lb = p.seq_lens[b];
   if (threadIdx.x == 0 && kr == 0 && qb == 0) dbg_seq_len(p.dbg, Lb, p.Q, p.max_seq_len);
   const int L = min(Lb, p.max_seq_len);
-  const int q0 = qb * kPfQB;
-  const int nq = min(kPfQB, p.Q - q0);             // rows of this block
+  const int q_end = p.q_begin + p.q_count;
+  const int q0 = p.q_begin + qb * kPfQB;
+  const int nq = min(kPfQB, q_end - q0);           // rows of this block
   const int t_begin = kr * p.tiles_per_wg * kPfST;
   const int t_end = min(L, t_begin + p.tiles_per_wg * kPfST);
   if (t_begin >= t_end) return;                    // uniform
@@ -204,7 +206,7 @@ __global__ __launch_bounds__(kPfThreads) void indexer_prefill_kernel(IndexerPara
   bf16x8 afrag[kPfQW][2][8];
 #pragma unroll
   for (int qi = 0; qi < kPfQW; ++qi) {
-    const int row = min(q0 + wave * kPfQW + qi, p.Q - 1);
+    const int row = min(q0 + wave * kPfQW + qi, q_end - 1);
     const __bf16* qrow = (const __bf16*)p.q + ((int64_t)b * p.Q + row) * kHi * kDi;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
@@ -213,13 +215,13 @@ __global__ __launch_bounds__(kPfThreads) void indexer_prefill_kernel(IndexerPara
         afrag[qi][mb][s] = *(const bf16x8*)(qrow + (mb * 32 + n_in_sub) * kDi + half * 64 + s * 8);
   }
   for (int e = threadIdx.x; e < kPfQB * kHi; e += kPfThreads) {
-    const int row = min(q0 + e / kHi, p.Q - 1);
+    const int row = min(q0 + e / kHi, q_end - 1);
     (&sm.w[0][0])[e] = p.w[((int64_t)b * p.Q + row) * kHi + e % kHi];
   }
   for (int e = threadIdx.x; e < npg; e += kPfThreads) sm.pt[e] = dbg_page(p.dbg, ptab_g[page0 + e], p.num_slots, P);
   __syncthreads();
 
-  float* out_b = p.scores + ((int64_t)b * p.Q + q0) * p.ld;
+  float* out_b = p.scores + ((int64_t)b * p.q_count + (q0 - p.q_begin)) * p.ld;
   // head reduction of row qi's 32 tokens (acc) at token t; weights from LDS
   auto finish = [&](const PfSmem* __restrict__ rd, const f32x16 (&acc)[2], int qi, int t) {
     const float* wrow = rd->w[wave * kPfQW + qi];
@@ -623,12 +625,20 @@ bool indexer_uses_mfma(int Hi, int Di, dsa_dtype_t q_dtype, dsa_dtype_t k_dtype)
   return Hi == kHi && Di == kDi && q_dtype == DSA_BF16 && (k_dtype == DSA_BF16 || k_dtype == DSA_FP8_E4M3FN);
 }
 
+bool indexer_uses_prefill(int Hi, int Di, int Q, int P, dsa_dtype_t q_dtype, dsa_dtype_t k_dtype) {
+  return indexer_uses_mfma(Hi, Di, q_dtype, k_dtype) && k_dtype == DSA_BF16 && Q >= kPfQB && P % kSub == 0;
+}
+
 hipError_t launch_indexer(const IndexerParams& p0, dsa_dtype_t q_dtype, dsa_dtype_t k_dtype, hipStream_t s) {
   IndexerParams p = p0;
-  if (indexer_uses_mfma(p.Hi, p.Di, q_dtype, k_dtype) && k_dtype == DSA_BF16 && p.Q >= kPfQB && p.P % kSub == 0) {
+  if (p.q_count == 0) {
+    p.q_begin = 0;
+    p.q_count = p.Q;
+  }
+  if (indexer_uses_prefill(p.Hi, p.Di, p.Q, p.P, q_dtype, k_dtype)) {
     // many rows per sequence: blocks of 16 rows, key ranges so that about 256 workgroups run
     // (and one range's page-table entries fit the LDS copy)
-    const int64_t nqb = (p.Q + kPfQB - 1) / kPfQB;
+    const int64_t nqb = (p.q_count + kPfQB - 1) / kPfQB;
     const int64_t stages = ((int64_t)p.max_seq_len + kPfST - 1) / kPfST;
     int64_t ranges = (256 + nqb * p.B - 1) / (nqb * p.B);
     const int64_t max_stages = (int64_t)(kPfMaxPages - 2) * p.P / kPfST;
@@ -640,6 +650,7 @@ hipError_t launch_indexer(const IndexerParams& p0, dsa_dtype_t q_dtype, dsa_dtyp
     hipLaunchKernelGGL(indexer_prefill_kernel, dim3((unsigned)(nqb * ranges * p.B)), dim3(kPfThreads), 0, s, p);
     return hipGetLastError();
   }
+  if (p.q_begin != 0 || p.q_count != p.Q) return hipErrorInvalidValue;   // row windows: many-rows kernel only
   if (indexer_uses_mfma(p.Hi, p.Di, q_dtype, k_dtype)) {
     // Keys straight into registers: QB rows per workgroup (one row group for Q <= 4), about one
     // round of 256 workgroups (one per compute unit) per row group.

@@ -226,9 +226,10 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform (kept in a scalar register)
   const int row = MODE == 1 ? (int)blockIdx.x / p.nchunks : (int)blockIdx.x;
   const int chunk = MODE == 1 ? (int)blockIdx.x - row * p.nchunks : 0;
-  const int b = row / p.Q, i = row - b * p.Q;
+  const int b = row / p.q_count, il = row - b * p.q_count;
+  const int i = p.q_begin + il;                     // the row's query index in its sequence
   const int Lb = p.seq_lens[b];
-  if (tid == 0 && i == 0 && chunk == 0) dbg_seq_len(p.dbg, Lb, p.Q, p.max_seq_len);
+  if (tid == 0 && il == 0 && chunk == 0) dbg_seq_len(p.dbg, Lb, p.Q, p.max_seq_len);
   int n_row = Lb - p.Q + i + 1;                    // visible tokens of this row
 #ifdef DSA_DEBUG
   n_row = min(n_row, p.max_seq_len - p.Q + i + 1); // (a length past max_seq_len, flagged, is cut there)
@@ -263,8 +264,9 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkParams p) {
   // MODE 1 writes its winners after those of the chunks before it (each keeps kc)
   float* cs_out = MODE == 1 ? p.cand_score + (int64_t)row * p.cand_ld + (int64_t)chunk * kc : nullptr;
   int32_t* cc_out = MODE == 1 ? p.cand_col + (int64_t)row * p.cand_ld + (int64_t)chunk * kc : nullptr;
-  int32_t* idx_out = MODE == 1 ? nullptr : p.idx + (int64_t)row * k;
-  int32_t* slot_out = MODE != 1 && p.slots ? p.slots + (int64_t)row * k : nullptr;
+  const int64_t out_row = (int64_t)b * p.Q + i;
+  int32_t* idx_out = MODE == 1 ? nullptr : p.idx + out_row * k;
+  int32_t* slot_out = MODE != 1 && p.slots ? p.slots + out_row * k : nullptr;
 
   // The register block is requested before the row's length arrives: the loads need only the
   // row's extent in memory, and columns past the row are masked when the keys are formed.
@@ -893,8 +895,13 @@ size_t topk_workspace_bytes(int64_t rows, int max_seq_len, int k) {
   return (size_t)(rows * ld) * (sizeof(float) + sizeof(int32_t)) + 256;
 }
 
-hipError_t launch_topk(const TopkParams& p0, int rows, int max_seq_len, void* ws, hipStream_t s) {
+hipError_t launch_topk(const TopkParams& p1, int rows, int max_seq_len, void* ws, hipStream_t s) {
   if (rows == 0) return hipSuccess;
+  TopkParams p0 = p1;
+  if (p0.q_count == 0) {
+    p0.q_begin = 0;
+    p0.q_count = p0.Q;
+  }
   const TopkPlan pl = topk_plan(rows, max_seq_len, p0.k);
   if (pl.L == 0) {
     TopkParams p = p0;

@@ -381,6 +381,37 @@ def test_decode_step_dense_when_k_covers_context(name, lens, Q):
     check_attention(r["out"].cpu().numpy(), do, r["lse"].cpu().numpy(), dl)
 
 
+@pytest.mark.parametrize("lens,Q,block", [([64 + 1000], 48, 16), ([40 + 700, 40 + 2100], 40, 16),
+                                           ([64 + 3000], 64, 32)])
+def test_prefill_row_blocks_match_one_block(lens, Q, block):
+    """Chunked prefill scored and ranked in row blocks that reuse one score buffer (ragged last
+    block, two sequences) gives exactly the step of one block: every score element is the same
+    matrix-core sum whatever the workgroup partition, so indices, slots and attention agree bit
+    for bit; one block is itself checked against the oracle by the staged step tests."""
+    cfg = dsa_inputs.scaled_config("c4", lens, seed=117, q_per_seq=Q, top_k=256)
+    inp = dsa_inputs.make_inputs(cfg)
+    t = dsa_inputs.to_torch(inp, cfg, DEV)
+
+    def step(rows_per_block):
+        B, H, k = cfg.batch, cfg.mla_heads, cfg.top_k
+        out = torch.full((B, Q, H, 512), float("nan"), dtype=torch.float32, device=DEV)
+        lse = torch.full((B, Q, H), float("nan"), dtype=torch.float32, device=DEV)
+        idx = torch.full((B, Q, k), -7, dtype=torch.int32, device=DEV)
+        slots = torch.full((B, Q, k), -7, dtype=torch.int32, device=DEV)
+        args = dsa.decode_step_args(batch_of(cfg, t), t["q_idx"], t["w"], t["k_cache"], t["k_scale"], k,
+                                    t["q_mla"], t["kv_cache"], t["kv_scale"], cfg.sm_scale, out, lse, 0,
+                                    None, idx, slots, prefill_rows_per_block=rows_per_block)
+        ws = torch.empty(max(1, dsa.decode_step_workspace_bytes(args)), dtype=torch.uint8, device=DEV)
+        dsa.dsa_decode_step(args, ws)
+        torch.cuda.synchronize()
+        return out, lse, idx, slots
+
+    whole = step(Q)
+    blocked = step(block)
+    for a, b in zip(blocked, whole):
+        assert torch.equal(a, b)
+
+
 def test_decode_step_deterministic():
     cfg, inp, t = _case("c3", [5000, 3000, 7000], seed=108)
     r1 = run_step(cfg, t)

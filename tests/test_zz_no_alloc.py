@@ -59,7 +59,9 @@ def test_noalloc_rejects_a_step_beyond_the_scratch_size():
     q_mla = torch.zeros((1, cfg.q_per_seq, 64, 576), dtype=torch.bfloat16, device=DEV)
     kv = torch.zeros((64, 576), dtype=torch.bfloat16, device=DEV)
     out = torch.zeros((1, cfg.q_per_seq, 64, 512), dtype=torch.float32, device=DEV)
-    args = dsa.decode_step_args(batch, q_idx, w, keys, None, 2048, q_mla, kv, None, cfg.sm_scale, out)
+    # (the whole chunk's scores in one block: 1.14 GB)
+    args = dsa.decode_step_args(batch, q_idx, w, keys, None, 2048, q_mla, kv, None, cfg.sm_scale, out,
+                                prefill_rows_per_block=4096)
     assert dsa.decode_step_workspace_bytes(args) > dsa.decode_step_noalloc_max_bytes()
     st = dsa.lib().dsa_decode_step_noalloc(ctypes.byref(args), None)
     assert st == dsa.DSA_ERR_WORKSPACE_TOO_SMALL
