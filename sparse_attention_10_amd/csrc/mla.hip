@@ -713,26 +713,18 @@ __global__ __launch_bounds__(kNTF) void mla_fp8d_kernel(MlaParams p) {
   const bool s_active = hg < ngroups;             // this wave's S^T head group exists
   const int m16 = lane & 15, grp = lane >> 4;
 
-  {
-    const int span = ntiles * kTF;
-    for (int e0 = 0; e0 < span; e0 += 4 * kNTF) {
-      int32_t v[4];
+  // The chunk's slots (at most 4 * 512 = kChunkF) are requested, then q of this wave's head
+  // group (B operand of S^T: head 16hg + m16, a group past the head count loads the last head
+  // and never uses it; K step 2u + h holds dims 64u + 16grp + 8h .. +8, the order in which a
+  // lane's 16-byte row piece 4u + grp is widened), then the slots are written to LDS: the wait
+  // for the slots (the older loads) leaves q in flight through the barrier and the first tile
+  // loads.
+  static_assert(kChunkF <= 4 * kNTF, "one round of slot loads");
+  const int span = ntiles * kTF;
+  int32_t slv[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = sl[min(j0 + e0 + u * kNTF + (int)threadIdx.x, p.k - 1)];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int e = e0 + u * kNTF + threadIdx.x;
-        if (e < span) sm.sl[e] = j0 + e < j1 ? dbg_slot(p.dbg, v[u], p.num_slots) : -1;
-      }
-    }
-  }
-  if (threadIdx.x == 0) sm.redo = 0;
-  if (!s_active && tb == 0) sm.pex[hg][lane] = bf16x8{};   // head groups past the head count: P = 0
-  __syncthreads();
-
-  // q of this wave's head group (B operand of S^T): head 16hg + m16 (a group past the head count
-  // loads the last head and never uses it); K step 2u + h holds dims 64u + 16grp + 8h .. +8,
-  // the order in which a lane's 16-byte row piece 4u + grp is widened
+  for (int u = 0; u < 4; ++u) slv[u] = sl[min(j0 + u * kNTF + (int)threadIdx.x, p.k - 1)];
+  __builtin_amdgcn_sched_barrier(0);   // (the slot loads stay ahead of q's)
   bf16x8 qf[kStepsF];
   {
     const int qhead = min(hg * 16 + m16, p.H - 1);
@@ -742,6 +734,14 @@ __global__ __launch_bounds__(kNTF) void mla_fp8d_kernel(MlaParams p) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) qf[2 * u + h] = qrow[8 * u + 2 * grp + h];
   }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int e = u * kNTF + threadIdx.x;
+    if (e < span) sm.sl[e] = j0 + e < j1 ? dbg_slot(p.dbg, slv[u], p.num_slots) : -1;
+  }
+  if (threadIdx.x == 0) sm.redo = 0;
+  if (!s_active && tb == 0) sm.pex[hg][lane] = bf16x8{};   // head groups past the head count: P = 0
+  lds_barrier();
 
   // ---- staging of tile v: every wave issues the same four loads per tile.  Loads 0 and 1 of
   // wave w read the tile's 16-byte pieces q = 64(w + 8c) + lane (1 KiB of whole rows each), load
@@ -1052,26 +1052,17 @@ __global__ __launch_bounds__(kNT) void mla_bf16d_kernel(MlaParams p) {
   const bool s_active = hg < ngroups;             // this wave's S^T head group exists
   const int m16 = lane & 15, grp = lane >> 4;
 
-  {
-    const int span = ntiles * kTT;
-    for (int e0 = 0; e0 < span; e0 += 4 * kNT) {
-      int32_t v[4];
+  // The chunk's slots (at most 4 * 512 = kChunkD) are requested, then q of this wave's head
+  // group (B operand of S^T: head 16hg + m16, dims 32s + 8grp .. +8; a group past the head count
+  // loads the last head and never uses it), then the slots are written to LDS: the wait for
+  // the slots (the older loads) leaves q in flight through the barrier and the first tile
+  // copies, and the wait for tile 0 covers it.
+  static_assert(kChunkD <= 4 * kNT, "one round of slot loads");
+  const int span = ntiles * kTT;
+  int32_t slv[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = sl[min(j0 + e0 + u * kNT + (int)threadIdx.x, p.k - 1)];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int e = e0 + u * kNT + threadIdx.x;
-        if (e < span) sm.sl[e] = j0 + e < j1 ? dbg_slot(p.dbg, v[u], p.num_slots) : -1;
-      }
-    }
-  }
-  if (threadIdx.x == 0) sm.redo = 0;
-  if (!s_active) sm.pex[hg][lane] = bf16x8{};   // head groups past the head count: P = 0
-  __syncthreads();
-  // q of this wave's head group (B operand of S^T): head 16hg + m16, dims 32s + 8grp .. +8 (a
-  // group past the head count loads the last head and never uses it).  Requested after the
-  // slot list and before the first tiles, so that the wait for tile 0 covers it and no wait
-  // for it covers the tiles after.
+  for (int u = 0; u < 4; ++u) slv[u] = sl[min(j0 + u * kNT + (int)threadIdx.x, p.k - 1)];
+  __builtin_amdgcn_sched_barrier(0);   // (the slot loads stay ahead of q's)
   bf16x8 qf[kStepsD];
   {
     const int qhead = min(hg * 16 + m16, p.H - 1);
@@ -1079,6 +1070,14 @@ __global__ __launch_bounds__(kNT) void mla_bf16d_kernel(MlaParams p) {
 #pragma unroll
     for (int s = 0; s < kStepsD; ++s) qf[s] = qrow[4 * s + grp];
   }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int e = u * kNT + threadIdx.x;
+    if (e < span) sm.sl[e] = j0 + e < j1 ? dbg_slot(p.dbg, slv[u], p.num_slots) : -1;
+  }
+  if (threadIdx.x == 0) sm.redo = 0;
+  if (!s_active) sm.pex[hg][lane] = bf16x8{};   // head groups past the head count: P = 0
+  lds_barrier();
 
   // copies of tile v: wave w issues copies w, w+8, .. (< 36): 5 for waves 0-3, 4 for waves 4-7
   const int nld = wave < kTDCopies - 4 * 8 ? 5 : 4;

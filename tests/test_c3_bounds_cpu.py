@@ -25,6 +25,17 @@ def _c3():
     return cfg, pt
 
 
+# a batch of 32 ragged sequences at parity-test lengths (the GPU parity case
+# test_indexer_parity_batch32_ragged runs exactly this configuration)
+SCALED32_LENS = [int(x) for x in np.random.default_rng(3232).integers(256, 12000, size=32, endpoint=True)]
+
+
+def scaled32():
+    cfg = dsa_inputs.scaled_config("c3", SCALED32_LENS, seed=3233)
+    pt = dsa_inputs.page_table_for(cfg, np.random.default_rng([cfg.seed, dsa_inputs._T_PERM]))
+    return cfg, pt
+
+
 def _indexer_launch(cfg):
     """launch_indexer's host arithmetic for the register kernel (one query row per sequence)."""
     B, Q, P, maxL = cfg.batch, cfg.q_per_seq, cfg.page_size, cfg.max_seq_len
@@ -63,11 +74,21 @@ def _partition(lens, maxL, balanced, B):
 
 def test_c3_indexer_reads_and_writes_stay_in_bounds_and_cover_every_column_once():
     cfg, pt = _c3()
+    assert min(cfg.seq_lens) >= 4096 and max(cfg.seq_lens) <= 131072 and cfg.batch == 32
+    _emulate_indexer(cfg, pt)
+
+
+def test_scaled_batch32_indexer_stays_in_bounds():
+    cfg, pt = scaled32()
+    assert cfg.batch == 32 and cfg.q_per_seq == 1
+    _emulate_indexer(cfg, pt)
+
+
+def _emulate_indexer(cfg, pt):
     B, Q, P, maxL = cfg.batch, cfg.q_per_seq, cfg.page_size, cfg.max_seq_len
     lens = cfg.seq_lens
-    assert min(lens) >= 4096 and max(lens) <= 131072 and B == 32
     lp = _indexer_launch(cfg)
-    assert lp["balanced"] > 0 and lp["grid"] == 256 and lp["QB"] == 1
+    assert lp["balanced"] > 0 and lp["grid"] == 256 and lp["QB"] == 1   # the balanced partition
     T, gi = _partition(lens, maxL, lp["balanced"], B)
     incl = np.cumsum(gi)
     assert incl[-1] <= lp["grid"], "every range gets a workgroup"

@@ -344,6 +344,21 @@ def test_decode_step_staged(name, lens, kw):
     (4) its selection against the oracle's fp64 selection, where every disagreement must sit
     within 2e-5 * max|s| of the k-th score."""
     cfg, inp, t = _case(name, lens, seed=106, **kw)
+    _check_staged(cfg, inp, t)
+
+
+def test_decode_step_staged_batch32_ragged():
+    """The staged protocol on a batch of 32 ragged sequences (contexts 515-11865): the indexer's
+    balanced key-range partition at B = 32, its ranges crossing sequence boundaries, 32 top-k rows
+    and 32 MLA rows.  tests/test_c3_bounds_cpu.py emulates this exact configuration's index
+    arithmetic on the CPU."""
+    from tests.test_c3_bounds_cpu import scaled32
+    cfg, _ = scaled32()
+    inp = dsa_inputs.make_inputs(cfg)
+    _check_staged(cfg, inp, dsa_inputs.to_torch(inp, cfg, DEV))
+
+
+def _check_staged(cfg, inp, t):
     r = run_step(cfg, t)
     s_g = r["scores"].cpu().numpy()
     s_ref = O.indexer_scores(inp["q_idx"], cfg.q_idx_dtype, inp["w"], inp["k_cache"], cfg.key_dtype,
