@@ -633,9 +633,11 @@ def measure_up_projection(rows, H, dev, stream, evict, KS):
     ms = time_graph([(lambda j=j: dsa.dsa_latent_up_projection(o, sets[j % nrep][0], sets[j % nrep][1], y, ws,
                                                               stream=stream)) for j in range(KS)], stream, evict) / KS
     by = wbytes + rows * H * 512 * 4 + rows * UP_D_MODEL * 4
+    fl = 2.0 * rows * (H * UP_V_DIM * 512 + UP_D_MODEL * H * UP_V_DIM)   # (the hi/lo parts not counted)
     us = ms * 1e3
-    return dict(us=round(us, 3), bytes=by, GBps=round(by / (us * 1e-6) / 1e9, 1), rows=rows, v_dim=UP_V_DIM,
-                d_model=UP_D_MODEL, kernels=["up_v_kernel", "up_y_kernel", "up_reduce_kernel"],
+    return dict(us=round(us, 3), bytes=by, GBps=round(by / (us * 1e-6) / 1e9, 1), flops=fl,
+                TFLOPs=round(fl / (us * 1e-6) / 1e12, 1), rows=rows, v_dim=UP_V_DIM,
+                d_model=UP_D_MODEL, kernels=["up_gemm_kernel", "up_reduce_kernel"],
                 timing="hip-graph of launches, weight sets cycled")
 
 
