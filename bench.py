@@ -377,9 +377,12 @@ def copy_calibration():
 def kernel_names(cfg, ns):
     """Names of the kernels the library launches for this workload (as rocprofv3 lists them)."""
     k = cfg.top_k
+    rows = cfg.batch * cfg.q_per_seq
     chunk = -(-(-(-k // ns)) // 32) * 32
     if cfg.kv_dtype == "fp8":
         mla = "mla_fp8d_kernel" if chunk <= 2048 else "mla_fp8_kernel"
+    elif cfg.mla_heads % 16 == 0 and cfg.mla_heads <= 64 and rows * (cfg.mla_heads // 16) <= 16 and chunk <= 512:
+        mla = "mla_bf16n_kernel"          # few bf16 rows: 16 heads per workgroup
     else:
         mla = "mla_bf16d_kernel" if chunk <= 2048 else "mla_mfma_kernel"
     idx = ("indexer_prefill_kernel" if cfg.q_per_seq >= 16 and cfg.key_dtype == "bf16" and cfg.page_size % 32 == 0

@@ -319,6 +319,9 @@ hipError_t launch_page_map(const int32_t* idx, int64_t total, int k, int Q, cons
 hipError_t launch_mla(const MlaParams& p, dsa_dtype_t q_dtype, dsa_dtype_t kv_dtype, hipStream_t s);
 hipError_t launch_combine(const CombineParams& p, hipStream_t s);
 int mla_default_split(int rows, int H, int k, dsa_dtype_t kv_dtype);
+// bf16 rows and at most 16 (query row, 16-head group) pairs: the few-rows kernel (16 heads per
+// workgroup, 128-token tiles)
+bool mla_uses_narrow(int rows, int H, dsa_dtype_t kv_dtype);
 hipError_t launch_cache_append(const AppendParams& p, hipStream_t s);
 int up_proj_ksplit(int R, int Dm, int K);
 hipError_t launch_up_proj(const UpProjParams& p, hipStream_t s);

@@ -3,7 +3,10 @@
 // 512 values, weight-absorbed and without GQA (Show HN "Chay GLM 5.2 tren may tinh cham",
 // main-features section).
 //
-// Kernels (bf16 q; the launcher picks one by row type and chunk length):
+// Kernels (bf16 q; the launcher picks one by row type, row count and chunk length):
+//   mla_bf16n_kernel  bf16 rows, at most 16 (query row, 16-head group) pairs, chunks <= 512:
+//                     one workgroup per (row, head group, chunk), 128-token tiles staged through
+//                     registers, the same fixed-reference softmax.
 //   mla_bf16d_kernel  bf16 rows, chunks <= 2048: 8 waves, 32-token tiles copied HBM -> LDS into
 //                     a 4-deep ring, S^T per (head group, 16-token block), P.V per 64 output
 //                     values over all heads, softmax against a fixed per-head reference.
@@ -1021,7 +1024,7 @@ struct BDSmem {
   bf16x8 pex[4][64];                          // P^T operands: head group, lane
   int32_t sl[kChunkD + 3 * kTT];              // the chunk's slots, -1 padded past the chunk
   float m0[2][64];                            // largest logit of the first tile, by token block
-  float fin_m[2][64], fin_l[2][64];           // per head and token block, after the last tile
+  float fin_m[2][64], fin_l[2][64], fin_r[2][64];   // per head and token block, after the last tile
   int32_t redo;
 };
 
@@ -1107,6 +1110,7 @@ __global__ __launch_bounds__(kNT) void mla_bf16d_kernel(MlaParams p) {
   float ref = 0.f;           // R of this lane's head
   float m_seen = -INFINITY;  // the head's largest logit in this wave's token blocks
   float l_run = 0.f;         // this lane group's share of sum exp2(z - R)
+  float l_rnd = 0.f;         // the same sum of P as rounded to bf16 for P.V (the output's normaliser)
 
   // S^T operand of block tb: row m = token 8(m/4) + 4tb + m%4, logical piece 4s + grp
   const int a_tok = 8 * (m16 >> 2) + 4 * tb + (m16 & 3);
@@ -1152,6 +1156,7 @@ __global__ __launch_bounds__(kNT) void mla_bf16d_kernel(MlaParams p) {
       const float pe = z[j] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(z[j] - ref);
       l_run += pe;
       pb[j] = (__bf16)pe;
+      l_rnd += (float)pb[j];
     }
     *(bf16x4*)((uint8_t*)&rd->pex[hg][lane] + 8 * tb) = pb;
   };
@@ -1183,6 +1188,7 @@ __global__ __launch_bounds__(kNT) void mla_bf16d_kernel(MlaParams p) {
 #pragma unroll
       for (int db = 0; db < kDBlocksD; ++db) o[g][db] = f32x4{0.f, 0.f, 0.f, 0.f};
     l_run = 0.f;
+    l_rnd = 0.f;
 #pragma unroll
     for (int v = 0; v < kRingD - 1; ++v)
       if (v < ntiles) issue(&sm, sm.ring[v], v);
@@ -1216,9 +1222,11 @@ __global__ __launch_bounds__(kNT) void mla_bf16d_kernel(MlaParams p) {
     // does some head's largest logit lie outside R +- 64?
     if (s_active) {
       const float l_blk = lanes4_sum(l_run);   // (all lanes of the wave take part)
+      const float r_blk = lanes4_sum(l_rnd);
       if (grp == 0) {
         sm.fin_m[tb][hg * 16 + m16] = m_seen;
         sm.fin_l[tb][hg * 16 + m16] = l_blk;
+        sm.fin_r[tb][hg * 16 + m16] = r_blk;
       }
     }
     __syncthreads();
@@ -1249,7 +1257,8 @@ __global__ __launch_bounds__(kNT) void mla_bf16d_kernel(MlaParams p) {
     // R of this head as its S^T waves used it (recomputed from what they published)
     const float m0 = fmaxf(sm.m0[0][head], sm.m0[1][head]);
     const float rh = sm.redo ? (mh > -INFINITY ? mh : 0.f) : (m0 == -INFINITY ? 0.f : m0);
-    const float inv = lh > 0.f ? 1.f / lh : 0.f;
+    const float lr = sm.fin_r[0][head] + sm.fin_r[1][head];
+    const float inv = lr > 0.f ? 1.f / lr : 0.f;
     if (wave == 0 && grp == 0) {
       if (p.n_split == 1) {
         if (p.lse) p.lse[(int64_t)r * p.H + head] = lh > 0.f ? (rh + log2f(lh)) * kLn2 : -INFINITY;
@@ -1271,6 +1280,266 @@ __global__ __launch_bounds__(kNT) void mla_bf16d_kernel(MlaParams p) {
     const int head = e >> 7, c = (e & 127) * 4;
     *(f32x4*)(dst + head * kVDim + c) = *(const f32x4*)(stage + head * kStageLd + c);
   }
+}
+
+// ---------------------------------------------------------------------------------------------
+// bf16 rows, few query rows: one workgroup per (query row, group of 16 heads, chunk of at most
+// kChunkN selected rows), 8 waves.  With one or two query rows the 64-head kernel above runs
+// few workgroups, each computing every head of its tiles; here the head groups of a chunk run
+// on separate compute units (ids 8 apart, so they share one L2 for the chunk's rows), each
+// tile's matrix work is a quarter as long, and the partials are per 16 heads.
+//   * 128-token tiles: each wave loads the rows of 16 tokens (18 KiB, 1 KiB of consecutive
+//     pieces per load) into registers, then stores them into the single LDS tile buffer in the
+//     layout of the kernel above (row t at t*1152, piece p in slot p ^ bf16_swz(t)); a skipped
+//     slot (-1) reads row 0 and is zeroed on the way in.  The next tile's loads are issued as soon as this one is
+//     stored, so they are in flight while it is computed.
+//   * q of the 16 heads is read from HBM once per workgroup and passed to the waves through the
+//     tile buffer (rows padded to 1168 bytes: conflict-free fragment reads) before the first
+//     tile is stored.
+//   * S^T: wave w covers 16 tokens of the tile over the full K: row m of its block is token
+//     32(w/2) + 8(m/4) + 4(w%2) + m%4, so lane group g of the result holds 4 consecutive tokens,
+//     one half of the P^T operand of the 32-token K step w/2 (the other half is wave w^1's).
+//   * P.V: wave w owns output values 64w .. 64w+63 of the 16 heads, four K steps per tile, V^T
+//     from the transposing LDS reads.
+//   * Softmax against a fixed per-head reference (the first tile's largest logit), with the
+//     second pass of the kernels above when a head's logits leave R +- 64.
+
+constexpr int kNTN = 512;                                 // threads per workgroup (8 waves)
+constexpr int kTN = 128;                                  // tokens per tile
+constexpr int kChunkN = 512;                              // selected rows per workgroup at most
+constexpr int kTNBytes = kTN * kRowDim * 2;               // 147456
+constexpr int kTNLoads = kTNBytes / 1024 / 8;             // 18 loads of 1 KiB per wave and tile
+constexpr int kKStepsN = kTN / 32;                        // 4 K steps of P.V per tile
+constexpr int kQPitchN = kRowDim * 2 + 16;                // bytes per staged q row
+constexpr int kFewHeadRows = 16;                          // rows x head groups served by this kernel
+static_assert(16 * kQPitchN <= kTNBytes, "q is staged in the tile buffer");
+
+struct NSmem {
+  uint8_t tile[kTNBytes];                     // the tile (q of the head group before the first)
+  bf16x8 pex[kKStepsN][64];                   // P^T operands of the tile's K steps
+  int32_t sl[kChunkN];                        // the chunk's slots, -1 past the chunk
+  float m0[8][16];                            // largest logit of the first tile, by wave
+  float fin_m[8][16], fin_l[8][16], fin_r[8][16];   // per wave and head, after the last tile
+};
+
+__global__ __launch_bounds__(kNTN) void mla_bf16n_kernel(MlaParams p) {
+  __shared__ __attribute__((aligned(16))) NSmem sm;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ks = wave >> 1, half = wave & 1;
+  const int m16 = lane & 15, grp = lane >> 4;
+  const int ng = p.H / 16;
+  // block b: chunk index rs = 8 * ((b / 8) / ng) + b % 8 (row rs / n_split), head group (b / 8) % ng
+  const int xq = blockIdx.x & 7, yq = blockIdx.x >> 3;
+  const int hg = yq % ng;
+  const int rs = 8 * (yq / ng) + xq;
+  if (rs >= p.rows * p.n_split) return;          // grid padding (uniform)
+  const int r = rs / p.n_split, split = rs - r * p.n_split;
+  const int j0 = split * p.chunk;
+  const int j1 = min(p.k, j0 + p.chunk);
+  const int ntiles = j1 > j0 ? (j1 - j0 + kTN - 1) / kTN : 0;
+  const int32_t* sl = p.slots + (int64_t)r * p.k;
+
+  // the chunk's slots (one per thread), then q of the head group into the tile buffer
+  static_assert(kChunkN <= kNTN, "one round of slot loads");
+  const int32_t slv = sl[min(j0 + (int)threadIdx.x, p.k - 1)];
+  __builtin_amdgcn_sched_barrier(0);
+  constexpr int kQPieces = 16 * (kRowDim * 2 / 16);       // 1152 pieces of 16 bytes
+  u32x4 qv[3];
+  const uint8_t* qbase = (const uint8_t*)p.q + ((int64_t)r * p.H + 16 * hg) * (kRowDim * 2);
+#pragma unroll
+  for (int c = 0; c < 3; ++c) {
+    const int e = min(c * kNTN + (int)threadIdx.x, kQPieces - 1);
+    qv[c] = *(const u32x4*)(qbase + 16 * e);
+  }
+  if ((int)threadIdx.x < ntiles * kTN)
+    sm.sl[threadIdx.x] = j0 + (int)threadIdx.x < j1 ? dbg_slot(p.dbg, slv, p.num_slots) : -1;
+#pragma unroll
+  for (int c = 0; c < 3; ++c) {
+    const int e = c * kNTN + (int)threadIdx.x;
+    if (e < kQPieces) {
+      const int h = e / 72, pc = e - h * 72;
+      *(u32x4*)(sm.tile + h * kQPitchN + 16 * pc) = qv[c];
+    }
+  }
+  lds_barrier();
+  bf16x8 qf[kStepsD];   // S^T B operand: head 16hg + m16, dims 32s + 8grp .. +8
+
+  // tile loads: wave w gathers the rows of tokens 16w .. 16w+15, 1152 pieces of 16 bytes in row
+  // order (piece P: row P / 72, piece P % 72); load c, lane i takes piece 64c + i, so each load
+  // reads 1 KiB of at most two rows (r0 = 64c / 72 and r0 + 1) and each store writes 1 KiB of
+  // LDS with no bank conflict.  The two rows' slots are wave-uniform (read lanes of sv16).
+  const uint8_t* kvb = (const uint8_t*)p.kv;
+  u32x4 st[kTNLoads];
+  uint32_t dead = 0;
+  auto load_tile = [&](const NSmem* __restrict__ rd, int v) {
+    const int32_t sv16 = rd->sl[v * kTN + 16 * wave + (lane & 15)];
+    int ln = lane;
+    asm volatile("" : "+v"(ln));   // (keeps the per-load lane arithmetic inside the tile loop)
+    dead = 0;
+#pragma unroll
+    for (int c = 0; c < kTNLoads; ++c) {
+      const int r0 = 64 * c / 72, r1 = r0 < 15 ? r0 + 1 : 15;
+      const int kb = 72 * (r0 + 1) - 64 * c;        // lanes below kb are in row r0
+      const int sa = __builtin_amdgcn_readlane(sv16, r0), sb = __builtin_amdgcn_readlane(sv16, r1);
+      const bool lo = ln < kb;
+      const int sv = lo ? sa : sb;
+      const int pc = ln + (lo ? 64 * c - 72 * r0 : 64 * c - 72 * (r0 + 1));
+      dead |= (sv < 0 ? 1u : 0u) << c;
+      st[c] = *(const u32x4*)(kvb + (int64_t)max(sv, 0) * (kRowDim * 2) + 16 * pc);
+    }
+  };
+  auto store_tile = [&](NSmem* __restrict__ rd) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+#pragma unroll
+    for (int c = 0; c < kTNLoads; ++c) {
+      const int r0 = 64 * c / 72;
+      const int kb = 72 * (r0 + 1) - 64 * c;
+      const bool lo = ln < kb;
+      const int t = 16 * wave + (lo ? r0 : r0 + 1);
+      const int pc = ln + (lo ? 64 * c - 72 * r0 : 64 * c - 72 * (r0 + 1));
+      *(u32x4*)(rd->tile + bf16_pos(t, pc)) = ((dead >> c) & 1u) ? u32x4{0u, 0u, 0u, 0u} : st[c];
+    }
+  };
+
+  f32x4 o[kDBlocksD];         // lane: O^T[64w + 16db + 4grp + j][head m16]
+  const float scale2 = p.sm_scale * kLog2e;
+  // l_run: sum of P (for lse and the chunk weight); l_rnd: sum of P as rounded to bf16 for P.V,
+  // the normaliser of the output, so that it is an exact convex combination of the V rows
+  float ref = 0.f, m_seen = -INFINITY, l_run = 0.f, l_rnd = 0.f;
+  const int a_tok = 32 * ks + 8 * (m16 >> 2) + 4 * half + (m16 & 3);
+  const int v_tok = 8 * grp + (m16 >> 2);
+
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+    for (int db = 0; db < kDBlocksD; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    l_run = 0.f;
+    l_rnd = 0.f;
+    if (ntiles > 0) load_tile(&sm, 0);
+    if (pass == 0) {
+      // q out of the tile buffer while the first tile's loads are in flight
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int s = 0; s < kStepsD; ++s) qf[s] = *(const bf16x8*)(sm.tile + m16 * kQPitchN + 16 * (4 * s + grp));
+      lds_barrier();   // every wave has read q
+    }
+    for (int v = 0; v < ntiles; ++v) {
+      wait_vmcnt<0>();
+      store_tile(&sm);
+      if (v + 1 < ntiles) load_tile(&sm, v + 1);
+      lds_barrier();   // tile v stored
+      const uint8_t* T = sm.tile;
+      // S^T of this wave's 16 tokens
+      f32x4 acc0 = f32x4{0.f, 0.f, 0.f, 0.f}, acc1 = f32x4{0.f, 0.f, 0.f, 0.f};
+      {
+        constexpr int kAhead = 4;
+        bf16x8 a[kAhead];
+#pragma unroll
+        for (int s = 0; s < kAhead; ++s) a[s] = *(const bf16x8*)(T + bf16_pos(a_tok, 4 * s + grp));
+#pragma unroll
+        for (int s = 0; s < kStepsD; ++s) {
+          const bf16x8 x = a[s % kAhead];
+          if (s + kAhead < kStepsD) a[s % kAhead] = *(const bf16x8*)(T + bf16_pos(a_tok, 4 * (s + kAhead) + grp));
+          if (s & 1) acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, qf[s], acc1, 0, 0, 0);
+          else acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, qf[s], acc0, 0, 0, 0);
+        }
+      }
+      const f32x4 sacc = acc0 + acc1;
+      // lane: head 16hg + m16, tokens 32ks + 8grp + 4half + j
+      float z[4];
+      float tmax = -INFINITY;
+      {
+        const int32_t* slt = sm.sl + v * kTN + 32 * ks + 8 * grp + 4 * half;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          z[j] = slt[j] >= 0 ? sacc[j] * scale2 : -INFINITY;
+          tmax = fmaxf(tmax, z[j]);
+        }
+        tmax = lanes4_max(tmax);
+      }
+      if (pass == 0 && v == 0) {
+        // the reference: the first tile's largest logit of the head (0 without a live token)
+        if (grp == 0) sm.m0[wave][m16] = tmax;
+        lds_barrier();   // (the next tile's loads stay in flight)
+        float m0 = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) m0 = fmaxf(m0, sm.m0[w][m16]);
+        ref = m0 == -INFINITY ? 0.f : m0;
+      }
+      m_seen = fmaxf(m_seen, tmax);
+      {
+        bf16x4 pb;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float pe = z[j] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(z[j] - ref);
+          l_run += pe;
+          pb[j] = (__bf16)pe;
+          l_rnd += (float)pb[j];
+        }
+        *(bf16x4*)((uint8_t*)&sm.pex[ks][lane] + 8 * half) = pb;
+      }
+      lds_barrier();   // P of the tile is published
+#pragma unroll
+      for (int kk = 0; kk < kKStepsN; ++kk) {
+        const bf16x8 pg = sm.pex[kk][lane];
+#pragma unroll
+        for (int db = 0; db < kDBlocksD; ++db) {
+          const int pc = 8 * wave + 2 * db + ((m16 & 3) >> 1);
+          const int off = 8 * (m16 & 1);
+          const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (__attribute__((address_space(3))) bf16x4*)(T + bf16_pos(32 * kk + v_tok, pc) + off));
+          const bf16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (__attribute__((address_space(3))) bf16x4*)(T + bf16_pos(32 * kk + v_tok + 4, pc) + off));
+          o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7),
+                                                          pg, o[db], 0, 0, 0);
+        }
+      }
+      if (v + 1 < ntiles) lds_barrier();   // every wave is done with the tile and P
+    }
+    // does some head's largest logit lie outside R +- 64?
+    {
+      const float l_blk = lanes4_sum(l_run), r_blk = lanes4_sum(l_rnd);
+      if (grp == 0) {
+        sm.fin_m[wave][m16] = m_seen;
+        sm.fin_l[wave][m16] = l_blk;
+        sm.fin_r[wave][m16] = r_blk;
+      }
+    }
+    lds_barrier();
+    // every wave reaches the same answer: its lanes cover the 16 heads
+    float mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) mx = fmaxf(mx, sm.fin_m[w][m16]);
+    const bool wide = mx > -INFINITY && (mx > ref + kRefMargin || mx < ref - kRefMargin);
+    if (pass == 1 || __builtin_amdgcn_ballot_w64(wide) == 0) break;
+    ref = mx > -INFINITY ? mx : 0.f;
+  }
+
+  // output: lane holds values 64w + 16db + 4grp .. +3 of head 16hg + m16
+  const int head = 16 * hg + m16;
+  float lh = 0.f, rh = 0.f;
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    lh += sm.fin_l[w][m16];
+    rh += sm.fin_r[w][m16];
+  }
+  const float inv = rh > 0.f ? 1.f / rh : 0.f;
+  // R as the S^T waves used it: ref (pass 0, or the chunk maximum after a second pass)
+  if (wave == 0 && grp == 0) {
+    if (p.n_split == 1) {
+      if (p.lse) p.lse[(int64_t)r * p.H + head] = lh > 0.f ? (ref + log2f(lh)) * kLn2 : -INFINITY;
+    } else {
+      const int64_t prow = ((int64_t)r * p.n_split + split) * p.H + head;
+      p.part_m[prow] = lh > 0.f ? ref * kLn2 : -INFINITY;
+      p.part_l[prow] = lh;
+    }
+  }
+  float* dst = p.n_split == 1 ? p.out + ((int64_t)r * p.H + head) * kVDim
+                              : p.part_o + (((int64_t)r * p.n_split + split) * p.H + head) * kVDim;
+#pragma unroll
+  for (int db = 0; db < kDBlocksD; ++db) *(f32x4*)(dst + 64 * wave + 16 * db + 4 * grp) = o[db] * inv;
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -1385,8 +1654,17 @@ __global__ __launch_bounds__(256) void mla_combine_few_kernel(CombineParams p) {
 
 }  // namespace
 
+bool mla_uses_narrow(int rows, int H, dsa_dtype_t kv_dtype) {
+  return kv_dtype == DSA_BF16 && H % 16 == 0 && H <= 64 && (int64_t)rows * (H / 16) <= kFewHeadRows;
+}
+
 int mla_default_split(int rows, int H, int k, dsa_dtype_t kv_dtype) {
-  (void)H;
+  if (mla_uses_narrow(rows, H, kv_dtype)) {
+    // one 128-token tile per chunk, at most about one workgroup per compute unit
+    const int per = rows * (H / 16);
+    const int cap = per > 0 ? std::max(1, 256 / per) : 1;
+    return std::max(1, std::min((k + kTN - 1) / kTN, cap));
+  }
   // about one workgroup per compute unit, at least 64 selected rows per chunk, and for fp8 rows
   // at most kChunkF (the fp8 ring kernel's staging limit)
   int ns = 256 / (rows > 0 ? rows : 1);
@@ -1419,7 +1697,10 @@ hipError_t launch_mla(const MlaParams& p0, dsa_dtype_t q_dtype, dsa_dtype_t kv_d
                          dim3(kNTF), 0, s, p);
     else hipLaunchKernelGGL(mla_fp8_kernel, grid, dim3(kNT), 0, s, p);
   }
-  else if (chunk <= kChunkD)
+  else if (mla_uses_narrow(p.rows, p.H, kv_dtype) && chunk <= kChunkN) {
+    const int64_t rs = (int64_t)p.rows * p.n_split;
+    hipLaunchKernelGGL(mla_bf16n_kernel, dim3((unsigned)((rs + 7) / 8 * 8 * (p.H / 16))), dim3(kNTN), 0, s, p);
+  } else if (chunk <= kChunkD)
     hipLaunchKernelGGL(mla_bf16d_kernel, dim3((unsigned)((p.rows >= 8 ? (p.rows + 7) / 8 * 8 : p.rows) * p.n_split)),
                        dim3(kNT), 0, s, p);
   else hipLaunchKernelGGL(mla_mfma_kernel<false>, grid, dim3(kNT), 0, s, p);

@@ -144,7 +144,8 @@ def test_mla_workspace_sizes(L):
     # one chunk needs no workspace; k chunks need partial o, m and l per head
     assert L.dsa_sparse_mla_workspace_size(1, 1, 64, 2048, 1, dsa.DSA_BF16, dsa.DSA_BF16) == 0
     ns = L.dsa_sparse_mla_default_split(1, 1, 64, 2048, dsa.DSA_BF16)
-    assert 1 < ns <= 64
+    assert ns == 16          # few bf16 rows: one 128-row tile per chunk (16-head workgroups)
+    assert L.dsa_sparse_mla_default_split(4, 1, 64, 2048, dsa.DSA_BF16) == 16
     need = L.dsa_sparse_mla_workspace_size(1, 1, 64, 2048, 4, dsa.DSA_BF16, dsa.DSA_BF16)
     assert need >= 4 * 64 * 512 * 4 + 2 * 4 * 64 * 4
     assert L.dsa_sparse_mla_workspace_size(1, 1, 16, 2048, 4, dsa.DSA_F32, dsa.DSA_BF16) == 0   # vector path: no split
