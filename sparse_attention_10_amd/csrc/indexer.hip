@@ -256,11 +256,15 @@ __global__ __launch_bounds__(kPfThreads) void indexer_prefill_kernel(IndexerPara
 #pragma unroll
       for (int qi = 0; qi < kPfQW; ++qi) {
         f32x16 acc[2] = {f32x16{}, f32x16{}};
+        // raised priority while issuing the row's MFMAs; the other wave of the SIMD runs its
+        // head reduction meanwhile (c4 indexer 3755 -> 3485 us)
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int s = 0; s < 8; ++s)
 #pragma unroll
           for (int mb = 0; mb < 2; ++mb)
             acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag[qi][mb][s], kf[s], acc[mb], 0, 0, 0);
+        __builtin_amdgcn_s_setprio(0);
         finish(rd, acc, qi, t);
       }
     }
