@@ -705,7 +705,17 @@ hipError_t launch_indexer(const IndexerParams& p0, dsa_dtype_t q_dtype, dsa_dtyp
     if (ct) hipLaunchKernelGGL((indexer_reg_kernel<F8, true, QBV, NWV, DV>), grid, dim3(NWV * 64), 0, s, p);  \
     else hipLaunchKernelGGL((indexer_reg_kernel<F8, false, QBV, NWV, DV>), grid, dim3(NWV * 64), 0, s, p);    \
   } while (0)
-    if (QB == 1) { if (f8) DSA_IDX_REG2(true, 1, 8, 4); else DSA_IDX_REG2(false, 1, 8, 3); }
+    // one row: the ring depth follows this wave's block count when it is small, so that the
+    // loop runs no iteration on dummy blocks (c2 at 32K: one block per wave)
+    const int64_t bpw = (tb + NW - 1) / NW;
+    if (QB == 1) {
+      if (p.balanced) { if (f8) DSA_IDX_REG2(true, 1, 8, 4); else DSA_IDX_REG2(false, 1, 8, 3); }
+      else if (bpw <= 1) { if (f8) DSA_IDX_REG2(true, 1, 8, 1); else DSA_IDX_REG2(false, 1, 8, 1); }
+      else if (bpw == 2) { if (f8) DSA_IDX_REG2(true, 1, 8, 2); else DSA_IDX_REG2(false, 1, 8, 2); }
+      else if (f8) DSA_IDX_REG2(true, 1, 8, 4);
+      else if (bpw % 4 == 0) DSA_IDX_REG2(false, 1, 8, 4);
+      else DSA_IDX_REG2(false, 1, 8, 3);
+    }
     else if (QB == 2) { if (f8) DSA_IDX_REG2(true, 2, 8, 3); else DSA_IDX_REG2(false, 2, 8, 2); }
     else if (QB == 3) { if (f8) DSA_IDX_REG2(true, 3, 4, 4); else DSA_IDX_REG2(false, 3, 4, 3); }
     else { if (f8) DSA_IDX_REG2(true, 4, 4, 3); else DSA_IDX_REG2(false, 4, 4, 2); }

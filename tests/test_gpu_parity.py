@@ -45,6 +45,10 @@ INDEXER_CASES = [
     # rows of one sequence scored from one key read: 3 and 4 rows per workgroup, row groups
     ("c2", [1000, 333], dict(q_per_seq=4)),
     ("c5", [2000, 515], dict(q_per_seq=4)),
+    # one row of one sequence: the key ring is 1, 2 or 4 blocks deep by the blocks per wave
+    ("c2", [40000], dict()),
+    ("c5", [3000], dict(q_per_seq=1)),
+    ("c5", [40000], dict(q_per_seq=1)),
     ("c5", [1500], dict(q_per_seq=3)),
     ("c2", [700, 450], dict(q_per_seq=6)),
     ("c5", [300 + 20], dict(q_per_seq=20)),
