@@ -126,7 +126,10 @@ dsa_status_t dsa_page_map(const dsa_batch_t *batch, const int32_t *topk_idx, int
  *   out[r,h,:] = sum_s softmax(z)_s * c~[s, 0:512]  (V is the first 512 values of the row)
  *   lse[r,h]   = log sum_s exp(z_s)                 (natural log)
  * c~ = kv_cache row, or kv_scale[s] * code for fp8.  A row with no valid slot gives out = 0
- * and lse = -inf.
+ * and lse = -inf.  On the matrix cores (bf16 q) the logits are exact products summed in f32;
+ * the softmax weights enter the weighted sum of V as bf16 (fp8 rows: with the row's scale
+ * folded in), and for bf16 rows the output is divided by the sum of those rounded weights, so
+ * it stays a convex combination of the selected rows; lse uses the unrounded sum.
  *   q         [B, Q, n_heads, 576] f32 or bf16
  *   kv_cache  [num_slots, 576] f32, bf16 or fp8;  kv_scale [num_slots] f32 for fp8, else NULL
  *   slots     [B, Q, k] int32 (any order; -1 entries are skipped)
@@ -147,8 +150,10 @@ dsa_status_t dsa_sparse_mla_decode(int32_t batch, int32_t q_per_seq,
                                    void *workspace, size_t workspace_bytes, void *stream);
 size_t dsa_sparse_mla_workspace_size(int32_t batch, int32_t q_per_seq, int32_t n_heads, int32_t k,
                                      int32_t n_split, dsa_dtype_t q_dtype, dsa_dtype_t kv_dtype);
-/* The n_split that dsa_sparse_mla_decode uses when passed 0 (fp8 rows: at most 2048 selected
- * rows per chunk). */
+/* The n_split that dsa_sparse_mla_decode uses when passed 0: about one workgroup per compute
+ * unit; fp8 rows keep at most 2048 selected rows per chunk; bf16 rows with at most 16 (query
+ * row, 16-head group) pairs in all take chunks of 128 selected rows (one workgroup per row,
+ * head group and chunk). */
 int32_t dsa_sparse_mla_default_split(int32_t batch, int32_t q_per_seq, int32_t n_heads, int32_t k,
                                      dsa_dtype_t kv_dtype);
 
