@@ -16,7 +16,8 @@
 //     many rows) and a range of k.  Each 128-wide (64-wide) chunk of k of the tile's activations
 //     is loaded once, split into its two bf16 parts and stored in LDS (rows padded by 16 bytes,
 //     so the operand reads are free of bank conflicts); wave w reads the weights of its 32 (64)
-//     columns straight into registers.
+//     columns into registers, with tiles of up to 64 rows as 1 KiB runs that it turns around
+//     through its own LDS area into the operand layout.
 //     Weights are therefore read once per row tile (once in decode, where the rows are few), and
 //     the next chunk's loads are in flight while the current one is multiplied.
 //   * v: one group of tiles per head (A = o[:, h, :], B = W_UV[h], K = 512).  y: K = H * Dv is
@@ -50,6 +51,16 @@ __global__ __launch_bounds__(kGT) void up_gemm_kernel(GemmArgs g) {
   constexpr int kS = KC / 32;         // k steps per chunk
   constexpr int kF4 = KC / 4;         // float4 per staged row
   __shared__ __attribute__((aligned(16))) __bf16 as[2][2][RB * 16][kPitch];   // [buffer][hi, lo][row][k]
+  // Tiles of up to 64 rows (where the weight stream sets the time): weights go HBM -> registers
+  // with 1 KiB loads of consecutive 16-byte pieces (whole column runs of the chunk), then turn
+  // around in a per-wave LDS area into the operand layout (one row: 42.8 -> 29.6 us).  128-row
+  // tiles load the operand layout directly (64 bytes of 16 columns per load), as the LDS
+  // traffic of the turnaround costs more than the coalescing gains there.
+  constexpr bool kTT = RB <= 4;
+  constexpr int kPPC = KC / 8;                       // 16-byte pieces of a column in one chunk
+  constexpr int kWL = CB * 16 * kPPC / 64;           // 1 KiB loads per wave and chunk
+  constexpr int kColsPer256 = 16 / kPPC;             // columns in 256 bytes of the area
+  __shared__ __attribute__((aligned(16))) uint8_t wt[kTT ? 4 : 1][kTT ? CB * 16 * KC * 2 : 16];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -93,6 +104,24 @@ __global__ __launch_bounds__(kGT) void up_gemm_kernel(GemmArgs g) {
       *(bf16x4*)&as[buf][1][r][kk] = lo;
     }
   };
+  // turned-around layout: column c of the wave at c * 2KC bytes, its piece q in slot
+  // q ^ ((c / kColsPer256) % kPPC), so that the 16 columns of one operand read fall on distinct
+  // banks and each 1 KiB store is a permutation of a contiguous KiB
+  auto wt_off = [](int c, int q) { return c * (2 * KC) + ((q ^ ((c / kColsPer256) & (kPPC - 1))) << 4); };
+  // chunk c's weights of this wave: load j, lane i takes piece 64j + i of the wave's columns in
+  // column order (column (64j + i) / kPPC, values 8 * ((64j + i) % kPPC) .. +8; 0 past the range)
+  auto load_raw = [&](u32x4 (&raw)[kWL], int c) {
+    const int kb = k0 + c * KC;
+#pragma unroll
+    for (int j = 0; j < kWL; ++j) {
+      const int pc = 64 * j + lane;
+      const int cl = pc / kPPC, q = pc - cl * kPPC;
+      const int n = min(col0 + 16 * CB * wave + cl, g.N - 1);
+      const int k = kb + 8 * q;
+      const u32x4 x = *(const u32x4*)(B + (int64_t)n * g.ldb + min(k, k1 - 8));
+      raw[j] = k < k1 ? x : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
   // weights of chunk c for this wave's CB column blocks: lane (n16, grp) of block cb, k step s
   // reads column col0 + 16(CB w + cb) + n16, values kb + 32s + 8grp .. +8 (0 past the range)
   auto load_b = [&](bf16x8 (&bb)[CB][kS], int c) {
@@ -130,24 +159,71 @@ __global__ __launch_bounds__(kGT) void up_gemm_kernel(GemmArgs g) {
       }
   };
 
-  // two chunks per loop trip, so that the two weight buffers keep their registers; every step
-  // issues the same loads (the chunk index is clamped past the end)
-  bf16x8 bx[CB][kS], by[CB][kS];
-  load_a(0);
-  load_b(bx, 0);
-  store_a(0);
-  lds_barrier();
-  for (int c = 0; c < nch; c += 2) {
-    load_a(min(c + 1, nch - 1));
-    load_b(by, min(c + 1, nch - 1));
-    compute(0, bx);
-    store_a(1);
-    lds_barrier();   // chunk c + 1 staged; buffer 0 is no longer read
-    load_a(min(c + 2, nch - 1));
-    load_b(bx, min(c + 2, nch - 1));
-    if (c + 1 < nch) compute(1, by);
+  if constexpr (kTT) {
+    // the wave's weights through its LDS area (a wave's LDS accesses complete in order: no
+    // barrier), then the same MFMAs with the operands read per k step
+    uint8_t* my = wt[kTT ? wave : 0];
+    auto compute_tt = [&](int buf, const u32x4 (&raw)[kWL]) {
+#pragma unroll
+      for (int j = 0; j < kWL; ++j) {
+        const int pc = 64 * j + lane;
+        const int cl = pc / kPPC, q = pc - cl * kPPC;
+        *(u32x4*)(my + wt_off(cl, q)) = raw[j];
+      }
+#pragma unroll
+      for (int s = 0; s < kS; ++s) {
+        bf16x8 bb[CB];
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) bb[cb] = *(const bf16x8*)(my + wt_off(16 * cb + n16, 4 * s + grp));
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const bf16x8 ah = *(const bf16x8*)&as[buf][0][16 * rb + n16][32 * s + 8 * grp];
+          const bf16x8 al = *(const bf16x8*)&as[buf][1][16 * rb + n16][32 * s + 8 * grp];
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb) {
+            acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bb[cb], acc[rb][cb], 0, 0, 0);
+            acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bb[cb], acc[rb][cb], 0, 0, 0);
+          }
+        }
+      }
+    };
+    u32x4 rx[kWL], ry[kWL];
+    load_a(0);
+    load_raw(rx, 0);
     store_a(0);
-    lds_barrier();   // chunk c + 2 staged; buffer 1 is no longer read
+    lds_barrier();
+    for (int c = 0; c < nch; c += 2) {
+      load_a(min(c + 1, nch - 1));
+      load_raw(ry, min(c + 1, nch - 1));
+      compute_tt(0, rx);
+      store_a(1);
+      lds_barrier();   // chunk c + 1 staged; buffer 0 is no longer read
+      load_a(min(c + 2, nch - 1));
+      load_raw(rx, min(c + 2, nch - 1));
+      if (c + 1 < nch) compute_tt(1, ry);
+      store_a(0);
+      lds_barrier();   // chunk c + 2 staged; buffer 1 is no longer read
+    }
+  } else {
+    // two chunks per loop trip, so that the two weight buffers keep their registers; every step
+    // issues the same loads (the chunk index is clamped past the end)
+    bf16x8 bx[CB][kS], by[CB][kS];
+    load_a(0);
+    load_b(bx, 0);
+    store_a(0);
+    lds_barrier();
+    for (int c = 0; c < nch; c += 2) {
+      load_a(min(c + 1, nch - 1));
+      load_b(by, min(c + 1, nch - 1));
+      compute(0, bx);
+      store_a(1);
+      lds_barrier();   // chunk c + 1 staged; buffer 0 is no longer read
+      load_a(min(c + 2, nch - 1));
+      load_b(bx, min(c + 2, nch - 1));
+      if (c + 1 < nch) compute(1, by);
+      store_a(0);
+      lds_barrier();   // chunk c + 2 staged; buffer 1 is no longer read
+    }
   }
 
   // lane (n16, grp) holds C[16rb + 4grp + j][16(CB w + cb) + n16]
