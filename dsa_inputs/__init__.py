@@ -81,7 +81,8 @@ def _std(d: int) -> float:
 def base_config(name: str, seed: Optional[int] = None) -> DsaConfig:
     """The workloads, by name: c1 (tiny fp32), c2 (32K single stream), c2_128k (the
     same layer at 128K), c3 (batch 32, ragged 4K-128K), c4 (4096-token chunked prefill
-    over a 64K prefix), c5 (fp8 caches, batch 64 x 2 speculative-verify rows at 64K)."""
+    over a 64K prefix), c5 (fp8 caches, batch 64 x 2 speculative-verify rows at 64K),
+    c5_q4 (the same with 4 verify rows per sequence: a draft depth of 3)."""
     name = name.lower()
     s = 1000 + int(name[1]) if seed is None else seed
     if name == "c1":
@@ -106,6 +107,10 @@ def base_config(name: str, seed: Optional[int] = None) -> DsaConfig:
         c = dict(common)
         c.update(key_dtype="fp8", kv_dtype="fp8")
         return DsaConfig("c5", 64, 2, [65536] * 64, **c)
+    if name == "c5_q4":        # deeper speculative verify: 4 rows per sequence
+        c = dict(common)
+        c.update(key_dtype="fp8", kv_dtype="fp8", seed=1007 if seed is None else seed)
+        return DsaConfig("c5_q4", 64, 4, [65536] * 64, **c)
     raise ValueError(f"unknown config {name!r}")
 
 

@@ -3,8 +3,9 @@
 // The pages name this stage the "lightning-indexer GEMM" ("GLM-52 Runs on RTX 4090", section
 // "how did he do it"; renning22/glm-5.2-4090 README, section "how it works").  Three kernels:
 //
-//  * indexer_reg_kernel (decode: 64 heads x 128 dims, bf16 q, bf16 or fp8 keys, up to 4 query
-//    rows of a sequence per workgroup).  v_mfma_f32_16x16x32_bf16 with 16 heads as M and 16
+//  * indexer_reg_kernel (decode: 64 heads x 128 dims, bf16 q, bf16 or fp8 keys, one or two query
+//    rows of a sequence per workgroup; more rows in groups of two whose workgroups share an XCD,
+//    so the repeated key reads come from L2).  v_mfma_f32_16x16x32_bf16 with 16 heads as M and 16
 //    tokens as N; keys stream HBM -> registers with 1 KB coalesced loads, turn around in a
 //    per-wave LDS area into the operand layout, and every key is read once for all the rows of
 //    its workgroup.  ReLU, head weights and the head sum stay in registers.
@@ -678,8 +679,12 @@ hipError_t launch_indexer(const IndexerParams& p0, dsa_dtype_t q_dtype, dsa_dtyp
   if (indexer_uses_mfma(p.Hi, p.Di, q_dtype, k_dtype)) {
     // Keys straight into registers: QB rows per workgroup (one row group for Q <= 4), about one
     // round of 256 workgroups (one per compute unit) per row group.
-    const int QB = p.Q <= 2 ? p.Q : (p.Q == 3 ? 3 : 4);
-    const int NW = QB <= 2 ? 8 : 4;
+    // At most two rows per workgroup: q of four rows fills all 256 registers of the only wave a
+    // SIMD could then hold, and without a second wave to cover its latencies that was slower
+    // than two groups of two rows whose repeated key reads come from L2 (64 sequences x 4 fp8
+    // rows at 64K: 508 against 311 us; one sequence x 3 bf16 rows at 32K: 11.0 against 9.6 us)
+    const int QB = p.Q <= 2 ? p.Q : 2;
+    const int NW = 8;
     const int64_t ng = (p.Q + QB - 1) / QB;
     const int64_t blocks = ((int64_t)p.max_seq_len + kRB - 1) / kRB;
     const int64_t tb_max = std::max<int64_t>(1, (int64_t)(kRegMaxPages - 2) * p.P / kRB);
@@ -717,8 +722,6 @@ hipError_t launch_indexer(const IndexerParams& p0, dsa_dtype_t q_dtype, dsa_dtyp
       else DSA_IDX_REG2(false, 1, 8, 3);
     }
     else if (QB == 2) { if (f8) DSA_IDX_REG2(true, 2, 8, 3); else DSA_IDX_REG2(false, 2, 8, 2); }
-    else if (QB == 3) { if (f8) DSA_IDX_REG2(true, 3, 4, 4); else DSA_IDX_REG2(false, 3, 4, 3); }
-    else { if (f8) DSA_IDX_REG2(true, 4, 4, 3); else DSA_IDX_REG2(false, 4, 4, 2); }
 #undef DSA_IDX_REG2
     return hipGetLastError();
   }
