@@ -252,7 +252,9 @@ __global__ __launch_bounds__(256) void up_reduce_kernel(UpProjParams p) {
   p.y[e] = s;
 }
 
-int rows_per_tile_blocks(int R) { return R <= 16 ? 1 : R <= 32 ? 2 : R <= 64 ? 4 : 8; }
+// rows per tile in blocks of 16: up to 128 rows in tiles of at most 64 (whose weights take the
+// LDS turnaround; 128 rows: 88.8 -> 84.6 us although the weights are read by two tiles)
+int rows_per_tile_blocks(int R) { return R <= 16 ? 1 : R <= 32 ? 2 : R <= 128 ? 4 : 8; }
 // column blocks per wave: with at least two rounds of 128 x 256 tiles (many rows), 64 columns
 // per wave, so that each activation operand read from LDS feeds twice the matrix work;
 // otherwise 32, which keeps more workgroups in flight
