@@ -39,7 +39,7 @@ def scaled32():
 def _indexer_launch(cfg):
     """launch_indexer's host arithmetic for the register kernel (one query row per sequence)."""
     B, Q, P, maxL = cfg.batch, cfg.q_per_seq, cfg.page_size, cfg.max_seq_len
-    QB = Q if Q <= 2 else (3 if Q == 3 else 4)
+    QB = Q if Q <= 2 else 2
     ng = (Q + QB - 1) // QB
     blocks = (maxL + KRB - 1) // KRB
     tb_max = max(1, (REG_MAX_PAGES - 2) * P // KRB)

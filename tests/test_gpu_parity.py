@@ -42,9 +42,10 @@ INDEXER_CASES = [
     # long contexts: several 128-token tiles per workgroup (work >= 4096 tiles)
     ("c2", [131072, 131072, 60000, 60000, 60001, 59999, 4097, 77], dict()),
     ("c5", [131072, 100000, 70000, 9000], dict()),                    # fp8, Q = 2, two tiles per workgroup
-    # rows of one sequence scored from one key read: 3 and 4 rows per workgroup, row groups
+    # more rows per sequence than one workgroup takes: rows in groups of two, a partial last group
     ("c2", [1000, 333], dict(q_per_seq=4)),
     ("c5", [2000, 515], dict(q_per_seq=4)),
+    ("c2", [1500, 700], dict(q_per_seq=3)),
     # one row of one sequence: the key ring is 1, 2 or 4 blocks deep by the blocks per wave
     ("c2", [40000], dict()),
     ("c5", [3000], dict(q_per_seq=1)),
