@@ -576,6 +576,14 @@ __global__ __launch_bounds__(NW * 64) void indexer_reg_kernel(IndexerParams p) {
 #pragma unroll
   for (int u = 0; u < D; ++u) pgr[u] = CT ? blk_pe(u + D) : 0;
   const int nbw_pad = (nbw + D - 1) / D * D;
+  // the lane's head weights (its 16 heads of each row) stay in registers where they fit (two
+  // bf16 rows need those registers for their keys and are read from LDS per block)
+  constexpr bool WREG = FP8 || QB == 1;
+  f32x4 wr[WREG ? QB : 1][4];
+#pragma unroll
+  for (int qi = 0; qi < (WREG ? QB : 1); ++qi)
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb) wr[qi][hb] = *(const f32x4*)&rd->w[qi][16 * hb + 4 * g];
   for (int j0 = 0; j0 < nbw_pad; j0 += D) {
 #pragma unroll
     for (int u = 0; u < D; ++u) {
@@ -623,7 +631,7 @@ __global__ __launch_bounds__(NW * 64) void indexer_reg_kernel(IndexerParams p) {
         float s_ = 0.f;
 #pragma unroll
         for (int hb = 0; hb < 4; ++hb) {
-          const f32x4 wv = *(const f32x4*)&rd->w[qi][16 * hb + 4 * g];
+          const f32x4 wv = WREG ? wr[WREG ? qi : 0][hb] : *(const f32x4*)&rd->w[qi][16 * hb + 4 * g];
 #pragma unroll
           for (int jx = 0; jx < 4; ++jx)   // ReLU as one integer max on the bits (negatives -> +0)
             s_ = fmaf(wv[jx], __int_as_float(max(__float_as_int(acc[4 * qi + hb][jx]), 0)), s_);
