@@ -12,8 +12,7 @@
 //                     values over all heads, softmax against a fixed per-head reference.
 //   mla_fp8d_kernel   fp8 rows, chunks <= 2048: 8 waves, 32-token e4m3 tiles staged HBM ->
 //                     registers -> LDS with coalesced loads, rows widened exactly to bf16 at
-//                     each operand read, the same fixed-reference softmax; with 64 heads and
-//                     128-255 unsplit rows, one workgroup per head half and 64-token tiles.
+//                     each operand read, the same fixed-reference softmax.
 //   mla_fp8_kernel    fp8 rows, longer chunks: 8 waves, online softmax with lazy rescaling.
 //   mla_mfma_kernel   bf16 rows, longer chunks: 8 waves, rows staged through registers.
 // Common to all: S^T = rows . q^T and O^T += V^T . P^T on the bf16 (or e4m3) MFMAs in fp32,
@@ -675,72 +674,45 @@ __global__ __launch_bounds__(kNT) void mla_fp8_kernel(MlaParams p) {
 //     computed again with R = the head's largest logit.  The accumulators are only touched by
 //     the matrix core.
 //   * Two barriers per tile (next tile stored; P published).
-//   * Head halves (HG = 2, below): the same roles with 2 head groups x 4 token blocks over a
-//     64-token tile, P.V in two K steps of 32 tokens, two tiles staged in registers into two LDS
-//     slots; a workgroup covers 32 heads of one row over its whole selection, so the two halves
-//     of a row need no merge.
+constexpr int kTF = 32;                                   // tokens per tile
+constexpr int kTFBytes = kTF * kRowDim;                   // 18432
 constexpr int kNTF = 512;                                 // 8 waves
 constexpr int kChunkF = 2048;                             // selected rows staged per workgroup
 constexpr int kStepsF = kRowDim / 32;                     // 18 K steps of 32
 constexpr int kDBlocksF = kVDim / 16 / 8;                 // 4 output blocks of 16 per wave
 
-// HG head groups of 16 per workgroup (4: all 64 heads, 32-token tiles; 2: 32 heads, 64-token
-// tiles, one head half of the row per workgroup), 8 / HG token blocks of 16 per tile.
-template <int HG>
-struct FDCfg {
-  static constexpr int TB = 8 / HG;                       // token blocks per tile
-  static constexpr int TT = 16 * TB;                      // tokens per tile: 32 or 64
-  static constexpr int KS = TT / 32;                      // P.V K steps per tile
-  static constexpr int TFB = TT * kRowDim;                // tile bytes: 18432 or 36864
-  static constexpr int NLD = TFB / 8192;                  // 1 KiB loads per wave: 2 or 4
-  static constexpr int EW = (TFB - 8192 * NLD) / 2048;    // words of the last load per lane: 1 or 2
-  static constexpr int SPW = TT / 8;                      // scales per wave: 4 or 8
-  static constexpr int NR = HG == 4 ? 3 : 2;              // LDS tile slots = tiles staged in registers
-};
-
-template <int HG>
 struct FDSmem {
-  using C = FDCfg<HG>;
-  uint8_t ring[C::NR][C::TFB + C::TT * 4];    // tile, then its per-token scales
-  int32_t sl[kChunkF + C::TT];                // the chunk's slots, -1 padded
-  bf16x8 pex[HG][C::KS][64];                  // P^T operands: head group, K step, lane
-  float m0[C::TB][64];                        // largest logit of the first tile, by token block
-  float fin_m[C::TB][64], fin_l[C::TB][64];   // per head and token block, after the last tile
+  uint8_t ring[3][kTFBytes + kTF * 4];        // tile, then its 32 per-token scales
+  int32_t sl[kChunkF + kTF];                  // the chunk's slots, -1 padded
+  bf16x8 pex[4][64];                          // P^T operands: head group, lane
+  float m0[2][64];                            // largest logit of the first tile, by token block
+  float fin_m[2][64], fin_l[2][64];           // per head and token block, after the last tile
   int32_t redo;
 };
 
-template <int HG>
 __global__ __launch_bounds__(kNTF) void mla_fp8d_kernel(MlaParams p) {
-  using C = FDCfg<HG>;
-  constexpr int TB = C::TB, TT = C::TT, KS = C::KS, TFB = C::TFB, NLD = C::NLD, EW = C::EW, SPW = C::SPW;
-  using Sm = FDSmem<HG>;
-  __shared__ __attribute__((aligned(16))) Sm sm;
+  __shared__ __attribute__((aligned(16))) FDSmem sm;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int hg = wave % HG, tb = wave / HG;
-  // Blocks go to the 8 XCDs round-robin.  With 8 rows or more the chunks (and head parts) of
-  // row r run on XCD r % 8, so the row's q and rows are read from HBM into one L2; with fewer
-  // rows they spread.  A row has HS head parts (HS = 1 when a workgroup takes every head).
-  const int HS = HG == 4 ? 1 : p.H / (16 * HG);
-  const int U = p.n_split * HS;                   // workgroups per row
-  int r, rem;
+  const int hg = wave & 3, tb = wave >> 2;
+  // Blocks go to the 8 XCDs round-robin.  With 8 rows or more the chunks of row r run on XCD
+  // r % 8, so the row's q is read from HBM into one L2; with fewer rows they spread.
+  int r, split;
   if (p.rows >= 8) {
     const int xcd = blockIdx.x & 7, jx = blockIdx.x >> 3;
-    r = 8 * (jx / U) + xcd;
-    rem = jx - (jx / U) * U;
+    r = 8 * (jx / p.n_split) + xcd;
+    split = jx - (jx / p.n_split) * p.n_split;
     if (r >= p.rows) return;
   } else {
-    r = blockIdx.x / U;
-    rem = blockIdx.x - r * U;
+    r = blockIdx.x / p.n_split;
+    split = blockIdx.x - r * p.n_split;
   }
-  const int split = rem / HS, hpart = rem - split * HS;
-  const int hbase = 16 * HG * hpart;              // first head of this workgroup
   const int j0 = split * p.chunk;
   const int j1 = min(p.k, j0 + p.chunk);
-  const int ntiles = j1 > j0 ? (j1 - j0 + TT - 1) / TT : 0;
+  const int ntiles = j1 > j0 ? (j1 - j0 + kTF - 1) / kTF : 0;
   const int32_t* sl = p.slots + (int64_t)r * p.k;
-  const int ngroups = min(HG, (p.H - hbase) / 16);   // live head groups (H is a multiple of 16)
+  const int ngroups = min(4, p.H / 16);           // live head groups (H is a multiple of 16)
   const bool s_active = hg < ngroups;             // this wave's S^T head group exists
   const int m16 = lane & 15, grp = lane >> 4;
 
@@ -751,14 +723,14 @@ __global__ __launch_bounds__(kNTF) void mla_fp8d_kernel(MlaParams p) {
   // for the slots (the older loads) leaves q in flight through the barrier and the first tile
   // loads.
   static_assert(kChunkF <= 4 * kNTF, "one round of slot loads");
-  const int span = ntiles * TT;
+  const int span = ntiles * kTF;
   int32_t slv[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) slv[u] = sl[min(j0 + u * kNTF + (int)threadIdx.x, p.k - 1)];
   __builtin_amdgcn_sched_barrier(0);   // (the slot loads stay ahead of q's)
   bf16x8 qf[kStepsF];
   {
-    const int qhead = min(hbase + hg * 16 + m16, p.H - 1);
+    const int qhead = min(hg * 16 + m16, p.H - 1);
     const bf16x8* qrow = (const bf16x8*)((const __bf16*)p.q + ((int64_t)r * p.H + qhead) * kRowDim);
 #pragma unroll
     for (int u = 0; u < kStepsF / 2; ++u)
@@ -771,35 +743,32 @@ __global__ __launch_bounds__(kNTF) void mla_fp8d_kernel(MlaParams p) {
     if (e < span) sm.sl[e] = j0 + e < j1 ? dbg_slot(p.dbg, slv[u], p.num_slots) : -1;
   }
   if (threadIdx.x == 0) sm.redo = 0;
-  if (!s_active && tb == 0)                       // head groups past the head count: P = 0
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) sm.pex[hg][ks][lane] = bf16x8{};
+  if (!s_active && tb == 0) sm.pex[hg][lane] = bf16x8{};   // head groups past the head count: P = 0
   lds_barrier();
 
-  // ---- staging of tile v: every wave issues the same NLD + 2 loads per tile.  Load c < NLD of
-  // wave w reads the tile's 16-byte pieces q = 64(w + 8c) + lane (1 KiB of whole rows each),
-  // load NLD the 4 EW bytes at tile offset 8192 NLD + 256 EW w + 4 EW lane, the last one the
-  // scale of token SPW w + lane % SPW.  Tile offset o holds token o / 576 at LDS slot
-  // (o % 576) / 16, i.e. the row's logical piece slot ^ fp8_swz(token).  Tiles past the chunk
-  // re-read row 0 and are never used, so every step issues the same loads.
-  using EWord = typename std::conditional<EW == 1, uint32_t, u32x2>::type;
+  // ---- staging of tile v: every wave issues the same four loads per tile.  Loads 0 and 1 of
+  // wave w read the tile's 16-byte pieces q = 64(w + 8c) + lane (1 KiB of whole rows each), load
+  // 2 the 4 bytes at tile offset 16384 + 256w + 4 lane, load 3 the scale of token 4w + lane % 4.
+  // Tile offset o holds token o / 576 at LDS slot (o % 576) / 16, i.e. the row's logical piece
+  // slot ^ fp8_swz(token).  Tiles past the chunk re-read row 0 and are never used, so every
+  // step issues the same loads.
   struct Stage {
-    u32x4 d[NLD];
-    EWord e;
+    u32x4 d[2];
+    uint32_t e;
     float sc;
-    uint32_t dead;   // bit c: load c belongs to a skipped token (bit NLD: load NLD)
+    uint32_t dead;   // bit c: load c belongs to a skipped token
   };
-  const int e_off = 8192 * NLD + 256 * EW * wave + 4 * EW * lane;   // tile offset of load NLD
+  const int e_off = kTFBytes - 2048 + 256 * wave + 4 * lane;   // tile offset of load 2
   auto row_src = [&](int o, int32_t sv) {                       // global address of tile offset o
     const int t = o / kRowDim, w = o - t * kRowDim;
     return (const uint8_t*)p.kv + (int64_t)(sv < 0 ? 0 : sv) * kRowDim + ((((w >> 4) ^ fp8_swz(t)) << 4) | (w & 15));
   };
-  auto load_tile = [&](const Sm* __restrict__ rd, Stage& st, int v) {
+  auto load_tile = [&](const FDSmem* __restrict__ rd, Stage& st, int v) {
     const bool real = v < ntiles;
-    const int vb = (real ? v : 0) * TT;           // (a tile past the chunk reads entries it ignores)
+    const int vb = (real ? v : 0) * kTF;          // (a tile past the chunk reads entries it ignores)
     uint32_t dead = 0u;
 #pragma unroll
-    for (int c = 0; c < NLD; ++c) {
+    for (int c = 0; c < 2; ++c) {
       const int o = ((wave + 8 * c) * 64 + lane) * 16;
       const int32_t sl_t = rd->sl[vb + o / kRowDim];
       const int32_t sv = real ? sl_t : 0;
@@ -809,31 +778,31 @@ __global__ __launch_bounds__(kNTF) void mla_fp8d_kernel(MlaParams p) {
     {
       const int32_t sl_t = rd->sl[vb + e_off / kRowDim];
       const int32_t sv = real ? sl_t : 0;
-      dead |= (sv < 0 ? 1u : 0u) << NLD;
-      st.e = *(const EWord*)row_src(e_off, sv);
+      dead |= (sv < 0 ? 4u : 0u);
+      st.e = *(const uint32_t*)row_src(e_off, sv);
     }
-    const int32_t sl_s = rd->sl[vb + SPW * wave + (lane & (SPW - 1))];
+    const int32_t sl_s = rd->sl[vb + 4 * wave + (lane & 3)];
     const int32_t ss = real ? sl_s : 0;
     st.sc = p.kv_scale[ss < 0 ? 0 : ss];
     st.dead = dead;
   };
   auto store_tile = [&](const Stage& st, uint8_t* __restrict__ dst) {
 #pragma unroll
-    for (int c = 0; c < NLD; ++c) {
+    for (int c = 0; c < 2; ++c) {
       const int o = ((wave + 8 * c) * 64 + lane) * 16;
       *(u32x4*)(dst + o) = (st.dead >> c) & 1u ? u32x4{0u, 0u, 0u, 0u} : st.d[c];
     }
-    *(EWord*)(dst + e_off) = (st.dead >> NLD) & 1u ? EWord{} : st.e;
-    if (lane < SPW) *(float*)(dst + TFB + 4 * (SPW * wave + lane)) = st.sc;
+    *(uint32_t*)(dst + e_off) = st.dead & 4u ? 0u : st.e;
+    if (lane < 4) *(float*)(dst + kTFBytes + 4 * (4 * wave + lane)) = st.sc;
   };
 
-  Stage X, Y, Z;   // (Z: three-deep staging only)
+  Stage X, Y, Z;
   load_tile(&sm, X, 0);
   load_tile(&sm, Y, 1);
-  if constexpr (C::NR == 3) load_tile(&sm, Z, 2);
+  load_tile(&sm, Z, 2);
 
   // P.V accumulators: head group g, output block db; lane holds O^T[64w + 16db + 4grp + j][16g + m16]
-  f32x4 o[HG][kDBlocksF];
+  f32x4 o[4][kDBlocksF];
   const float scale2 = p.sm_scale * kLog2e;
   float ref = 0.f;           // R of this lane's head
   float m_seen = -INFINITY;  // the head's largest logit in this wave's token block
@@ -868,11 +837,11 @@ __global__ __launch_bounds__(kNTF) void mla_fp8d_kernel(MlaParams p) {
     return acc0 + acc1;
   };
   // lane holds head 16hg + m16, tokens 16tb + 4grp + j: logits (scale folded), -inf if skipped
-  auto logits = [&](const Sm* __restrict__ rd, const uint8_t* __restrict__ T, int v, const f32x4& sacc,
+  auto logits = [&](const FDSmem* __restrict__ rd, const uint8_t* __restrict__ T, int v, const f32x4& sacc,
                     float (&z)[4], float (&sc)[4]) {
     const int t0 = 16 * tb + 4 * grp;
-    const int32_t* slt = rd->sl + v * TT + t0;
-    const f32x4 sc4 = *(const f32x4*)(T + TFB + 4 * t0);
+    const int32_t* slt = rd->sl + v * kTF + t0;
+    const f32x4 sc4 = *(const f32x4*)(T + kTFBytes + 4 * t0);
     float tmax = -INFINITY;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -882,7 +851,7 @@ __global__ __launch_bounds__(kNTF) void mla_fp8d_kernel(MlaParams p) {
     }
     return lanes4_max(tmax);   // over the block's 16 tokens
   };
-  auto publish = [&](Sm* __restrict__ rd, const float (&z)[4], const float (&sc)[4]) {
+  auto publish = [&](FDSmem* __restrict__ rd, const float (&z)[4], const float (&sc)[4]) {
     bf16x4 pb;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -890,45 +859,35 @@ __global__ __launch_bounds__(kNTF) void mla_fp8d_kernel(MlaParams p) {
       l_run += pe;
       pb[j] = (__bf16)(pe * sc[j]);
     }
-    // token block tb is half tb % 2 of the P^T operand of K step tb / 2
-    *(bf16x4*)((uint8_t*)&rd->pex[hg][tb >> 1][lane] + 8 * (tb & 1)) = pb;
+    *(bf16x4*)((uint8_t*)&rd->pex[hg][lane] + 8 * tb) = pb;
   };
-  auto pv_tile = [&](const Sm* __restrict__ rd, const uint8_t* __restrict__ T) {
+  auto pv_tile = [&](const FDSmem* __restrict__ rd, const uint8_t* __restrict__ T) {
+    u32x2 raw[kDBlocksF];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      // tokens 32ks + tau share the swizzle of tau, so K step ks reads 32ks rows further on
-      u32x2 raw[kDBlocksF];
+    for (int db = 0; db < kDBlocksF; ++db)
+      raw[db] = __builtin_bit_cast(
+          u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)(T + v_base[db])));
+    bf16x8 av[kDBlocksF];
 #pragma unroll
-      for (int db = 0; db < kDBlocksF; ++db)
-        raw[db] = __builtin_bit_cast(
-            u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                       (__attribute__((address_space(3))) i32x2*)(T + v_base[db] + ks * 32 * kRowDim)));
-      bf16x8 av[kDBlocksF];
+    for (int db = 0; db < kDBlocksF; ++db) av[db] = fp8x8_to_bf16x8(raw[db][0], raw[db][1]);
 #pragma unroll
-      for (int db = 0; db < kDBlocksF; ++db) av[db] = fp8x8_to_bf16x8(raw[db][0], raw[db][1]);
+    for (int g = 0; g < 4; ++g) {
+      const bf16x8 pg = rd->pex[g][lane];
 #pragma unroll
-      for (int g = 0; g < HG; ++g) {
-        const bf16x8 pg = rd->pex[g][ks][lane];
-#pragma unroll
-        for (int db = 0; db < kDBlocksF; ++db)
-          o[g][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[db], pg, o[g][db], 0, 0, 0);
-      }
-      if (ks + 1 < KS) __builtin_amdgcn_sched_barrier(0);   // one K step's operands live at a time
+      for (int db = 0; db < kDBlocksF; ++db) o[g][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[db], pg, o[g][db], 0, 0, 0);
     }
   };
   // one tile (v, in ring slot T): S^T, the first tile's reference, P, then P.V
-  auto tile = [&](Sm* __restrict__ rd, const uint8_t* __restrict__ T, int v, bool first) {
+  auto tile = [&](FDSmem* __restrict__ rd, const uint8_t* __restrict__ T, int v, bool first) {
     float z[4], sc[4];
     float tmax = -INFINITY;
     if (s_active) tmax = logits(rd, T, v, s_tile(T), z, sc);
     if (first) {
-      // the reference: the first tile's largest logit over its token blocks (0 without one)
+      // the reference: the first tile's largest logit over both token blocks (0 without one)
       if (s_active && grp == 0) rd->m0[tb][hg * 16 + m16] = tmax;
       lds_barrier();
       if (s_active) {
-        float m0 = rd->m0[0][hg * 16 + m16];
-#pragma unroll
-        for (int b = 1; b < TB; ++b) m0 = fmaxf(m0, rd->m0[b][hg * 16 + m16]);
+        const float m0 = fmaxf(rd->m0[0][hg * 16 + m16], rd->m0[1][hg * 16 + m16]);
         ref = m0 == -INFINITY ? 0.f : m0;
       }
     }
@@ -949,40 +908,25 @@ __global__ __launch_bounds__(kNTF) void mla_fp8d_kernel(MlaParams p) {
   // partial.
   auto run_pass = [&](bool first) {
 #pragma unroll
-    for (int g = 0; g < HG; ++g)
+    for (int g = 0; g < 4; ++g)
 #pragma unroll
       for (int db = 0; db < kDBlocksF; ++db) o[g][db] = f32x4{0.f, 0.f, 0.f, 0.f};
     l_run = 0.f;
     store_tile(X, sm.ring[0]);
     lds_barrier();   // tile 0 landed
-    if constexpr (C::NR == 3) {
-      for (int v = 0; v < ntiles; v += 3) {
-        load_tile(&sm, X, v + 3);
-        tile(&sm, sm.ring[0], v, first && v == 0);
-        store_tile(Y, sm.ring[1]);
-        lds_barrier();   // tile v + 1 landed; tile v and its P are no longer read
-        load_tile(&sm, Y, v + 4);
-        if (v + 1 < ntiles) tile(&sm, sm.ring[1], v + 1, false);
-        store_tile(Z, sm.ring[2]);
-        lds_barrier();   // tile v + 2 landed
-        load_tile(&sm, Z, v + 5);
-        if (v + 2 < ntiles) tile(&sm, sm.ring[2], v + 2, false);
-        store_tile(X, sm.ring[0]);
-        lds_barrier();   // tile v + 3 landed
-      }
-    } else {
-      // 64-token tiles: two staged in registers (v + 1 waiting for its store, v + 2 in flight)
-      // and two LDS slots
-      for (int v = 0; v < ntiles; v += 2) {
-        load_tile(&sm, X, v + 2);
-        tile(&sm, sm.ring[0], v, first && v == 0);
-        store_tile(Y, sm.ring[1]);
-        lds_barrier();   // tile v + 1 landed; tile v and its P are no longer read
-        load_tile(&sm, Y, v + 3);
-        if (v + 1 < ntiles) tile(&sm, sm.ring[1], v + 1, false);
-        store_tile(X, sm.ring[0]);
-        lds_barrier();   // tile v + 2 landed
-      }
+    for (int v = 0; v < ntiles; v += 3) {
+      load_tile(&sm, X, v + 3);
+      tile(&sm, sm.ring[0], v, first && v == 0);
+      store_tile(Y, sm.ring[1]);
+      lds_barrier();   // tile v + 1 landed; tile v and its P are no longer read
+      load_tile(&sm, Y, v + 4);
+      if (v + 1 < ntiles) tile(&sm, sm.ring[1], v + 1, false);
+      store_tile(Z, sm.ring[2]);
+      lds_barrier();   // tile v + 2 landed
+      load_tile(&sm, Z, v + 5);
+      if (v + 2 < ntiles) tile(&sm, sm.ring[2], v + 2, false);
+      store_tile(X, sm.ring[0]);
+      lds_barrier();   // tile v + 3 landed
     }
     // does some head's largest logit lie outside R +- 64?
     if (s_active) {
@@ -998,8 +942,7 @@ __global__ __launch_bounds__(kNTF) void mla_fp8d_kernel(MlaParams p) {
   {
     float mx = -INFINITY;
     if (s_active) {
-#pragma unroll
-      for (int b = 0; b < TB; ++b) mx = fmaxf(mx, sm.fin_m[b][hg * 16 + m16]);
+      mx = fmaxf(sm.fin_m[0][hg * 16 + m16], sm.fin_m[1][hg * 16 + m16]);
       if (mx > -INFINITY && (mx > ref + kRefMargin || mx < ref - kRefMargin)) sm.redo = 1;
     }
     __syncthreads();
@@ -1007,24 +950,20 @@ __global__ __launch_bounds__(kNTF) void mla_fp8d_kernel(MlaParams p) {
       ref = mx > -INFINITY ? mx : 0.f;
       load_tile(&sm, X, 0);
       load_tile(&sm, Y, 1);
-      if constexpr (C::NR == 3) load_tile(&sm, Z, 2);
+      load_tile(&sm, Z, 2);
       run_pass(false);
     }
   }
 
   // ---- output: each wave writes its 64 values of every head
 #pragma unroll
-  for (int g = 0; g < HG; ++g) {
+  for (int g = 0; g < 4; ++g) {
     if (g >= ngroups) break;
-    const int hl = g * 16 + m16, head = hbase + hl;
+    const int head = g * 16 + m16;
+    const float mh = fmaxf(sm.fin_m[0][head], sm.fin_m[1][head]);
+    const float lh = sm.fin_l[0][head] + sm.fin_l[1][head];
     // R of this head as its S^T waves used it (recomputed from what they published)
-    float mh = sm.fin_m[0][hl], lh = sm.fin_l[0][hl], m0 = sm.m0[0][hl];
-#pragma unroll
-    for (int b = 1; b < TB; ++b) {
-      mh = fmaxf(mh, sm.fin_m[b][hl]);
-      lh += sm.fin_l[b][hl];
-      m0 = fmaxf(m0, sm.m0[b][hl]);
-    }
+    const float m0 = fmaxf(sm.m0[0][head], sm.m0[1][head]);
     const float rh = sm.redo ? (mh > -INFINITY ? mh : 0.f) : (m0 == -INFINITY ? 0.f : m0);
     const float inv = lh > 0.f ? 1.f / lh : 0.f;
     float* dst;
@@ -1715,14 +1654,6 @@ __global__ __launch_bounds__(256) void mla_combine_few_kernel(CombineParams p) {
 
 }  // namespace
 
-// fp8 rows, 64 heads, 128-255 query rows, no split, a selection one workgroup stages: one
-// workgroup per head half of a row (mla_fp8d_kernel<2>), 256-511 workgroups and no merge.  (At
-// 128 rows this beats two chunks per row plus the merge, 239 against 244 us per fp8 verify step;
-// from 256 rows one workgroup per row is faster, 402 against 421 us at 64 x 4 rows.)
-bool mla_fp8_head_halves(int rows, int H, int k, dsa_dtype_t kv_dtype, int n_split) {
-  return kv_dtype == DSA_FP8_E4M3FN && H == 64 && rows >= 128 && rows < 256 && n_split == 1 && k <= kChunkF;
-}
-
 bool mla_uses_narrow(int rows, int H, dsa_dtype_t kv_dtype) {
   return kv_dtype == DSA_BF16 && H % 16 == 0 && H <= 64 && (int64_t)rows * (H / 16) <= kFewHeadRows;
 }
@@ -1734,8 +1665,6 @@ int mla_default_split(int rows, int H, int k, dsa_dtype_t kv_dtype) {
     const int cap = per > 0 ? std::max(1, 256 / per) : 1;
     return std::max(1, std::min((k + kTN - 1) / kTN, cap));
   }
-  // fp8 rows where head halves fill the compute units: no split (mla_fp8d_kernel<2>, no merge)
-  if (mla_fp8_head_halves(rows, H, k, kv_dtype, 1)) return 1;
   // about one workgroup per compute unit, at least 64 selected rows per chunk, and for fp8 rows
   // at most kChunkF (the fp8 ring kernel's staging limit)
   int ns = 256 / (rows > 0 ? rows : 1);
@@ -1763,11 +1692,9 @@ hipError_t launch_mla(const MlaParams& p0, dsa_dtype_t q_dtype, dsa_dtype_t kv_d
   p.chunk = chunk;
   const dim3 grid((unsigned)p.n_split, (unsigned)p.rows);
   if (kv_dtype == DSA_FP8_E4M3FN) {
-    const unsigned rws = (unsigned)(p.rows >= 8 ? (p.rows + 7) / 8 * 8 : p.rows);
-    if (mla_fp8_head_halves(p.rows, p.H, p.k, kv_dtype, p.n_split))
-      hipLaunchKernelGGL(mla_fp8d_kernel<2>, dim3(rws * 2), dim3(kNTF), 0, s, p);
-    else if (chunk <= kChunkF)
-      hipLaunchKernelGGL(mla_fp8d_kernel<4>, dim3(rws * (unsigned)p.n_split), dim3(kNTF), 0, s, p);
+    if (chunk <= kChunkF)
+      hipLaunchKernelGGL(mla_fp8d_kernel, dim3((unsigned)((p.rows >= 8 ? (p.rows + 7) / 8 * 8 : p.rows) * p.n_split)),
+                         dim3(kNTF), 0, s, p);
     else hipLaunchKernelGGL(mla_fp8_kernel, grid, dim3(kNT), 0, s, p);
   }
   else if (mla_uses_narrow(p.rows, p.H, kv_dtype) && chunk <= kChunkN) {

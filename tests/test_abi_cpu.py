@@ -153,13 +153,7 @@ def test_mla_workspace_sizes(L):
     assert L.dsa_sparse_mla_default_split(4096, 1, 64, 2048, dsa.DSA_BF16) == 1
     assert L.dsa_sparse_mla_default_split(4096, 1, 64, 2048, dsa.DSA_FP8_E4M3FN) == 1
     assert L.dsa_sparse_mla_default_split(4096, 1, 64, 4096, dsa.DSA_FP8_E4M3FN) == 2
-    # 128-255 fp8 rows of 64 heads: one workgroup per head half of a row, no split; other head
-    # counts and 64 rows split the selection in two
-    assert L.dsa_sparse_mla_default_split(64, 2, 64, 2048, dsa.DSA_FP8_E4M3FN) == 1
-    assert L.dsa_sparse_mla_workspace_size(64, 2, 64, 2048, 0, dsa.DSA_BF16, dsa.DSA_FP8_E4M3FN) == 0
-    assert L.dsa_sparse_mla_default_split(64, 2, 32, 2048, dsa.DSA_FP8_E4M3FN) == 2
-    assert L.dsa_sparse_mla_default_split(32, 2, 64, 2048, dsa.DSA_FP8_E4M3FN) == 4
-    assert L.dsa_sparse_mla_default_split(64, 4, 64, 2048, dsa.DSA_FP8_E4M3FN) == 1
+    assert L.dsa_sparse_mla_default_split(64, 2, 64, 2048, dsa.DSA_FP8_E4M3FN) == 2
 
 
 def test_decode_step_workspace_and_rejects(L):

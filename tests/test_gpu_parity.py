@@ -200,13 +200,6 @@ MLA_CASES = [
     # fp8 with fewer heads than the wide kernel's four groups, partial last tiles
     ("c5", [1500], 200, 32, 3, 0.1),
     ("c5", [1500], 200, 48, 0, 0.0),
-    # fp8, 64 heads, at least 128 rows and no split: one workgroup per head half of a row with
-    # 64-token tiles (the verify workload's launch), skipped slots, a partial last tile, a row
-    # count that leaves part of the last group of 8 rows empty
-    ("c5", [300] * 64, 512, 64, 1, 0.0),
-    ("c5", [2500] * 64, 2048, 64, 0, 0.05),
-    ("c5", [300] * 64, 200, 64, 1, 0.1),
-    ("c5", [900] * 68, 1000, 64, 0, 0.0),
 ]
 
 
@@ -236,7 +229,7 @@ def test_sparse_mla_empty_selection_and_single_row():
 
 
 @pytest.mark.parametrize("name,ns,qps", [("c2", 1, 1), ("c2", 2, 1), ("c2", 1, 5), ("c2", 2, 5), ("c5", 1, 1),
-                                         ("c5", 2, 1), ("c5", 1, 128)])
+                                         ("c5", 2, 1)])
 def test_sparse_mla_wide_logit_range(name, ns, qps):
     """Heads whose largest logit lies far above or far below the kernels' first-tile reference.
 
@@ -248,8 +241,7 @@ def test_sparse_mla_wide_logit_range(name, ns, qps):
     a token's contribution carries a relative rounding of up to 2^-9; the boosted row's large
     norm makes that visible in every head of row 0, so the output bound there is relative to
     each head's output scale (2^-8), while the direction (cosine) and lse keep the strict bar.
-    One bf16 query row runs on the 16-head kernel, five on the 64-head one; 128 fp8 rows run on
-    the head-half kernel."""
+    One bf16 query row runs on the 16-head kernel, five on the 64-head one."""
     cfg, inp, _ = _case(name, [3000], seed=106, top_k=512, q_per_seq=qps)
     rng = np.random.default_rng(12)
     slots = _random_slots(cfg, rng, 512)
