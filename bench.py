@@ -663,8 +663,8 @@ def main():
         copy_calibration()
         return
     if args.gpus != 1:
-        print(f"bench.py runs on exactly one GPU (got --gpus {args.gpus}): the path is single-GPU; "
-              "how it would shard over several GPUs is described in DESIGN.md", file=sys.stderr)
+        print(f"bench.py runs on exactly one GPU (got --gpus {args.gpus}): the library computes one "
+              "GPU's share of the work and has no multi-GPU path", file=sys.stderr)
         sys.exit(2)
     extras = [e for e in args.extras.split(",") if e and e != args.config]
     for n in [args.config] + extras:
