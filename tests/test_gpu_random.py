@@ -7,7 +7,10 @@ selection up to ties at the k-th score.
 Each configuration draws the dtype family (f32, bf16, fp8 caches), batch, rows per sequence
 (decode, verify and a few many-row chunks), ragged lengths (some below k, so rows are padded
 with -1), page size (powers of two, sizes that 16 does not divide, page size 1), k and the MLA
-head count from a fixed seed, so every run checks the same cases."""
+head count from a fixed seed, so every run checks the same cases (the first DSA_RANDOM_CASES of the
+sequence, 96 by default)."""
+import os
+
 import numpy as np
 import pytest
 
@@ -17,7 +20,7 @@ from tests.test_gpu_parity import _check_staged
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 96
+N_CASES = int(os.environ.get("DSA_RANDOM_CASES", "96"))   # a longer sweep: set it higher
 
 
 def draw_case(i):
