@@ -45,6 +45,22 @@ def test_debug_build_matches_release_on_valid_inputs(dbg_lib, name, lens):
             got[key].cpu().numpy(), ref[key].cpu().numpy(), equal_nan=True)), key
 
 
+@pytest.mark.parametrize("i", range(24))
+def test_debug_build_matches_release_on_random_steps(dbg_lib, i):
+    """The first 24 configurations of the seeded step sweep (tests/test_gpu_random.py): every
+    dtype family, ragged lengths below k, page sizes 1-128, verify and chunk rows."""
+    from tests.test_gpu_random import draw_case
+    name, lens, kw = draw_case(i)
+    cfg, _, t = _case(name, lens, seed=3000 + i, **kw)
+    ref = run_step(cfg, t)
+    with dsa.using_library(dbg_lib):
+        got = run_step(cfg, t)
+        assert dsa.debug_check() == 0
+    for key in ("out", "lse", "idx", "slots"):
+        assert torch.equal(got[key], ref[key]), key
+    assert np.array_equal(got["scores"].cpu().numpy(), ref["scores"].cpu().numpy(), equal_nan=True)
+
+
 def test_debug_flags_page_id_out_of_range(dbg_lib):
     cfg, _, t = _case("c2", [5000], seed=402)
     pages = cfg.num_slots // cfg.page_size
