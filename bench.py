@@ -85,6 +85,9 @@ def parse():
     ap.add_argument("--summarize-mfma", metavar="DIR",
                     help="print the per-kernel matrix-core use of a rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES "
                          "GRBM_GUI_ACTIVE SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F8 run")
+    ap.add_argument("--summarize-sq", nargs="+", metavar="DIR",
+                    help="print per-SIMD instruction and cycle counts of the indexer and MLA kernels from "
+                         "rocprofv3 --pmc runs of SQ counters (one or more runs of the same workload)")
     return ap.parse_args()
 
 
@@ -167,6 +170,39 @@ def summarize_mfma(d):
             continue
         util = busy[k] / (gui[k] / xcds * simds) if gui.get(k) else float("nan")
         print(f"| `{k}` | {100 * util:.1f}% | {bf16.get(k, 0) * 512:.3e} | {f8.get(k, 0) * 512:.3e} |")
+
+
+def summarize_sq(dirs):
+    """Per dispatch (averaged over the run's dispatches of a kernel), per SIMD: the SQ counters
+    summed over the chip.  *_CYCLES and ACTIVE/WAIT counters are in units of 4 cycles per wave
+    (quad-cycles) except SQ_BUSY_CYCLES and SQ_VALU_MFMA_BUSY_CYCLES; instruction counts are per
+    wave instruction."""
+    import collections
+    simds = 1024
+    per = collections.defaultdict(dict)
+    names = set()
+    for d in dirs:
+        for r in _csv_rows(d, "counter_collection.csv"):
+            names.add(r["Counter_Name"])
+        for c in sorted(names):
+            for k, v in _per_dispatch(d, c).items():
+                per[k].setdefault(c, v)
+    cols = sorted(names)
+    print("| kernel | " + " | ".join(cols) + " |")
+    print("|---|" + "---|" * len(cols))
+    for k in sorted(per):
+        if not (k.startswith("indexer") or k.startswith("mla")):
+            continue
+        vals = []
+        for c in cols:
+            v = per[k].get(c)
+            if v is None:
+                vals.append("")
+            elif c in ("GRBM_GUI_ACTIVE", "SQ_WAVES", "SQ_BUSY_CYCLES"):
+                vals.append(f"{v:.4g}")
+            else:
+                vals.append(f"{v / simds:.4g}")
+        print(f"| `{k}` | " + " | ".join(vals) + " |")
 
 
 # ---------------------------------------------------------------------------------------------
@@ -655,6 +691,9 @@ def main():
         return
     if args.summarize_mfma:
         summarize_mfma(args.summarize_mfma)
+        return
+    if args.summarize_sq:
+        summarize_sq(args.summarize_sq)
         return
     if args.cpu_one_core_child:
         print(json.dumps(cpu_sample(args.config, args.cpu_seconds)))
