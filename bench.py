@@ -677,7 +677,8 @@ def measure_up_projection(rows, H, dev, stream, evict, KS):
     us = ms * 1e3
     return dict(us=round(us, 3), bytes=by, GBps=round(by / (us * 1e-6) / 1e9, 1), flops=fl,
                 TFLOPs=round(fl / (us * 1e-6) / 1e12, 1), rows=rows, v_dim=UP_V_DIM,
-                d_model=UP_D_MODEL, kernels=["up_gemm_kernel", "up_reduce_kernel"],
+                d_model=UP_D_MODEL,
+                kernels=["up_gemv_kernel"] if rows <= 2 else ["up_gemm_kernel", "up_reduce_kernel"],
                 timing="hip-graph of launches, weight sets cycled")
 
 

@@ -23,6 +23,7 @@
 //   * v: one group of tiles per head (A = o[:, h, :], B = W_UV[h], K = 512).  y: K = H * Dv is
 //     split over workgroups when the tiles alone would not fill the GPU; up_reduce_kernel adds
 //     the partial sums in split order, so the result is deterministic.
+// One or two rows take up_gemv_kernel instead (below): matrix-vector products on the vector ALU.
 #include "dsa_internal.hpp"
 
 namespace dsa {
@@ -242,6 +243,56 @@ __global__ __launch_bounds__(kGT) void up_gemm_kernel(GemmArgs g) {
   }
 }
 
+// One or two rows (decode): C[g][r][n] = sum_k A[g][r][k] * B[g][n][k] as a matrix-vector product
+// on the vector ALU, where the matrix core would compute 16 rows for every one used and only the
+// weight stream matters.  A workgroup (8 waves) stages its group's RR activation rows in LDS and
+// owns 8 columns, one per wave; lane l of a wave reads the 16-byte pieces 64i + l of its column's
+// weights (all K / 512 of them requested at once, whole 1 KiB runs per load instruction) and
+// accumulates their 8 products with the matching activations in fp32 (each fma rounds once),
+// then the wave adds its lanes' sums.  K = 512 NI with NI a power of two up to 16.
+template <int RR, int NI>
+__global__ __launch_bounds__(512) void up_gemv_kernel(GemmArgs g) {
+  constexpr int K = 512 * NI;
+  __shared__ __attribute__((aligned(16))) float as[RR * K];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int gz = blockIdx.y;
+  const float* A = g.A + gz * g.a_gs;
+  for (int e = threadIdx.x; e < RR * K / 4; e += 512) {
+    const int r = e / (K / 4), c = e - r * (K / 4);
+    *(f32x4*)&as[r * K + 4 * c] = r < g.R ? *(const f32x4*)(A + r * g.lda + 4 * c) : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const int n = blockIdx.x * 8 + wave;
+  const bool live = n < g.N;
+  const __bf16* Bn = g.B + gz * g.b_gs + (int64_t)(live ? n : 0) * g.ldb;
+  u32x4 w[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) w[i] = __builtin_nontemporal_load((const u32x4*)(Bn + 512 * i + 8 * lane));
+  __syncthreads();
+  float acc[RR];
+#pragma unroll
+  for (int r = 0; r < RR; ++r) acc[r] = 0.f;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const bf16x8 wb = __builtin_bit_cast(bf16x8, w[i]);
+#pragma unroll
+    for (int r = 0; r < RR; ++r) {
+      const f32x4 a0 = *(const f32x4*)&as[r * K + 512 * i + 8 * lane];
+      const f32x4 a1 = *(const f32x4*)&as[r * K + 512 * i + 8 * lane + 4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[r] = fmaf((float)wb[j], a0[j], acc[r]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[r] = fmaf((float)wb[4 + j], a1[j], acc[r]);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < RR; ++r) {
+    float v = acc[r];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+    if (lane == 0 && live && r < g.R) g.C[gz * g.c_gs + (int64_t)r * g.ldc + n] = v;
+  }
+}
+
 // y = sum over the K splits of the partial sums, in split order.
 __global__ __launch_bounds__(256) void up_reduce_kernel(UpProjParams p) {
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -285,9 +336,36 @@ hipError_t launch_gemm(const GemmArgs& a, int groups, hipStream_t s) {
 // K values per split of a product (a multiple of 32)
 int up_proj_kchunk(int K, int ks) { return ((K + ks - 1) / ks + 31) / 32 * 32; }
 
+// the matrix-vector path: one row with K = 512 times a power of two up to 16, or two rows up
+// to 8 (two rows of 16 would not fit the registers)
+bool up_proj_gemv(int R, int K) {
+  const int ni = K / 512;
+  return K % 512 == 0 && (ni & (ni - 1)) == 0 && ((R == 1 && ni <= 16) || (R == 2 && ni <= 8));
+}
+
+template <int RR>
+hipError_t launch_gemv_r(const GemmArgs& a, int groups, hipStream_t s) {
+  const dim3 grid((unsigned)((a.N + 7) / 8), (unsigned)groups);
+  switch (a.K / 512) {
+    case 1: hipLaunchKernelGGL((up_gemv_kernel<RR, 1>), grid, dim3(512), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((up_gemv_kernel<RR, 2>), grid, dim3(512), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((up_gemv_kernel<RR, 4>), grid, dim3(512), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((up_gemv_kernel<RR, 8>), grid, dim3(512), 0, s, a); break;
+    default:
+      if constexpr (RR == 1) hipLaunchKernelGGL((up_gemv_kernel<1, 16>), grid, dim3(512), 0, s, a);
+      break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemv(const GemmArgs& a, int groups, hipStream_t s) {
+  return a.R == 1 ? launch_gemv_r<1>(a, groups, s) : launch_gemv_r<2>(a, groups, s);
+}
+
 }  // namespace
 
 int up_proj_ksplit(int R, int Dm, int K) {
+  if (up_proj_gemv(R, K)) return 1;   // (every column is one wave's whole sum)
   // enough workgroups for one full round (tiles of up to 32 rows fit two workgroups per compute
   // unit), splits of at least 512 values, partial sums of at most a quarter of the weight bytes
   // (2 * ks * R * Dm floats against Dm * K bf16), at most 16 splits; every split non-empty
@@ -323,7 +401,7 @@ hipError_t launch_up_proj(const UpProjParams& p, hipStream_t s) {
   v.K = kVDim;
   v.k_chunk = kVDim;
   v.ksplit = 1;
-  hipError_t e = launch_gemm(v, p.H, s);
+  hipError_t e = up_proj_gemv(p.R, kVDim) ? launch_gemv(v, p.H, s) : launch_gemm(v, p.H, s);
   if (e != hipSuccess) return e;
   // y (or its K-split partial sums) = v . W_O^T
   GemmArgs y{};
@@ -342,7 +420,7 @@ hipError_t launch_up_proj(const UpProjParams& p, hipStream_t s) {
   y.K = K;
   y.k_chunk = up_proj_kchunk(K, p.ksplit);
   y.ksplit = p.ksplit;
-  e = launch_gemm(y, 1, s);
+  e = up_proj_gemv(p.R, K) && p.ksplit == 1 ? launch_gemv(y, 1, s) : launch_gemm(y, 1, s);
   if (e != hipSuccess || p.ksplit == 1) return e;
   const int64_t total = (int64_t)p.R * p.Dm;
   hipLaunchKernelGGL(up_reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, p);

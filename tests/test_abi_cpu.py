@@ -236,6 +236,9 @@ def test_up_projection_rejects(L, R, H, Dv, Dm, ptrs, ws, status):
 
 def test_up_projection_workspace_size(L):
     # v [R, H, Dv] f32, plus K-split partials [ksplit, R, Dm] f32 when the rows leave the GPU idle
+    # (one or two rows take the vector path, whose columns are whole sums: no partials)
     assert L.dsa_latent_up_projection_workspace_size(128, 64, 128, 6144) >= 128 * 64 * 128 * 4
-    assert L.dsa_latent_up_projection_workspace_size(1, 64, 128, 6144) > 64 * 128 * 4
+    assert L.dsa_latent_up_projection_workspace_size(4, 64, 128, 6144) > 4 * 64 * 128 * 4
+    assert L.dsa_latent_up_projection_workspace_size(1, 64, 128, 6144) == 64 * 128 * 4
+    assert L.dsa_latent_up_projection_workspace_size(2, 16, 128, 6144) == 2 * 16 * 128 * 4
     assert L.dsa_latent_up_projection_workspace_size(0, 64, 128, 6144) == 0

@@ -1,8 +1,9 @@
 """The latent up-projection after attention (dsa_latent_up_projection) against the fp64 oracle.
 
-Pass criterion (derived from the arithmetic, the pages state none for this step): the f32
-activations enter the bf16 matrix cores as hi + lo parts (2^-18 relative) and every product is
-exact in the fp32 accumulator, so per row max_m |y - y_ref| <= 1e-5 * max_m |y_ref|.
+Pass criterion (derived from the arithmetic, the pages state none for this step): on the matrix
+cores the f32 activations enter as hi + lo bf16 parts (2^-18 relative) and every product is exact
+in the fp32 accumulator; on the one- and two-row vector path every product is exact inside an
+fp32 fma that rounds once.  Either way per row max_m |y - y_ref| <= 1e-5 * max_m |y_ref|.
 """
 import numpy as np
 import pytest
@@ -46,6 +47,11 @@ CASES = [  # rows, heads, value dim, model width
     (1, 20, 96, 160),        # K = 1920 over three splits whose last 128-chunk is partial
     (50, 4, 32, 144),        # 64-row tiles, a ragged second column tile
     (300, 8, 64, 272),       # three 128-row tiles with a ragged tail, three column tiles
+    # the vector path for one and two rows (K = 512 times a power of two)
+    (2, 16, 128, 6144),      # two rows, K = 2048
+    (2, 64, 128, 1008),      # two rows, K = 8192: the matrix cores (the vector path holds up to 4096)
+    (1, 16, 64, 1008),       # one row, K = 1024
+    (2, 8, 64, 80),          # two rows, K = 512
 ]
 
 
