@@ -345,10 +345,14 @@ def test_split_invariance_gpu(ns):
 STEP_CASES = [("c1", [4096], dict()), ("c2", [6000], dict()), ("c3", [4100, 2500, 9000], dict()),
               ("c5", [5000, 3000], dict()), ("c4", [64 + 3000], dict(q_per_seq=64, top_k=512)),
               # deeper speculative verify: draft depth 3 (4 rows per sequence, fp8 caches) and 2
-              ("c5", [5000, 3000, 2100], dict(q_per_seq=4)), ("c2", [4500, 2600], dict(q_per_seq=3))]
+              ("c5", [5000, 3000, 2100], dict(q_per_seq=4)), ("c2", [4500, 2600], dict(q_per_seq=3)),
+              # the largest batch of the indexer's length-balanced key ranges (128 sequences, some
+              # below k), and a batch beyond it (200 fp8 sequences: ranges per sequence)
+              ("c3", [int(x) for x in np.random.default_rng(128).integers(100, 2600, size=128)], dict()),
+              ("c5", [int(x) for x in np.random.default_rng(200).integers(2, 2600, size=200)], dict(q_per_seq=1))]
 
 
-@pytest.mark.parametrize("name,lens,kw", STEP_CASES, ids=[c[0] for c in STEP_CASES])
+@pytest.mark.parametrize("name,lens,kw", STEP_CASES, ids=[f"{c[0]}-B{len(c[1])}" for c in STEP_CASES])
 def test_decode_step_staged(name, lens, kw):
     """Staged protocol: (1) the step's scores against the oracle; (2) its selection against the
     oracle's top-k run on the step's own f32 scores (bit-exact) and its slots against the page
