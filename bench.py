@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the DSA decode step on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c2|c2_128k|c4|c5|c5_q4|c1] [--eager]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c2|c2_128k|c4|c5|c5_q4|c5_shared|c1] [--eager]
                     [--extras c5,c2_128k] [--no-cpu-baseline]
 
 One step = one dsa_decode_step call: lightning indexer -> top-k with the fused page map ->
@@ -51,7 +51,8 @@ WORKLOAD_NAMES = {"c1": "tiny fp32 decode, 4K ctx", "c2": "single-stream decode 
                   "c3": "batch-32 ragged decode, 4K-128K ctx",
                   "c4": "4096-token chunked prefill over 64K ctx",
                   "c5": "fp8 decode, batch 64 x 2 verify rows, 64K ctx",
-                  "c5_q4": "fp8 decode, batch 64 x 4 verify rows (draft depth 3), 64K ctx"}
+                  "c5_q4": "fp8 decode, batch 64 x 4 verify rows (draft depth 3), 64K ctx",
+                  "c5_shared": "fp8 decode, batch 64 x 2 verify rows sharing one indexer query, 64K ctx"}
 
 # The batch-32 ragged workload faulted the GPU once on an earlier revision of the kernels and
 # the cause has not been shown; it is not run on the GPU until it is.

@@ -52,6 +52,9 @@ class DsaConfig:
     sm_scale: float
     page_size: int = PAGE_SIZE
     seed: int = 0
+    # the verify rows of a sequence share the indexer query and head weights of its first row
+    # (their selections then nest: row i sees one more token than row i - 1)
+    shared_index_query: bool = False
 
     @property
     def max_seq_len(self) -> int:
@@ -82,7 +85,9 @@ def base_config(name: str, seed: Optional[int] = None) -> DsaConfig:
     """The workloads, by name: c1 (tiny fp32), c2 (32K single stream), c2_128k (the
     same layer at 128K), c3 (batch 32, ragged 4K-128K), c4 (4096-token chunked prefill
     over a 64K prefix), c5 (fp8 caches, batch 64 x 2 speculative-verify rows at 64K),
-    c5_q4 (the same with 4 verify rows per sequence: a draft depth of 3)."""
+    c5_q4 (the same with 4 verify rows per sequence: a draft depth of 3), c5_shared (c5
+    whose two verify rows per sequence share one indexer query, so that they select nearly the
+    same tokens)."""
     name = name.lower()
     s = 1000 + int(name[1]) if seed is None else seed
     if name == "c1":
@@ -107,6 +112,10 @@ def base_config(name: str, seed: Optional[int] = None) -> DsaConfig:
         c = dict(common)
         c.update(key_dtype="fp8", kv_dtype="fp8")
         return DsaConfig("c5", 64, 2, [65536] * 64, **c)
+    if name == "c5_shared":    # c5 with a sequence's verify rows selecting nearly the same tokens
+        c = dict(common)
+        c.update(key_dtype="fp8", kv_dtype="fp8")
+        return DsaConfig("c5_shared", 64, 2, [65536] * 64, shared_index_query=True, **c)
     if name == "c5_q4":        # deeper speculative verify: 4 rows per sequence
         c = dict(common)
         c.update(key_dtype="fp8", kv_dtype="fp8", seed=1007 if seed is None else seed)
@@ -191,6 +200,9 @@ def make_inputs(cfg: DsaConfig, with_mla: bool = True, with_indexer: bool = True
                                   cfg.q_idx_dtype)
         r = np.random.default_rng([s, _T_W])
         out["w"] = (r.random((B, Q, cfg.idx_heads)) * cfg.w_scale).astype(np.float32)
+        if cfg.shared_index_query:
+            out["q_idx"] = np.ascontiguousarray(np.broadcast_to(out["q_idx"][:, :1], out["q_idx"].shape))
+            out["w"] = np.ascontiguousarray(np.broadcast_to(out["w"][:, :1], out["w"].shape))
         r = np.random.default_rng([s, _T_KEYS])
         out["k_cache"], out["k_scale"] = _encode(r.standard_normal((N, cfg.idx_dim)) * cfg.key_std,
                                                  cfg.key_dtype)
@@ -261,6 +273,9 @@ def make_inputs_torch(cfg: DsaConfig, device, with_mla: bool = True, with_indexe
     if with_indexer:
         out["q_idx"], _ = draw((B, Q, cfg.idx_heads, cfg.idx_dim), cfg.q_idx_std, cfg.q_idx_dtype)
         out["w"] = torch.rand((B, Q, cfg.idx_heads), generator=g, device=device) * cfg.w_scale
+        if cfg.shared_index_query:
+            out["q_idx"] = out["q_idx"][:, :1].expand_as(out["q_idx"]).contiguous()
+            out["w"] = out["w"][:, :1].expand_as(out["w"]).contiguous()
         # the caches are drawn in slabs to bound the f32 temporary
         out["k_cache"], out["k_scale"] = _draw_cache(draw, N, cfg.idx_dim, cfg.key_std, cfg.key_dtype, device)
     if with_mla:

@@ -204,7 +204,7 @@ int32_t effective_split(int64_t rows, int32_t H, int32_t k, int32_t n_split, dsa
   return ns > max_ns ? max_ns : ns;
 }
 
-dsa_status_t run_mla(int64_t rows, const void* q, dsa_dtype_t q_dtype, const void* kv, dsa_dtype_t kv_dtype,
+dsa_status_t run_mla(int64_t rows, int32_t q_per_seq, const void* q, dsa_dtype_t q_dtype, const void* kv, dsa_dtype_t kv_dtype,
                      const float* kv_scale, int64_t num_slots, const int32_t* slots, int32_t k, int32_t H, float sm_scale, float* out,
                      float* lse, int32_t ns, void* ws, size_t ws_bytes, uint32_t* dbg, hipStream_t s) {
   MlaWs w = mla_ws(rows, H, ns);
@@ -220,6 +220,11 @@ dsa_status_t run_mla(int64_t rows, const void* q, dsa_dtype_t q_dtype, const voi
   p.out = out;
   p.lse = lse;
   p.rows = (int32_t)rows;
+  // The verify rows of a sequence share one XCD when the sequences fill the 8 XCDs evenly:
+  // row i's chunk j runs beside the other rows' chunk j, so a token that several rows of the
+  // sequence selected is fetched from HBM once and read again from that XCD's L2.
+  const int64_t nseq = q_per_seq > 0 ? rows / q_per_seq : 0;
+  p.group = q_per_seq > 1 && nseq >= 8 && nseq % 8 == 0 ? q_per_seq : 1;
   p.H = H;
   p.k = k;
   p.n_split = ns;
@@ -363,7 +368,7 @@ dsa_status_t dsa_sparse_mla_decode(int32_t batch, int32_t q_per_seq, const void*
   DSA_TRY(check_device());
   uint32_t* dbg = nullptr;
   DSA_TRY(debug_word(&dbg));
-  return run_mla(rows, q, q_dtype, kv_cache, kv_dtype, kv_scale, num_slots, slots, k, n_heads, sm_scale, out, lse, ns,
+  return run_mla(rows, q_per_seq, q, q_dtype, kv_cache, kv_dtype, kv_scale, num_slots, slots, k, n_heads, sm_scale, out, lse, ns,
                  workspace, workspace_bytes, dbg, (hipStream_t)stream);
 }
 
@@ -504,7 +509,7 @@ dsa_status_t launch_step(const dsa_decode_step_args_t* a, const StepWs& w, void*
 
   const int64_t rows = (int64_t)b->batch * b->q_per_seq;
   const size_t mla_bytes = workspace_bytes - w.mla_off;
-  return run_mla(rows, a->q_mla, a->q_mla_dtype, a->kv_cache, a->kv_dtype, a->kv_scale, b->num_slots, slots, a->top_k,
+  return run_mla(rows, b->q_per_seq, a->q_mla, a->q_mla_dtype, a->kv_cache, a->kv_dtype, a->kv_scale, b->num_slots, slots, a->top_k,
                  a->mla_heads, a->sm_scale, a->out, a->lse, w.ns, ws + w.mla_off, mla_bytes, dbg, s);
 }
 

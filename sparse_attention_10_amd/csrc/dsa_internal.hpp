@@ -256,6 +256,8 @@ struct MlaParams {
   float* part_m;     // [rows, n_split, H]
   float* part_l;     // [rows, n_split, H]
   int32_t rows, H, k, n_split, chunk;
+  int32_t group;     // rows per XCD group: a sequence's verify rows (rows / group sequences,
+                     // a multiple of 8), or 1
   float sm_scale;
   uint32_t* dbg;     // DSA_DEBUG error word
 };

@@ -696,13 +696,18 @@ __global__ __launch_bounds__(kNTF) void mla_fp8d_kernel(MlaParams p) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hg = wave & 3, tb = wave >> 2;
-  // Blocks go to the 8 XCDs round-robin.  With 8 rows or more the chunks of row r run on XCD
-  // r % 8, so the row's q is read from HBM into one L2; with fewer rows they spread.
+  // Blocks go to the 8 XCDs round-robin.  With 8 rows or more, row group u = r / p.group (a
+  // sequence's verify rows, or one row) runs on XCD u % 8, so each row's q is read from HBM into
+  // one L2, and within an XCD the group's rows take chunk `split` one after another: tokens
+  // selected by several rows of a sequence are read from HBM once.  With fewer rows the chunks
+  // spread over all XCDs.
   int r, split;
   if (p.rows >= 8) {
     const int xcd = blockIdx.x & 7, jx = blockIdx.x >> 3;
-    r = 8 * (jx / p.n_split) + xcd;
-    split = jx - (jx / p.n_split) * p.n_split;
+    const int t = jx / p.group, ri = jx - t * p.group;
+    const int uu = t / p.n_split;
+    split = t - uu * p.n_split;
+    r = (8 * uu + xcd) * p.group + ri;
     if (r >= p.rows) return;
   } else {
     r = blockIdx.x / p.n_split;
@@ -1034,14 +1039,17 @@ __global__ __launch_bounds__(kNT) void mla_bf16d_kernel(MlaParams p) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hg = wave & 3, tb = wave >> 2;
-  // Blocks go to the 8 XCDs round-robin.  With 8 rows or more the chunks of row r run on XCD
-  // r % 8, so the row's q is read from HBM into one L2 (the grid covers the rows rounded up to
-  // a multiple of 8); with fewer rows the chunks spread over all XCDs.
+  // Blocks go to the 8 XCDs round-robin, as in mla_fp8d_kernel: with 8 rows or more, row group
+  // r / p.group runs on XCD (r / p.group) % 8 (the grid covers the groups rounded up to a
+  // multiple of 8), its rows taking each chunk one after another; with fewer rows the chunks
+  // spread over all XCDs.
   int r, split;
   if (p.rows >= 8) {
     const int xcd = blockIdx.x & 7, jx = blockIdx.x >> 3;
-    r = 8 * (jx / p.n_split) + xcd;
-    split = jx - (jx / p.n_split) * p.n_split;
+    const int t = jx / p.group, ri = jx - t * p.group;
+    const int uu = t / p.n_split;
+    split = t - uu * p.n_split;
+    r = (8 * uu + xcd) * p.group + ri;
     if (r >= p.rows) return;
   } else {
     r = blockIdx.x / p.n_split;
@@ -1690,19 +1698,20 @@ hipError_t launch_mla(const MlaParams& p0, dsa_dtype_t q_dtype, dsa_dtype_t kv_d
   int chunk = (p.k + p.n_split - 1) / p.n_split;
   chunk = (chunk + kTT - 1) / kTT * kTT;
   p.chunk = chunk;
+  if (p.group < 1 || p.rows % p.group != 0) p.group = 1;
   const dim3 grid((unsigned)p.n_split, (unsigned)p.rows);
+  // XCD-mapped launches: the row groups rounded up to a multiple of 8, times group and n_split
+  const unsigned xgrid = (unsigned)((p.rows >= 8 ? (p.rows / p.group + 7) / 8 * 8 * p.group : p.rows) * p.n_split);
   if (kv_dtype == DSA_FP8_E4M3FN) {
     if (chunk <= kChunkF)
-      hipLaunchKernelGGL(mla_fp8d_kernel, dim3((unsigned)((p.rows >= 8 ? (p.rows + 7) / 8 * 8 : p.rows) * p.n_split)),
-                         dim3(kNTF), 0, s, p);
+      hipLaunchKernelGGL(mla_fp8d_kernel, dim3(xgrid), dim3(kNTF), 0, s, p);
     else hipLaunchKernelGGL(mla_fp8_kernel, grid, dim3(kNT), 0, s, p);
   }
   else if (mla_uses_narrow(p.rows, p.H, kv_dtype) && chunk <= kChunkN) {
     const int64_t rs = (int64_t)p.rows * p.n_split;
     hipLaunchKernelGGL(mla_bf16n_kernel, dim3((unsigned)((rs + 7) / 8 * 8 * (p.H / 16))), dim3(kNTN), 0, s, p);
   } else if (chunk <= kChunkD)
-    hipLaunchKernelGGL(mla_bf16d_kernel, dim3((unsigned)((p.rows >= 8 ? (p.rows + 7) / 8 * 8 : p.rows) * p.n_split)),
-                       dim3(kNT), 0, s, p);
+    hipLaunchKernelGGL(mla_bf16d_kernel, dim3(xgrid), dim3(kNT), 0, s, p);
   else hipLaunchKernelGGL(mla_mfma_kernel<false>, grid, dim3(kNT), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_split == 1) return e;

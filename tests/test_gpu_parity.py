@@ -349,10 +349,17 @@ STEP_CASES = [("c1", [4096], dict()), ("c2", [6000], dict()), ("c3", [4100, 2500
               # the largest batch of the indexer's length-balanced key ranges (128 sequences, some
               # below k), and a batch beyond it (200 fp8 sequences: ranges per sequence)
               ("c3", [int(x) for x in np.random.default_rng(128).integers(100, 2600, size=128)], dict()),
-              ("c5", [int(x) for x in np.random.default_rng(200).integers(2, 2600, size=200)], dict(q_per_seq=1))]
+              ("c5", [int(x) for x in np.random.default_rng(200).integers(2, 2600, size=200)], dict(q_per_seq=1)),
+              # verify rows sharing their indexer query (nested, nearly equal selections) with the
+              # MLA's rows of a sequence on one XCD: 16 fp8 sequences x 2 rows, 8 bf16 x 3 rows
+              ("c5", [int(x) for x in np.random.default_rng(16).integers(2100, 3000, size=16)],
+               dict(q_per_seq=2, shared_index_query=True)),
+              ("c2", [int(x) for x in np.random.default_rng(8).integers(2100, 4000, size=8)],
+               dict(q_per_seq=3, shared_index_query=True))]
 
 
-@pytest.mark.parametrize("name,lens,kw", STEP_CASES, ids=[f"{c[0]}-B{len(c[1])}" for c in STEP_CASES])
+@pytest.mark.parametrize("name,lens,kw", STEP_CASES, ids=[f"{c[0]}-B{len(c[1])}" + ("-shared" if c[2].get("shared_index_query") else "")
+                              for c in STEP_CASES])
 def test_decode_step_staged(name, lens, kw):
     """Staged protocol: (1) the step's scores against the oracle; (2) its selection against the
     oracle's top-k run on the step's own f32 scores (bit-exact) and its slots against the page

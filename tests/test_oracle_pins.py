@@ -642,3 +642,26 @@ def test_up_projection_is_linear_in_o():
     assert not np.allclose(y1, 0)
     yz, _ = O.latent_up_projection(np.zeros((1, 2, 512)), w_uv, w_o)
     assert np.array_equal(yz, np.zeros((1, 6)))
+
+
+def test_shared_index_query_selections_nest():
+    """Verify rows that share one indexer query see nested prefixes of the same scores (row i
+    one token more than row i - 1, position L - Q + i), so the top-k of row i is that of row
+    i - 1 with at most one token exchanged for the newly visible one; and the inputs repeat the
+    first row's query and head weights."""
+    cfg = dsa_inputs.scaled_config("c5", [700, 420, 90], seed=33, q_per_seq=4, top_k=64, idx_heads=8,
+                                   shared_index_query=True)
+    inp = dsa_inputs.make_inputs(cfg, with_mla=False)
+    assert np.array_equal(inp["q_idx"], np.repeat(inp["q_idx"][:, :1], 4, axis=1))
+    assert np.array_equal(inp["w"], np.repeat(inp["w"][:, :1], 4, axis=1))
+    s = O.indexer_scores(inp["q_idx"], cfg.q_idx_dtype, inp["w"], inp["k_cache"], cfg.key_dtype,
+                         inp["k_scale"], inp["seq_lens"], inp["page_table"], cfg.q_per_seq, cfg.page_size)
+    idx = O.topk(s, inp["seq_lens"], cfg.q_per_seq, cfg.top_k)
+    changed = 0
+    for b, L in enumerate(cfg.seq_lens):
+        for i in range(1, 4):
+            a, c = set(idx[b, i - 1][idx[b, i - 1] >= 0]), set(idx[b, i][idx[b, i] >= 0])
+            new = L - 4 + i
+            assert c - a <= {new} and len(a - c) <= 1 and len(a) <= len(c)
+            changed += len(c - a)
+    assert changed > 0      # the new token enters some selection (not a vacuous comparison)
