@@ -8,7 +8,9 @@ Each configuration draws the dtype family (f32, bf16, fp8 caches), batch, rows p
 (decode, verify and a few many-row chunks), ragged lengths (some below k, so rows are padded
 with -1), page size (powers of two, sizes that 16 does not divide, page size 1), k and the MLA
 head count from a fixed seed, so every run checks the same cases (the first DSA_RANDOM_CASES of the
-sequence, 96 by default)."""
+sequence, 96 by default).  A second sweep (DSA_RANDOM_GROUPED_CASES, 32 by default) draws 8 or 16
+sequences of 2-4 verify rows, half of them sharing one indexer query per sequence, the batches
+whose sparse MLA runs a sequence's rows on one XCD."""
 import os
 
 import numpy as np
@@ -42,5 +44,35 @@ def test_decode_step_staged_random(i):
     name, lens, kw = draw_case(i)
     print(f"case {i}: {name} lens={lens} {kw}", flush=True)
     cfg = dsa_inputs.scaled_config(name, lens, seed=3000 + i, **kw)
+    inp = dsa_inputs.make_inputs(cfg)
+    _check_staged(cfg, inp, dsa_inputs.to_torch(inp, cfg, DEV))
+
+
+N_GROUPED = int(os.environ.get("DSA_RANDOM_GROUPED_CASES", "32"))
+
+
+def draw_grouped_case(i):
+    """8 or 16 sequences of 2-4 verify rows (bf16 or fp8 caches), with or without one indexer
+    query per sequence: the sparse MLA then runs each sequence's rows on one XCD, chunk by
+    chunk (nearly equal selections when the query is shared)."""
+    rng = np.random.default_rng([2025, i])
+    name = ["c2", "c5"][i % 2]
+    B = int(rng.choice([8, 16]))
+    Q = int(rng.integers(2, 5))
+    P = int(rng.choice([16, 24, 32, 64, 128]))
+    k = int(rng.choice([64, 256, 1000, 2048]))
+    H = int(rng.choice([16, 32, 48, 64]))
+    lens = [int(x) for x in rng.integers(Q, 3000, size=B)]
+    if rng.random() < 0.5:
+        lens[int(rng.integers(0, B))] = int(rng.integers(Q, max(Q + 1, min(k, 3000))))
+    shared = bool(rng.random() < 0.5)
+    return name, lens, dict(q_per_seq=Q, page_size=P, top_k=k, mla_heads=H, shared_index_query=shared)
+
+
+@pytest.mark.parametrize("i", range(N_GROUPED))
+def test_decode_step_staged_random_grouped(i):
+    name, lens, kw = draw_grouped_case(i)
+    print(f"grouped case {i}: {name} lens={lens} {kw}", flush=True)
+    cfg = dsa_inputs.scaled_config(name, lens, seed=4000 + i, **kw)
     inp = dsa_inputs.make_inputs(cfg)
     _check_staged(cfg, inp, dsa_inputs.to_torch(inp, cfg, DEV))
