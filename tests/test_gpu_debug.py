@@ -61,6 +61,22 @@ def test_debug_build_matches_release_on_random_steps(dbg_lib, i):
     assert np.array_equal(got["scores"].cpu().numpy(), ref["scores"].cpu().numpy(), equal_nan=True)
 
 
+@pytest.mark.parametrize("i", range(8))
+def test_debug_build_matches_release_on_grouped_steps(dbg_lib, i):
+    """The first 8 grouped verify batches of the seeded sweep (8 or 16 sequences x 2-4 rows):
+    the debug build's checks find nothing and change nothing."""
+    from tests.test_gpu_random import draw_grouped_case
+    name, lens, kw = draw_grouped_case(i)
+    cfg, _, t = _case(name, lens, seed=4000 + i, **kw)
+    ref = run_step(cfg, t)
+    with dsa.using_library(dbg_lib):
+        got = run_step(cfg, t)
+        assert dsa.debug_check() == 0
+    for key in ("out", "lse", "idx", "slots"):
+        assert torch.equal(got[key], ref[key]), key
+    assert np.array_equal(got["scores"].cpu().numpy(), ref["scores"].cpu().numpy(), equal_nan=True)
+
+
 def test_debug_flags_page_id_out_of_range(dbg_lib):
     cfg, _, t = _case("c2", [5000], seed=402)
     pages = cfg.num_slots // cfg.page_size
